@@ -1,0 +1,301 @@
+"""Pins of the fp64 oracle against facts fixed by the pages and by mathematics.
+
+Each check is independent of the oracle's own formulas: closed forms,
+invariants, central finite differences, and torch's fp64 cross_entropy with
+autograd on small shapes.  ``test_planted_mistakes_are_caught`` plants
+plausible mistakes in the oracle (on the CPU) and requires some pin to fail.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle.fce_oracle as orc
+
+RNG = np.random.default_rng(12345)
+
+
+def _case(N, H, V, ignore=0, seed=0, xs=1.0, ws=0.5):
+    g = np.random.default_rng(seed)
+    X = g.standard_normal((N, H)) * xs
+    W = g.standard_normal((V, H)) * ws
+    y = g.integers(0, V, size=N)
+    if ignore:
+        y[g.choice(N, size=ignore, replace=False)] = -100
+    return X, W, y
+
+
+# --------------------------------------------------------------- closed forms
+def check_zero_weights_give_log_V():
+    # W = 0: every logit is 0, softmax is uniform, loss = log V for any
+    # smoothing and mask ([LLMS] "The Vocabulary Memory Wall" loss with z = 0).
+    for V, eps in [(7, 0.0), (50, 0.1), (1000, 0.3)]:
+        X, _, y = _case(9, 5, V, ignore=3, seed=V)
+        W = np.zeros((V, 5))
+        r = orc.linear_cross_entropy(X, W, y, label_smoothing=eps)
+        assert abs(r.loss - math.log(V)) < 1e-12, (V, eps, r.loss)
+        r = orc.linear_cross_entropy(X, W, y, label_smoothing=eps, reduction="sum")
+        assert abs(r.loss - 6 * math.log(V)) < 1e-10
+
+
+def check_two_class_closed_form():
+    # N = 1, H = 1, V = 2, x = 1, W = (a, b), label 0: the loss is the
+    # cross-entropy between target (1 - eps/2, eps/2) and the logistic
+    # probabilities, i.e. (1-eps/2) softplus(b-a) + (eps/2) softplus(a-b);
+    # its derivative wrt (a, b) is (sigmoid(a-b) - 1 + eps/2, sigmoid(b-a) - eps/2).
+    def softplus(t):
+        return math.log1p(math.exp(-abs(t))) + max(t, 0.0)
+
+    def sigmoid(t):
+        return 1.0 / (1.0 + math.exp(-t))
+
+    for a, b, eps in [(0.3, -1.2, 0.0), (2.0, 5.0, 0.0), (-1.0, 0.7, 0.2), (4.0, 4.0, 0.5)]:
+        X = np.array([[1.0]])
+        W = np.array([[a], [b]])
+        r = orc.linear_cross_entropy(X, W, np.array([0]), label_smoothing=eps)
+        want = (1 - eps / 2) * softplus(b - a) + (eps / 2) * softplus(a - b)
+        assert abs(r.loss - want) < 1e-13, (a, b, eps)
+        ga = sigmoid(a - b) - (1 - eps / 2)
+        gb = sigmoid(b - a) - eps / 2
+        assert np.allclose(r.dW[:, 0], [ga, gb], atol=1e-14)
+        assert abs(r.dX[0, 0] - (ga * a + gb * b)) < 1e-13
+
+
+def check_single_class_is_zero():
+    # V = 1: softmax is 1 at the only class, loss and gradients vanish.
+    X, W, _ = _case(6, 4, 1, seed=3)
+    y = np.zeros(6, dtype=np.int64)
+    for eps in (0.0, 0.25):
+        r = orc.linear_cross_entropy(X, W, y, label_smoothing=eps)
+        assert abs(r.loss) < 1e-14
+        assert np.abs(r.dX).max() < 1e-14 and np.abs(r.dW).max() < 1e-14
+
+
+def check_uniform_logits_closed_form():
+    # X = 0: every logit is 0, so p = 1/V; dZ_ij = (1/V - q_ij)/D, dW = dZ^T X = 0
+    # and dX_i = (1-eps) (mean_j W_j - W_{y_i}) / D.
+    V, H, N = 11, 4, 7
+    _, W, y = _case(N, H, V, ignore=2, seed=5)
+    X = np.zeros((N, H))
+    eps = 0.2
+    r = orc.linear_cross_entropy(X, W, y, label_smoothing=eps)
+    D = 5.0
+    assert abs(r.loss - math.log(V)) < 1e-13
+    assert np.abs(r.dW).max() == 0.0
+    for i in range(N):
+        if y[i] == -100:
+            assert np.all(r.dX[i] == 0.0)
+        else:
+            want = (1 - eps) * (W.mean(axis=0) - W[y[i]]) / D
+            assert np.allclose(r.dX[i], want, atol=1e-14)
+
+
+# ------------------------------------------------------------ library routine
+def check_matches_torch_cross_entropy():
+    # torch's F.cross_entropy on materialised logits, fp64 on the CPU, with
+    # autograd: the unfused pipeline of [LLMS] "The Standard Execution
+    # Pipeline" and the per-chunk call of [CCE]'s chunked module.
+    cases = [(64, 32, 512, 6, 0.0, "mean"), (40, 16, 300, 0, 0.1, "mean"),
+             (33, 8, 129, 5, 0.3, "sum"), (17, 24, 64, 16, 0.05, "mean")]
+    for n, (N, H, V, ign, eps, red) in enumerate(cases):
+        X, W, y = _case(N, H, V, ignore=ign, seed=100 + n)
+        r = orc.linear_cross_entropy(X, W, y, label_smoothing=eps, reduction=red, grad_loss=1.7)
+        Xt = torch.tensor(X, requires_grad=True)
+        Wt = torch.tensor(W, requires_grad=True)
+        L = torch.nn.functional.cross_entropy(Xt @ Wt.T, torch.tensor(y), ignore_index=-100,
+                                              label_smoothing=eps, reduction=red)
+        (L * 1.7).backward()
+        assert abs(r.loss - L.item()) <= 1e-12 * max(1.0, abs(L.item())), (n, r.loss, L.item())
+        assert np.allclose(r.dX, Xt.grad.numpy(), rtol=1e-10, atol=1e-13), n
+        assert np.allclose(r.dW, Wt.grad.numpy(), rtol=1e-10, atol=1e-13), n
+
+
+# ------------------------------------------------------------- brute force
+def check_finite_differences():
+    # Central differences of the oracle's own loss, fp64, tiny shapes: the
+    # gradient must be the derivative of the loss.
+    h = 1e-6
+    for seed, (N, H, V, ign, eps, red) in enumerate([(8, 8, 16, 2, 0.1, "mean"), (5, 3, 9, 0, 0.0, "sum"),
+                                                     (6, 4, 12, 1, 0.3, "mean")]):
+        X, W, y = _case(N, H, V, ignore=ign, seed=200 + seed)
+        r = orc.linear_cross_entropy(X, W, y, label_smoothing=eps, reduction=red, grad_loss=0.8)
+
+        def L(X_, W_):
+            return 0.8 * orc.linear_cross_entropy(X_, W_, y, label_smoothing=eps, reduction=red).loss
+
+        for (i, k) in [(a, b) for a in range(N) for b in range(H)]:
+            Xp = X.copy(); Xp[i, k] += h
+            Xm = X.copy(); Xm[i, k] -= h
+            fd = (L(Xp, W) - L(Xm, W)) / (2 * h)
+            assert abs(fd - r.dX[i, k]) < 1e-7, ("dX", seed, i, k, fd, r.dX[i, k])
+        for (v, k) in [(a, b) for a in range(V) for b in range(H)]:
+            Wp = W.copy(); Wp[v, k] += h
+            Wm = W.copy(); Wm[v, k] -= h
+            fd = (L(X, Wp) - L(X, Wm)) / (2 * h)
+            assert abs(fd - r.dW[v, k]) < 1e-7, ("dW", seed, v, k, fd, r.dW[v, k])
+
+
+# ----------------------------------------------------------------- invariants
+def check_gradient_rows_sum_to_zero():
+    # Each row of dZ sums to 0 (softmax and q both sum to 1), hence
+    # sum_v dW[v, :] = 0 ([LLMS] step 3's gradient).
+    X, W, y = _case(30, 12, 77, ignore=4, seed=7)
+    r = orc.linear_cross_entropy(X, W, y, label_smoothing=0.15)
+    assert np.abs(r.dW.sum(axis=0)).max() < 1e-14 * 77 * 30
+    Z = orc.logits(X[y != -100], W)
+    lse = orc.log_sum_exp(Z)
+    dZ = orc.dlogits(Z, lse, y[y != -100], 0.15, 1.0)
+    assert np.abs(dZ.sum(axis=1)).max() < 1e-14
+
+
+def check_ignored_rows_are_inert():
+    # label == ignore_index: zero dX row; changing that X row changes
+    # neither the loss nor dW ([LLMS] "Numerical Considerations" item 2).
+    X, W, y = _case(20, 6, 40, ignore=5, seed=9)
+    r = orc.linear_cross_entropy(X, W, y, label_smoothing=0.1)
+    ign = y == -100
+    assert np.all(r.dX[ign] == 0.0)
+    X2 = X.copy()
+    X2[ign] = 1e3 * RNG.standard_normal((ign.sum(), 6))
+    r2 = orc.linear_cross_entropy(X2, W, y, label_smoothing=0.1)
+    assert r2.loss == r.loss
+    assert np.array_equal(r2.dW, r.dW)
+
+
+def check_shift_invariance():
+    # W -> W + 1 u^T adds x_i.u to every logit of row i: LSE and all logits
+    # shift together, so the loss, dZ, dX and dW are unchanged ([CCE]
+    # "Online Log-Sum-Exp": LSE(z) = m + log sum exp(z - m) for any m).
+    X, W, y = _case(25, 7, 60, ignore=3, seed=11)
+    u = RNG.standard_normal(7)
+    a = orc.linear_cross_entropy(X, W, y, label_smoothing=0.2)
+    b = orc.linear_cross_entropy(X, W + u[None, :], y, label_smoothing=0.2)
+    assert abs(a.loss - b.loss) < 1e-12
+    assert np.allclose(a.dX, b.dX, atol=1e-13)
+    assert np.allclose(a.dW, b.dW, atol=1e-13)
+
+
+def check_large_logits_stay_finite():
+    # Logits far above exp's fp32 overflow point ([CCE] "Numerical
+    # Stability": exp overflows for x > 88.7) still give finite results that
+    # agree with the logistic closed form in the two-class case.
+    X, W, y = _case(16, 8, 50, seed=13, xs=100.0)
+    r = orc.linear_cross_entropy(X, W, y)
+    assert np.isfinite(r.loss) and np.isfinite(r.dX).all() and np.isfinite(r.dW).all()
+    r2 = orc.linear_cross_entropy(np.array([[1.0]]), np.array([[800.0], [-300.0]]), np.array([1]))
+    assert abs(r2.loss - 1100.0) < 1e-9
+
+
+def check_all_ignored_gives_zero():
+    # D = max(N_valid, 1) ([CCE] chunked module's final division): with
+    # every row ignored the loss and gradients are 0, not NaN.
+    X, W, _ = _case(5, 3, 10, seed=15)
+    y = np.full(5, -100)
+    r = orc.linear_cross_entropy(X, W, y, label_smoothing=0.1)
+    assert r.loss == 0.0 and r.n_valid == 0
+    assert not r.dX.any() and not r.dW.any()
+
+
+def check_row_block_invariance():
+    # Row blocks only bound memory: per-row results agree to fp64 rounding
+    # (BLAS may pick a different kernel for a different block height).
+    X, W, y = _case(37, 9, 101, ignore=6, seed=17)
+    ref = orc.linear_cross_entropy(X, W, y, label_smoothing=0.1, row_block=1000)
+    for rb in (1, 7, 16):
+        r = orc.linear_cross_entropy(X, W, y, label_smoothing=0.1, row_block=rb)
+        assert abs(r.loss - ref.loss) < 1e-13
+        assert np.allclose(r.dX, ref.dX, rtol=1e-13, atol=1e-16)
+        assert np.allclose(r.dW, ref.dW, rtol=1e-13, atol=1e-16)
+
+
+CHECKS = [check_zero_weights_give_log_V, check_two_class_closed_form, check_single_class_is_zero,
+          check_uniform_logits_closed_form, check_matches_torch_cross_entropy,
+          check_finite_differences, check_gradient_rows_sum_to_zero, check_ignored_rows_are_inert,
+          check_shift_invariance, check_large_logits_stay_finite, check_all_ignored_gives_zero,
+          check_row_block_invariance]
+
+
+@pytest.mark.parametrize("check", CHECKS, ids=[c.__name__[6:] for c in CHECKS])
+def test_pin(check):
+    check()
+
+
+def test_out_of_range_label_raises():
+    X, W, y = _case(4, 3, 10, seed=19)
+    y[2] = 10
+    with pytest.raises(ValueError):
+        orc.linear_cross_entropy(X, W, y)
+    y[2] = -1
+    with pytest.raises(ValueError):
+        orc.linear_cross_entropy(X, W, y)
+
+
+def test_sampled_rows_match_full():
+    # The sampled entry points used at full workload sizes agree with the
+    # full computation (they are built from the same pinned steps).
+    X, W, y = _case(50, 10, 200, ignore=5, seed=21)
+    r = orc.linear_cross_entropy(X, W, y, label_smoothing=0.1, grad_loss=2.0)
+    rows = np.array([0, 3, 17, 49] + list(np.nonzero(y == -100)[0][:2]))
+    dx, lse, terms = orc.dX_rows(X, W, y, rows, label_smoothing=0.1, grad_loss=2.0)
+    assert np.allclose(dx, r.dX[rows], atol=1e-15)
+    v = np.array([0, 5, 199, int(y[0])])
+    dw = orc.dW_rows(X, W, y, r.lse, v, label_smoothing=0.1, grad_loss=2.0)
+    assert np.allclose(dw, r.dW[v], atol=1e-14)
+    loss, lse_f, nv = orc.forward(X, W, y, label_smoothing=0.1)
+    assert abs(loss - r.loss) < 1e-13 and nv == r.n_valid
+
+
+# ----------------------------------------------------------- planted mistakes
+def _mutants():
+    """Plausible mistakes, each planted into a copy of the oracle's steps."""
+    base_tl, base_dl, base_den = orc.token_losses, orc.dlogits, orc.denominator
+    base_lse = orc.log_sum_exp
+
+    def tl_drop_smooth(Z, lse, y, eps):
+        return base_tl(Z, lse, y, 0.0)
+
+    def tl_sign(Z, lse, y, eps):
+        return -base_tl(Z, lse, y, eps)
+
+    def tl_wrong_index(Z, lse, y, eps):
+        return base_tl(Z, lse, (y + 1) % Z.shape[1], eps)
+
+    def dl_drop_smooth(Z, lse, y, eps, scale):
+        return base_dl(Z, lse, y, 0.0, scale)
+
+    def dl_no_onehot_scale(Z, lse, y, eps, scale):
+        P = np.exp(Z - lse[:, None])
+        P[np.arange(Z.shape[0]), y] -= 1.0
+        return (P - eps / Z.shape[1]) * scale
+
+    def den_all_rows(n_valid, reduction):
+        return base_den(n_valid + 1, reduction)
+
+    def lse_no_max(Z):
+        return np.log(np.exp(Z).sum(axis=1))
+
+    def lse_drop_max(Z):
+        return np.log(np.exp(Z - Z.max(axis=1)[:, None]).sum(axis=1))
+
+    def logits_transposed_bad(X, W):
+        return X @ W.T * 1.0000001
+
+    return [("token_losses", tl_drop_smooth), ("token_losses", tl_sign),
+            ("token_losses", tl_wrong_index), ("dlogits", dl_drop_smooth),
+            ("dlogits", dl_no_onehot_scale), ("denominator", den_all_rows),
+            ("log_sum_exp", lse_no_max), ("log_sum_exp", lse_drop_max),
+            ("logits", logits_transposed_bad)]
+
+
+@pytest.mark.parametrize("name,fn", _mutants(), ids=lambda m: getattr(m, "__name__", str(m)))
+def test_planted_mistakes_are_caught(monkeypatch, name, fn):
+    monkeypatch.setattr(orc, name, fn)
+    failures = 0
+    with np.errstate(all="ignore"):
+        for check in CHECKS:
+            try:
+                check()
+            except (AssertionError, FloatingPointError, ValueError, OverflowError):
+                failures += 1
+    assert failures > 0, f"no pin catches the planted mistake in {name}"
