@@ -1,0 +1,162 @@
+/*
+ * fce.h -- fused linear cross-entropy for AMD MI355X (gfx950): C ABI.
+ *
+ * The operation is the language-model-head loss over a vocabulary of V
+ * classes.  With hidden states X[N,H], unembedding weights W[V,H] and labels
+ * y[N]:
+ *
+ *   Z = X W^T                                  ("Chunked and Fused Cross-Entropy: How Online
+ *                                                Logit Tiling Slashes ... VRAM Bottlenecks",
+ *                                                llms.blog, "The Vocabulary Memory Wall")
+ *   LSE_i = m_i + log sum_j exp(z_ij - m_i)      (same page, "Mathematical Mechanics", step 2)
+ *   l_i   = LSE_i - (1-eps) z_{i,y_i} - (eps/V) sum_j z_ij      (eps = label_smoothing)
+ *   loss  = sum_{i valid} l_i / D,  D = max(N_valid, 1) for mean, 1 for sum
+ *   dZ_ij = (softmax_ij - (1-eps)[j = y_i] - eps/V) * g / D     (same page, step 3;
+ *                                                "Fused cross-entropy -- the memory kernel",
+ *                                                "The gradient that makes fusion trivial")
+ *   dX = dZ W,  dW = dZ^T X                      (llms.blog step 4; lesson 27 "Trick 2")
+ *
+ * Rows whose label equals ignore_index carry no loss and no gradient
+ * (llms.blog, "Numerical Considerations", item 2).  The N x V logits never
+ * exist in device memory: the forward reduces each logit tile on chip with
+ * the running max / sum-exp recurrence (lesson 27, "Trick 1"), and the
+ * backward recomputes logit tiles into a scratch block of at most
+ * chunk x V elements (llms.blog, "Mathematical Mechanics", step 1 and
+ * "Peak Logit Memory Complexity"; lesson 27, "Worked number").
+ *
+ * Conventions shared by every entry point
+ *   - Pointers named X, W, labels, loss, lse, grad_loss, dX, dW and the
+ *     workspace are DEVICE pointers; every other argument is a host value.
+ *   - X is row-major [N][H], W row-major [V][H]; both have the dtype given by
+ *     `dtype` (FCE_BF16 or FCE_F32).  labels is int32[N], 0-based.
+ *   - Outputs (loss, lse, dX, dW) are float32.  dX [N][H] and dW [V][H] are
+ *     overwritten, never accumulated into.
+ *   - The caller owns every buffer, including the workspace, whose size is
+ *     given by fce_workspace_size().  The library never allocates or frees
+ *     device memory and never synchronises the stream (except
+ *     fce_get_label_errors and fce_timing_read, which say so).
+ *   - Work is enqueued asynchronously on `stream`.  Calls sharing one
+ *     workspace must be ordered on one stream.
+ *   - Results are deterministic: the same inputs give bitwise-identical
+ *     outputs on the same device and build (no floating-point atomics).
+ *   - Host-detectable argument errors return a negative status with nothing
+ *     enqueued.  A label outside [0, V) that is not ignore_index is detected
+ *     on the device: it is counted (fce_get_label_errors), its row is
+ *     treated as ignored, and the loss is set to NaN.
+ *   - Alignment: X, W, dX, dW and the workspace must be 16-byte aligned and
+ *     H must be a multiple of 8 (bf16) or 4 (fp32), so that every row starts
+ *     on a 16-byte boundary.
+ *   - Shapes: N >= 0, H >= 1, V >= 1.  N = 0 gives loss 0 and dW = 0.
+ *
+ * `chunk` bounds the logit-space scratch of the backward pass to chunk x V
+ * elements (bf16 for FCE_BF16, fp32 for FCE_F32, each dimension rounded up
+ * to the kernel tile).  `schedule` chooses the shape of that block:
+ *   FCE_SCHED_TOKEN  chunk tokens x all V, as the pages describe;
+ *   FCE_SCHED_VOCAB  all N tokens x (chunk*V/N) vocabulary columns;
+ *   FCE_SCHED_AUTO   the block shape with the same budget that moves the
+ *                    fewest fp32 gradient bytes (see fce_plan).
+ * The loss and gradients are the same up to fp32 summation order.
+ */
+#ifndef FCE_H
+#define FCE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  FCE_OK = 0,
+  FCE_ERR_NULL = -1,      /* a required pointer is NULL */
+  FCE_ERR_SHAPE = -2,     /* N < 0, H < 1, V < 1, or sizes overflow */
+  FCE_ERR_ARG = -3,       /* bad enum, chunk < 1, label_smoothing outside [0,1) or NaN */
+  FCE_ERR_WORKSPACE = -4, /* workspace smaller than fce_workspace_size() */
+  FCE_ERR_ALIGN = -5,     /* pointer not 16-byte aligned or H not a multiple of 8 / 4 */
+  FCE_ERR_DEVICE = -6,    /* current device is not gfx950 */
+  FCE_ERR_HIP = -7        /* a HIP runtime call or kernel launch failed */
+} fce_status;
+
+typedef enum { FCE_F32 = 0, FCE_BF16 = 1 } fce_dtype;
+typedef enum { FCE_MEAN = 0, FCE_SUM = 1 } fce_reduction;
+typedef enum { FCE_SCHED_AUTO = 0, FCE_SCHED_TOKEN = 1, FCE_SCHED_VOCAB = 2 } fce_schedule;
+
+/* The backward schedule chosen for a problem (host-only, no GPU needed). */
+typedef struct {
+  int64_t block_tokens;     /* tokens per logit block (C_N)                        */
+  int64_t block_vocab;      /* vocabulary columns per logit block (C_V)            */
+  int64_t n_token_blocks;   /* ceil(N / C_N)                                       */
+  int64_t n_vocab_blocks;   /* ceil(V / C_V)                                       */
+  int64_t scratch_bytes;    /* logit-space device bytes: the dZ block, tile-padded */
+  int64_t partial_bytes;    /* forward per-(split, token) LSE partials             */
+  int64_t workspace_bytes;  /* == fce_workspace_size()                             */
+  int64_t fwd_splits;       /* vocabulary splits of the forward reduction          */
+  int64_t grad_rmw_bytes;   /* fp32 dX/dW bytes written + re-read across blocks    */
+} fce_plan_info;
+
+/* Size in bytes of the workspace the three compute entry points need for
+ * this problem (host-only).  Returns 0 if the arguments are invalid. */
+size_t fce_workspace_size(int64_t N, int64_t H, int64_t V, fce_dtype dtype, int64_t chunk,
+                          fce_schedule schedule);
+
+/* Fill *out with the plan the compute entry points will use (host-only). */
+fce_status fce_plan(int64_t N, int64_t H, int64_t V, fce_dtype dtype, int64_t chunk,
+                    fce_schedule schedule, fce_plan_info* out);
+
+/* Forward pass (llms.blog "Mathematical Mechanics" steps 1-2; aifetchly
+ * "Cut Cross-Entropy ... Guide", "Online Log-Sum-Exp Accumulation").
+ * Writes loss[1] (device) and lse[N] (device; LSE of every valid row, NaN
+ * on ignored rows), which fce_backward needs. */
+fce_status fce_forward(const void* X, const void* W, const int32_t* labels, int64_t N, int64_t H,
+                       int64_t V, fce_dtype dtype, int32_t ignore_index, float label_smoothing,
+                       fce_reduction reduction, int64_t chunk, fce_schedule schedule, float* loss,
+                       float* lse, void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* Backward pass with recomputation (lesson 27 "Trick 1": the gradient tile
+ * is rebuilt from the saved LSE; "Trick 2": it feeds dX = dZ W and
+ * dW += dZ^T X block by block).  lse[N] must come from fce_forward with the
+ * same inputs.  grad_loss is a device pointer to the upstream scalar
+ * gradient g, or NULL for g = 1.  Overwrites dX[N][H] and dW[V][H]. */
+fce_status fce_backward(const void* X, const void* W, const int32_t* labels, int64_t N, int64_t H,
+                        int64_t V, fce_dtype dtype, int32_t ignore_index, float label_smoothing,
+                        fce_reduction reduction, int64_t chunk, fce_schedule schedule,
+                        const float* lse, const float* grad_loss, float* dX, float* dW,
+                        void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* Forward then backward with g = 1 in one call; the LSE stays in the
+ * workspace.  Bitwise identical to fce_forward followed by fce_backward. */
+fce_status fce_fused_fwd_bwd(const void* X, const void* W, const int32_t* labels, int64_t N,
+                             int64_t H, int64_t V, fce_dtype dtype, int32_t ignore_index,
+                             float label_smoothing, fce_reduction reduction, int64_t chunk,
+                             fce_schedule schedule, float* loss, float* dX, float* dW,
+                             void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* Number of labels outside [0, V) that were not ignore_index in the last
+ * call that used this workspace.  Synchronises `stream`. */
+fce_status fce_get_label_errors(const void* workspace, int32_t* host_count, hipStream_t stream);
+
+/* Static description of a status code. */
+const char* fce_status_string(fce_status status);
+
+/* Per-kernel timing.  While enabled, every kernel the library launches is
+ * bracketed by HIP events on the caller's stream.  fce_timing_read
+ * synchronises on the recorded events, fills up to `cap` entries and resets
+ * the counters.  Not thread-safe: meant for one benchmarking thread. */
+typedef struct {
+  char name[32];        /* kernel family: "fwd_lse", "bwd_dz", "bwd_dw", "bwd_dx", ... */
+  int64_t launches;     /* launches recorded                                      */
+  double total_ms;      /* summed event-to-event time                             */
+  double flops;         /* algorithmic flops of those launches (0 if not a GEMM)  */
+} fce_kernel_timing;
+
+fce_status fce_timing_enable(int enable);
+fce_status fce_timing_read(fce_kernel_timing* out, int cap, int* count);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FCE_H */

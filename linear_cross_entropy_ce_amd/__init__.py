@@ -1,0 +1,113 @@
+"""Fused linear cross-entropy for AMD MI355X (gfx950).
+
+The computation runs entirely in the HIP library ``lib/libfce.so`` (C ABI in
+``include/fce.h``).  This package only marshals arguments: torch provides
+device memory and the stream.
+
+    loss = linear_cross_entropy(hidden, weight, labels, ignore_index=-100)
+    loss.backward()
+
+No N x V logits tensor is ever allocated: the forward reduces logit tiles on
+chip, the backward recomputes them into a scratch block of at most
+chunk x V elements ("Chunked and Fused Cross-Entropy", llms.blog,
+"Mathematical Mechanics"; "Fused cross-entropy -- the memory kernel",
+"Trick 2").
+"""
+from __future__ import annotations
+
+from ._binding import (  # noqa: F401
+    FCE_BF16,
+    FCE_F32,
+    FceError,
+    SCHEDULES,
+    fce_backward,
+    fce_forward,
+    fce_fused_fwd_bwd,
+    fce_get_label_errors,
+    fce_plan,
+    status_string,
+    fce_timing_enable,
+    fce_timing_read,
+    fce_workspace_size,
+    load_library,
+)
+from .memory import logit_space_bytes  # noqa: F401
+
+
+def _dtype_code(t):
+    import torch
+
+    if t.dtype == torch.bfloat16:
+        return FCE_BF16
+    if t.dtype == torch.float32:
+        return FCE_F32
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def workspace_for(N, H, V, dtype, chunk=1024, schedule="auto", device="cuda"):
+    """A uint8 workspace tensor of the size the library asks for."""
+    import torch
+
+    code = dtype if isinstance(dtype, int) else (FCE_BF16 if dtype == torch.bfloat16 else FCE_F32)
+    n = fce_workspace_size(N, H, V, code, chunk, SCHEDULES.get(schedule, schedule))
+    if n == 0:
+        raise ValueError("invalid problem for fce_workspace_size")
+    return torch.empty(n, dtype=torch.uint8, device=device)
+
+
+def _make_function():
+    import torch
+
+    class _LinearCrossEntropy(torch.autograd.Function):
+        @staticmethod
+        def forward(ctx, hidden, weight, labels, ignore_index, label_smoothing, reduction, chunk,
+                    schedule):
+            H = hidden.shape[-1]
+            X = hidden.reshape(-1, H).contiguous()
+            W = weight.contiguous()
+            if X.dtype != W.dtype:
+                raise TypeError("hidden and weight must share a dtype")
+            y = labels.reshape(-1).to(torch.int32).contiguous()
+            N, V = X.shape[0], W.shape[0]
+            ws = workspace_for(N, H, V, X.dtype, chunk, schedule, X.device)
+            loss = torch.empty(1, dtype=torch.float32, device=X.device)
+            lse = torch.empty(max(N, 1), dtype=torch.float32, device=X.device)
+            fce_forward(X if N else None, W, y if N else None, loss, lse, ws, ignore_index,
+                        label_smoothing, reduction, chunk, schedule)
+            ctx.save_for_backward(X, W, y, lse)
+            ctx.cfg = (ignore_index, label_smoothing, reduction, chunk, schedule, hidden.shape,
+                       hidden.dtype, weight.dtype)
+            ctx.ws = ws
+            return loss[0]
+
+        @staticmethod
+        def backward(ctx, g):
+            X, W, y, lse = ctx.saved_tensors
+            ignore_index, eps, reduction, chunk, schedule, hshape, hdt, wdt = ctx.cfg
+            N, H = X.shape
+            g1 = g.reshape(1).to(torch.float32).contiguous()
+            dX = torch.empty((N, H), dtype=torch.float32, device=X.device)
+            dW = torch.empty(W.shape, dtype=torch.float32, device=X.device)
+            fce_backward(X if N else None, W, y if N else None, lse, g1, dX if N else None, dW,
+                         ctx.ws, ignore_index, eps, reduction, chunk, schedule)
+            return (dX.to(hdt).reshape(hshape), dW.to(wdt), None, None, None, None, None, None)
+
+    return _LinearCrossEntropy
+
+
+_FN = None
+
+
+def linear_cross_entropy(hidden, weight, labels, ignore_index: int = -100,
+                         label_smoothing: float = 0.0, reduction: str = "mean", chunk: int = 1024,
+                         schedule: str = "auto"):
+    """Mean (or summed) cross-entropy of ``hidden @ weight.T`` against ``labels``.
+
+    hidden [..., H] and weight [V, H] share a dtype (bfloat16 or float32);
+    labels [...] are class indices, ``ignore_index`` rows carry no loss.
+    Gradients for hidden and weight come from the fused backward."""
+    global _FN
+    if _FN is None:
+        _FN = _make_function()
+    return _FN.apply(hidden, weight, labels, ignore_index, label_smoothing, reduction, chunk,
+                     schedule)

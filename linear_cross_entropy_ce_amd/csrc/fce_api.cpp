@@ -1,0 +1,294 @@
+// C ABI of the fused linear cross-entropy library: argument validation,
+// planning, and the launch sequences of fce_forward / fce_backward /
+// fce_fused_fwd_bwd.  Nothing here allocates device memory.
+#include "fce.h"
+
+#include <hip/hip_runtime_api.h>
+
+#include <cmath>
+#include <cstring>
+#include <mutex>
+#include <string>
+#include <vector>
+
+#include "fce_kernels.h"
+#include "fce_plan.h"
+
+namespace {
+
+using fce::Dtype;
+using fce::Plan;
+using fce::Schedule;
+
+// --------------------------------------------------------------- timing
+struct EventPair {
+  hipEvent_t start = nullptr, stop = nullptr;
+};
+
+struct Record {
+  std::string name;
+  double flops;
+  int pair;
+};
+
+class EventTimer final : public fce::KernelTimer {
+ public:
+  bool enabled = false;
+  std::vector<EventPair> pool;
+  std::vector<Record> records;
+  int open = -1;
+  bool failed = false;
+
+  void begin(const char* name, double flops, hipStream_t st) override {
+    if (!enabled) return;
+    const int idx = static_cast<int>(records.size());
+    if (idx >= static_cast<int>(pool.size())) {
+      EventPair e;
+      if (hipEventCreate(&e.start) != hipSuccess || hipEventCreate(&e.stop) != hipSuccess) {
+        failed = true;
+        return;
+      }
+      pool.push_back(e);
+    }
+    records.push_back(Record{name, flops, idx});
+    open = idx;
+    if (hipEventRecord(pool[idx].start, st) != hipSuccess) failed = true;
+  }
+  void end(hipStream_t st) override {
+    if (!enabled || open < 0) return;
+    if (hipEventRecord(pool[open].stop, st) != hipSuccess) failed = true;
+    open = -1;
+  }
+};
+
+class NullTimer final : public fce::KernelTimer {
+ public:
+  void begin(const char*, double, hipStream_t) override {}
+  void end(hipStream_t) override {}
+};
+
+EventTimer g_timer;
+NullTimer g_null_timer;
+std::mutex g_arch_mu;
+int g_arch_ok[64] = {0};  // 0 unknown, 1 gfx950, -1 other
+
+fce::KernelTimer* timer() {
+  return g_timer.enabled ? static_cast<fce::KernelTimer*>(&g_timer) : &g_null_timer;
+}
+
+fce_status check_device() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return FCE_ERR_HIP;
+  if (dev < 0 || dev >= 64) return FCE_ERR_DEVICE;
+  std::lock_guard<std::mutex> lock(g_arch_mu);
+  if (g_arch_ok[dev] == 0) {
+    hipDeviceProp_t prop;
+    if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return FCE_ERR_HIP;
+    g_arch_ok[dev] = (std::strncmp(prop.gcnArchName, "gfx950", 6) == 0) ? 1 : -1;
+  }
+  return g_arch_ok[dev] == 1 ? FCE_OK : FCE_ERR_DEVICE;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+fce_status validate(const void* X, const void* W, const int32_t* labels, int64_t N, int64_t H,
+                    int64_t V, fce_dtype dtype, float eps, fce_reduction red, int64_t chunk,
+                    fce_schedule sched, size_t ws_bytes, const void* ws, Plan* plan) {
+  if (N < 0 || H < 1 || V < 1) return FCE_ERR_SHAPE;
+  if (W == nullptr || ws == nullptr) return FCE_ERR_NULL;
+  if (N > 0 && (X == nullptr || labels == nullptr)) return FCE_ERR_NULL;
+  if (dtype != FCE_F32 && dtype != FCE_BF16) return FCE_ERR_ARG;
+  if (red != FCE_MEAN && red != FCE_SUM) return FCE_ERR_ARG;
+  if (sched != FCE_SCHED_AUTO && sched != FCE_SCHED_TOKEN && sched != FCE_SCHED_VOCAB)
+    return FCE_ERR_ARG;
+  if (chunk < 1) return FCE_ERR_ARG;
+  if (!(eps >= 0.0f && eps < 1.0f)) return FCE_ERR_ARG;  // also rejects NaN
+  const int64_t vec = (dtype == FCE_BF16) ? 8 : 4;
+  if (H % vec != 0) return FCE_ERR_ALIGN;
+  if (!aligned16(W) || !aligned16(ws) || (N > 0 && !aligned16(X))) return FCE_ERR_ALIGN;
+  if (!fce::make_plan(N, H, V, static_cast<Dtype>(dtype), chunk, static_cast<Schedule>(sched),
+                      plan))
+    return FCE_ERR_SHAPE;
+  if (ws_bytes < plan->total) return FCE_ERR_WORKSPACE;
+  return FCE_OK;
+}
+
+fce_status from_hip(hipError_t e) { return e == hipSuccess ? FCE_OK : FCE_ERR_HIP; }
+
+}  // namespace
+
+extern "C" {
+
+size_t fce_workspace_size(int64_t N, int64_t H, int64_t V, fce_dtype dtype, int64_t chunk,
+                          fce_schedule schedule) {
+  if (dtype != FCE_F32 && dtype != FCE_BF16) return 0;
+  if (schedule != FCE_SCHED_AUTO && schedule != FCE_SCHED_TOKEN && schedule != FCE_SCHED_VOCAB)
+    return 0;
+  Plan p;
+  if (!fce::make_plan(N, H, V, static_cast<Dtype>(dtype), chunk, static_cast<Schedule>(schedule),
+                      &p))
+    return 0;
+  return p.total;
+}
+
+fce_status fce_plan(int64_t N, int64_t H, int64_t V, fce_dtype dtype, int64_t chunk,
+                    fce_schedule schedule, fce_plan_info* out) {
+  if (out == nullptr) return FCE_ERR_NULL;
+  if (N < 0 || H < 1 || V < 1) return FCE_ERR_SHAPE;
+  if (dtype != FCE_F32 && dtype != FCE_BF16) return FCE_ERR_ARG;
+  if (schedule != FCE_SCHED_AUTO && schedule != FCE_SCHED_TOKEN && schedule != FCE_SCHED_VOCAB)
+    return FCE_ERR_ARG;
+  if (chunk < 1) return FCE_ERR_ARG;
+  Plan p;
+  if (!fce::make_plan(N, H, V, static_cast<Dtype>(dtype), chunk, static_cast<Schedule>(schedule),
+                      &p))
+    return FCE_ERR_SHAPE;
+  out->block_tokens = p.CN;
+  out->block_vocab = p.CV;
+  out->n_token_blocks = p.a;
+  out->n_vocab_blocks = p.b;
+  out->scratch_bytes = static_cast<int64_t>(p.scratch_bytes);
+  out->partial_bytes = static_cast<int64_t>(p.partial_bytes);
+  out->workspace_bytes = static_cast<int64_t>(p.total);
+  out->fwd_splits = p.fwd_splits;
+  out->grad_rmw_bytes = p.grad_rmw_bytes;
+  return FCE_OK;
+}
+
+fce_status fce_forward(const void* X, const void* W, const int32_t* labels, int64_t N, int64_t H,
+                       int64_t V, fce_dtype dtype, int32_t ignore_index, float label_smoothing,
+                       fce_reduction reduction, int64_t chunk, fce_schedule schedule, float* loss,
+                       float* lse, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  Plan p;
+  fce_status s = validate(X, W, labels, N, H, V, dtype, label_smoothing, reduction, chunk,
+                          schedule, workspace_bytes, workspace, &p);
+  if (s != FCE_OK) return s;
+  if (loss == nullptr || (N > 0 && lse == nullptr)) return FCE_ERR_NULL;
+  if ((s = check_device()) != FCE_OK) return s;
+  char* ws = static_cast<char*>(workspace);
+  hipError_t e = fce::launch_label_scan(p, labels, ignore_index, reduction == FCE_SUM, nullptr, ws,
+                                        stream, timer());
+  if (e == hipSuccess)
+    e = fce::launch_forward(p, X, W, labels, ignore_index, label_smoothing, loss, lse, ws, stream,
+                            timer());
+  return from_hip(e);
+}
+
+fce_status fce_backward(const void* X, const void* W, const int32_t* labels, int64_t N, int64_t H,
+                        int64_t V, fce_dtype dtype, int32_t ignore_index, float label_smoothing,
+                        fce_reduction reduction, int64_t chunk, fce_schedule schedule,
+                        const float* lse, const float* grad_loss, float* dX, float* dW,
+                        void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  Plan p;
+  fce_status s = validate(X, W, labels, N, H, V, dtype, label_smoothing, reduction, chunk,
+                          schedule, workspace_bytes, workspace, &p);
+  if (s != FCE_OK) return s;
+  if (dW == nullptr || (N > 0 && (lse == nullptr || dX == nullptr))) return FCE_ERR_NULL;
+  if (!aligned16(dW) || (N > 0 && !aligned16(dX))) return FCE_ERR_ALIGN;
+  if ((s = check_device()) != FCE_OK) return s;
+  char* ws = static_cast<char*>(workspace);
+  hipError_t e = fce::launch_label_scan(p, labels, ignore_index, reduction == FCE_SUM, grad_loss,
+                                        ws, stream, timer());
+  if (e == hipSuccess)
+    e = fce::launch_backward(p, X, W, labels, ignore_index, label_smoothing, lse, dX, dW, ws,
+                             stream, timer());
+  return from_hip(e);
+}
+
+fce_status fce_fused_fwd_bwd(const void* X, const void* W, const int32_t* labels, int64_t N,
+                             int64_t H, int64_t V, fce_dtype dtype, int32_t ignore_index,
+                             float label_smoothing, fce_reduction reduction, int64_t chunk,
+                             fce_schedule schedule, float* loss, float* dX, float* dW,
+                             void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  Plan p;
+  fce_status s = validate(X, W, labels, N, H, V, dtype, label_smoothing, reduction, chunk,
+                          schedule, workspace_bytes, workspace, &p);
+  if (s != FCE_OK) return s;
+  if (loss == nullptr || dW == nullptr || (N > 0 && dX == nullptr)) return FCE_ERR_NULL;
+  if (!aligned16(dW) || (N > 0 && !aligned16(dX))) return FCE_ERR_ALIGN;
+  if ((s = check_device()) != FCE_OK) return s;
+  char* ws = static_cast<char*>(workspace);
+  float* lse = reinterpret_cast<float*>(ws + p.off_lse);
+  // One label scan serves both passes: with g = 1 its backward scale equals
+  // the one fce_backward would compute.
+  hipError_t e = fce::launch_label_scan(p, labels, ignore_index, reduction == FCE_SUM, nullptr, ws,
+                                        stream, timer());
+  if (e == hipSuccess)
+    e = fce::launch_forward(p, X, W, labels, ignore_index, label_smoothing, loss, lse, ws, stream,
+                            timer());
+  if (e == hipSuccess)
+    e = fce::launch_backward(p, X, W, labels, ignore_index, label_smoothing, lse, dX, dW, ws,
+                             stream, timer());
+  return from_hip(e);
+}
+
+fce_status fce_get_label_errors(const void* workspace, int32_t* host_count, hipStream_t stream) {
+  if (workspace == nullptr || host_count == nullptr) return FCE_ERR_NULL;
+  const fce::Ctrl* ctrl = static_cast<const fce::Ctrl*>(workspace);
+  fce::Ctrl h;
+  if (hipMemcpyAsync(&h, ctrl, sizeof(h), hipMemcpyDeviceToHost, stream) != hipSuccess)
+    return FCE_ERR_HIP;
+  if (hipStreamSynchronize(stream) != hipSuccess) return FCE_ERR_HIP;
+  *host_count = h.n_invalid;
+  return FCE_OK;
+}
+
+const char* fce_status_string(fce_status status) {
+  switch (status) {
+    case FCE_OK: return "ok";
+    case FCE_ERR_NULL: return "a required pointer is NULL";
+    case FCE_ERR_SHAPE: return "invalid shape (need N >= 0, H >= 1, V >= 1, extents < 2^30)";
+    case FCE_ERR_ARG: return "invalid argument (dtype, reduction, schedule, chunk >= 1, 0 <= label_smoothing < 1)";
+    case FCE_ERR_WORKSPACE: return "workspace smaller than fce_workspace_size()";
+    case FCE_ERR_ALIGN: return "pointers must be 16-byte aligned and H a multiple of 8 (bf16) or 4 (fp32)";
+    case FCE_ERR_DEVICE: return "current device is not gfx950 (MI355X)";
+    case FCE_ERR_HIP: return "HIP runtime error or kernel launch failure";
+  }
+  return "unknown status";
+}
+
+fce_status fce_timing_enable(int enable) {
+  g_timer.enabled = enable != 0;
+  if (!g_timer.enabled) {
+    g_timer.records.clear();
+    g_timer.open = -1;
+  }
+  return FCE_OK;
+}
+
+fce_status fce_timing_read(fce_kernel_timing* out, int cap, int* count) {
+  if (count == nullptr || (cap > 0 && out == nullptr)) return FCE_ERR_NULL;
+  std::vector<fce_kernel_timing> agg;
+  bool failed = g_timer.failed;
+  for (const Record& r : g_timer.records) {
+    const EventPair& e = g_timer.pool[r.pair];
+    float ms = 0.0f;
+    if (hipEventSynchronize(e.stop) != hipSuccess ||
+        hipEventElapsedTime(&ms, e.start, e.stop) != hipSuccess) {
+      failed = true;
+      continue;
+    }
+    fce_kernel_timing* slot = nullptr;
+    for (auto& a : agg)
+      if (r.name == a.name) slot = &a;
+    if (slot == nullptr) {
+      fce_kernel_timing t;
+      std::memset(&t, 0, sizeof(t));
+      std::strncpy(t.name, r.name.c_str(), sizeof(t.name) - 1);
+      agg.push_back(t);
+      slot = &agg.back();
+    }
+    slot->launches += 1;
+    slot->total_ms += ms;
+    slot->flops += r.flops;
+  }
+  g_timer.records.clear();
+  g_timer.open = -1;
+  g_timer.failed = false;
+  const int n = static_cast<int>(agg.size());
+  for (int i = 0; i < n && i < cap; ++i) out[i] = agg[i];
+  *count = n;
+  return failed ? FCE_ERR_HIP : FCE_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,307 @@
+// gfx950 building blocks for the fused linear cross-entropy kernels:
+// element traits over the MFMA instructions, global->LDS operand loaders,
+// the LDS double-buffered MFMA main loop, and the XCD-aware tile order.
+//
+// Conventions
+//   An operand is a 2-D array seen as (mn, k): mn runs along the output tile
+//   (M for the MFMA "A" operand, N for "B"), k along the contraction.
+//   K-major:  element (mn, k) at p[mn * ld + k]   (k contiguous)
+//   MN-major: element (mn, k) at p[k * ld + mn]   (mn contiguous)
+//   Both are staged into LDS as [mn][k] rows of BK elements (plus 16 bytes of
+//   padding), so the MFMA fragment reads are identical for every layout.
+//   MN-major tiles are transposed in registers, VEC x VEC at a time, between
+//   the 16-byte global loads and the 16-byte LDS stores.
+//
+//   32x32 MFMA accumulator layout (wave64): element i of lane l holds
+//   row 8*(i/4) + 4*(l/32) + (i%4), column l%32 of the 32x32 block.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "fce_tiles.h"
+
+namespace fce {
+
+typedef __bf16 bf16;
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float floatx16 __attribute__((ext_vector_type(16)));
+typedef float floatx4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr float kLog2e = 1.44269504088896340736f;
+constexpr float kLn2 = 0.69314718055994530942f;
+
+// Hardware transcendental units (v_exp_f32 / v_log_f32, base 2).
+__device__ __forceinline__ float hw_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+__device__ __forceinline__ float hw_log2(float x) { return __builtin_amdgcn_logf(x); }
+
+// ------------------------------------------------------------ element traits
+template <typename T>
+struct Traits;
+
+// bf16: one v_mfma_f32_32x32x16_bf16 per 16-deep K step.  Lane l supplies
+// row l%32 and the 8 consecutive k at 8*(l/32) of that step, for A and B
+// alike, so the hardware's own k order inside the instruction is irrelevant.
+template <>
+struct Traits<bf16> {
+  static constexpr int VEC = 8;  // elements per 16-byte vector
+  typedef bf16x8 Frag;
+  __device__ __forceinline__ static Frag frag(const bf16* p) {
+    return *reinterpret_cast<const bf16x8*>(p);
+  }
+  __device__ __forceinline__ static void mma(floatx16& c, const Frag& a, const Frag& b) {
+    c = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+  }
+};
+
+// fp32: eight v_mfma_f32_32x32x2_f32 per 16-deep K step.  Instruction j
+// takes k = 8*(l/32) + j from lane l, so the same 8 consecutive elements per
+// lane as the bf16 path are read from LDS.
+template <>
+struct Traits<float> {
+  static constexpr int VEC = 4;
+  struct Frag {
+    floatx4 lo, hi;
+  };
+  __device__ __forceinline__ static Frag frag(const float* p) {
+    Frag f;
+    f.lo = *reinterpret_cast<const floatx4*>(p);
+    f.hi = *reinterpret_cast<const floatx4*>(p + 4);
+    return f;
+  }
+  __device__ __forceinline__ static void mma(floatx16& c, const Frag& a, const Frag& b) {
+    c = __builtin_amdgcn_mfma_f32_32x32x2f32(a.lo[0], b.lo[0], c, 0, 0, 0);
+    c = __builtin_amdgcn_mfma_f32_32x32x2f32(a.lo[1], b.lo[1], c, 0, 0, 0);
+    c = __builtin_amdgcn_mfma_f32_32x32x2f32(a.lo[2], b.lo[2], c, 0, 0, 0);
+    c = __builtin_amdgcn_mfma_f32_32x32x2f32(a.lo[3], b.lo[3], c, 0, 0, 0);
+    c = __builtin_amdgcn_mfma_f32_32x32x2f32(a.hi[0], b.hi[0], c, 0, 0, 0);
+    c = __builtin_amdgcn_mfma_f32_32x32x2f32(a.hi[1], b.hi[1], c, 0, 0, 0);
+    c = __builtin_amdgcn_mfma_f32_32x32x2f32(a.hi[2], b.hi[2], c, 0, 0, 0);
+    c = __builtin_amdgcn_mfma_f32_32x32x2f32(a.hi[3], b.hi[3], c, 0, 0, 0);
+  }
+};
+
+// ------------------------------------------------------------------ config
+template <class S, typename T>
+struct Cfg {
+  typedef T Elem;
+  typedef Traits<T> Tr;
+  static constexpr int BM = S::BM, BN = S::BN, BK = S::BK;
+  static constexpr int WAVES_M = S::WAVES_M, WAVES_N = S::WAVES_N, NT = S::NT;
+  static constexpr int VEC = Tr::VEC;
+  static constexpr int LDK = BK + VEC;  // LDS row pitch (elements): 16 bytes of padding
+  static constexpr int WTM = BM / WAVES_M, WTN = BN / WAVES_N;
+  static constexpr int FM = WTM / 32, FN = WTN / 32;
+  static constexpr int A_ELEMS = BM * LDK, B_ELEMS = BN * LDK;
+  static constexpr int STAGE = A_ELEMS + B_ELEMS;
+  static constexpr int LDS_ELEMS = 2 * STAGE;
+  static_assert(BK % 16 == 0 && WTM % 32 == 0 && WTN % 32 == 0, "tile shape");
+  static_assert(LDS_ELEMS * sizeof(T) <= 160 * 1024, "gfx950 LDS is 160 KiB per workgroup");
+};
+
+template <typename T>
+struct Opnd {
+  const T* p;
+  int64_t ld;  // leading dimension in elements
+  int mn_ext;  // vectors starting at or beyond this mn are read as zero
+  int k_ext;   // k at or beyond this are read as zero (K-major: multiple of VEC)
+};
+
+__device__ __forceinline__ void transpose_block(const u32x4 (&in)[8], u32x4 (&out)[8]) {
+  // 8x8 of 16-bit: in[r] holds row r (k), element c in word c/2, half c%2.
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const uint32_t lo = in[2 * q][j >> 1];
+      const uint32_t hi = in[2 * q + 1][j >> 1];
+      out[j][q] = (j & 1) ? ((lo >> 16) | (hi & 0xffff0000u)) : ((lo & 0xffffu) | (hi << 16));
+    }
+  }
+}
+
+__device__ __forceinline__ void transpose_block(const u32x4 (&in)[4], u32x4 (&out)[4]) {
+  // 4x4 of 32-bit.
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) out[j][q] = in[q][j];
+  }
+}
+
+// Global -> register -> LDS staging of one ROWS x BK operand tile.
+template <class C, int ROWS, bool KMAJOR>
+struct Loader;
+
+template <class C, int ROWS>
+struct Loader<C, ROWS, true> {
+  typedef typename C::Elem T;
+  static constexpr int VEC = C::VEC;
+  static constexpr int VPR = C::BK / VEC;      // vectors per row
+  static constexpr int RSTEP = C::NT / VPR;    // rows between a thread's vectors
+  static constexpr int NREG = ROWS / RSTEP;
+  static_assert(C::NT % VPR == 0 && ROWS % RSTEP == 0, "K-major loader geometry");
+  u32x4 r[NREG];
+  const T* base;
+  int row0, kv;
+
+  __device__ __forceinline__ void init(const Opnd<T>& op, int mn0, int tid) {
+    kv = (tid % VPR) * VEC;
+    row0 = tid / VPR;
+    base = op.p + static_cast<int64_t>(mn0 + row0) * op.ld + kv;
+  }
+  __device__ __forceinline__ void load(const Opnd<T>& op, int mn0, int k0) {
+    const bool kok = k0 + kv < op.k_ext;
+#pragma unroll
+    for (int i = 0; i < NREG; ++i) {
+      const bool ok = kok && (mn0 + row0 + i * RSTEP < op.mn_ext);
+      u32x4 v = {0u, 0u, 0u, 0u};
+      if (ok) v = *reinterpret_cast<const u32x4*>(base + static_cast<int64_t>(i * RSTEP) * op.ld + k0);
+      r[i] = v;
+    }
+  }
+  __device__ __forceinline__ void store(T* lds) const {
+#pragma unroll
+    for (int i = 0; i < NREG; ++i)
+      *reinterpret_cast<u32x4*>(lds + (row0 + i * RSTEP) * C::LDK + kv) = r[i];
+  }
+};
+
+template <class C, int ROWS>
+struct Loader<C, ROWS, false> {
+  typedef typename C::Elem T;
+  static constexpr int VEC = C::VEC;
+  static constexpr int BPR = ROWS / VEC;           // VEC x VEC blocks along mn
+  static constexpr int KSTEP = C::NT / BPR;        // k-blocks between a thread's blocks
+  static constexpr int NBLK = (C::BK / VEC) / KSTEP;
+  static constexpr int NREG = NBLK * VEC;
+  static_assert(C::NT % BPR == 0 && (C::BK / VEC) % KSTEP == 0 && NBLK >= 1,
+                "MN-major loader geometry");
+  u32x4 r[NREG];
+  const T* base;
+  int mb, kb0;
+
+  __device__ __forceinline__ void init(const Opnd<T>& op, int mn0, int tid) {
+    mb = (tid % BPR) * VEC;
+    kb0 = (tid / BPR) * VEC;
+    base = op.p + static_cast<int64_t>(kb0) * op.ld + mn0 + mb;
+  }
+  __device__ __forceinline__ void load(const Opnd<T>& op, int mn0, int k0) {
+    const bool mok = mn0 + mb < op.mn_ext;
+#pragma unroll
+    for (int b = 0; b < NBLK; ++b) {
+#pragma unroll
+      for (int rr = 0; rr < VEC; ++rr) {
+        const int kk = b * KSTEP * VEC + rr;
+        const bool ok = mok && (k0 + kb0 + kk < op.k_ext);
+        u32x4 v = {0u, 0u, 0u, 0u};
+        if (ok) v = *reinterpret_cast<const u32x4*>(base + static_cast<int64_t>(k0 + kk) * op.ld);
+        r[b * VEC + rr] = v;
+      }
+    }
+  }
+  __device__ __forceinline__ void store(T* lds) const {
+#pragma unroll
+    for (int b = 0; b < NBLK; ++b) {
+      u32x4 in[VEC], out[VEC];
+#pragma unroll
+      for (int rr = 0; rr < VEC; ++rr) in[rr] = r[b * VEC + rr];
+      transpose_block(in, out);
+      const int kcol = kb0 + b * KSTEP * VEC;
+#pragma unroll
+      for (int j = 0; j < VEC; ++j)
+        *reinterpret_cast<u32x4*>(lds + (mb + j) * C::LDK + kcol) = out[j];
+    }
+  }
+};
+
+template <class C>
+struct Acc {
+  floatx16 v[C::FM][C::FN];
+};
+
+// One BM x BN output tile: acc = A[m0:m0+BM, 0:K] . B[n0:n0+BN, 0:K]^T.
+// LDS holds two stages; global loads of step k+1 are in flight while the
+// MFMAs of step k run.  Ends with a barrier, so LDS may be reused after it.
+template <class C, bool A_KMAJOR, bool B_KMAJOR>
+__device__ __forceinline__ void gemm_tile(Acc<C>& acc, const Opnd<typename C::Elem>& A,
+                                          const Opnd<typename C::Elem>& B, int m0, int n0, int K,
+                                          typename C::Elem* lds, int tid) {
+  typedef typename C::Elem T;
+  typedef typename C::Tr Tr;
+#pragma unroll
+  for (int fm = 0; fm < C::FM; ++fm)
+#pragma unroll
+    for (int fn = 0; fn < C::FN; ++fn)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) acc.v[fm][fn][i] = 0.0f;
+  const int nk = (K + C::BK - 1) / C::BK;
+  if (nk <= 0) return;
+
+  Loader<C, C::BM, A_KMAJOR> la;
+  Loader<C, C::BN, B_KMAJOR> lb;
+  la.init(A, m0, tid);
+  lb.init(B, n0, tid);
+  la.load(A, m0, 0);
+  lb.load(B, n0, 0);
+  la.store(lds);
+  lb.store(lds + C::A_ELEMS);
+  __syncthreads();
+
+  const int lane = tid & 63, wave = tid >> 6;
+  const int wm = wave / C::WAVES_N, wn = wave % C::WAVES_N;
+  const int frow = lane & 31, fk = (lane >> 5) * 8;
+  const int a_off = (wm * C::WTM + frow) * C::LDK + fk;
+  const int b_off = (wn * C::WTN + frow) * C::LDK + fk;
+
+  for (int kt = 0; kt < nk; ++kt) {
+    const T* As = lds + (kt & 1) * C::STAGE;
+    const T* Bs = As + C::A_ELEMS;
+    const bool more = kt + 1 < nk;
+    if (more) {
+      la.load(A, m0, (kt + 1) * C::BK);
+      lb.load(B, n0, (kt + 1) * C::BK);
+    }
+#pragma unroll
+    for (int k16 = 0; k16 < C::BK / 16; ++k16) {
+      typename Tr::Frag a[C::FM], b[C::FN];
+#pragma unroll
+      for (int fm = 0; fm < C::FM; ++fm) a[fm] = Tr::frag(As + a_off + fm * 32 * C::LDK + k16 * 16);
+#pragma unroll
+      for (int fn = 0; fn < C::FN; ++fn) b[fn] = Tr::frag(Bs + b_off + fn * 32 * C::LDK + k16 * 16);
+#pragma unroll
+      for (int fm = 0; fm < C::FM; ++fm)
+#pragma unroll
+        for (int fn = 0; fn < C::FN; ++fn) Tr::mma(acc.v[fm][fn], a[fm], b[fn]);
+    }
+    if (more) {
+      T* nxt = lds + ((kt + 1) & 1) * C::STAGE;
+      la.store(nxt);
+      lb.store(nxt + C::A_ELEMS);
+    }
+    __syncthreads();
+  }
+}
+
+// ------------------------------------------------------------- tile order
+// Workgroups are dealt to the 8 XCDs round-robin by linear id.  Renumber so
+// that ids running together on one XCD are consecutive, then walk tiles in
+// groups of `gm` rows so those neighbours share A and B tiles in that XCD's L2.
+__device__ __forceinline__ int xcd_remap(int w, int G) {
+  const int q = G / kNumXCDs, r = G % kNumXCDs;
+  const int xcd = w % kNumXCDs, slot = w / kNumXCDs;
+  return (xcd < r) ? xcd * (q + 1) + slot : r * (q + 1) + (xcd - r) * q + slot;
+}
+
+__device__ __forceinline__ void grouped_tile(int l, int TM, int TN, int gm, int& tm, int& tn) {
+  const int per = gm * TN;
+  const int first = (l / per) * gm;
+  const int gs = min(TM - first, gm);
+  const int r = l % per;
+  tm = first + r % gs;
+  tn = r / gs;
+}
+
+}  // namespace fce

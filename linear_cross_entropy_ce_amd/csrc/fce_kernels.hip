@@ -1,0 +1,556 @@
+// Fused linear cross-entropy kernels for gfx950 and their launch sequence.
+//
+// Forward ("Chunked and Fused Cross-Entropy", llms.blog, "Mathematical
+// Mechanics" steps 1-2; lesson 27 "Trick 1" and "Trick 2"):
+//   k_label_scan   valid-token count D, invalid-label count, scale g/D, and a
+//                  per-token-block "has a valid label" flag
+//   k_fwd_lse      logit tiles Z = W_tile . X_tile^T on MFMA, reduced on chip
+//                  with the running max / sum-exp recurrence into one
+//                  (m, l, z_y, sum z) partial per (vocab split, token)
+//   k_lse_merge    fixed-order merge of the partials -> LSE_i and l_i, plus a
+//                  fixed-order per-256-token loss sum
+//   k_loss_final   fixed-order sum of those block sums, / D (NaN on bad labels)
+// Backward, per logit block of C_N tokens x C_V vocabulary columns in fixed
+// order (lesson 27 "Trick 2": recompute, then the two matmul-backward products):
+//   k_bwd_dz       recompute the block's logits on MFMA and write
+//                  dZ = softmax - q (unscaled) to the scratch block
+//   k_bwd_grad     dW[block vocab] (=|+=) s * dZ^T X[block tokens]   (M = vocab)
+//                  dX[block tokens] (=|+=) s * dZ W[block vocab]     (M = tokens)
+// No floating-point atomics: every sum has a fixed order, so results are
+// bitwise reproducible.
+#include "fce_kernels.h"
+
+#include <hip/hip_runtime.h>
+#include <math.h>
+
+#include "fce_gemm.h"
+
+namespace fce {
+namespace {
+
+__device__ __forceinline__ bool label_ok(int y, int ignore, int V) {
+  return y != ignore && y >= 0 && y < V;
+}
+
+// (m, l, t, z) merge: running max m, sum l of exp(z - m), target logit t,
+// logit sum z.  Either side may be empty (m = -inf, l = 0).
+__device__ __forceinline__ void lse_merge(float& m, float& l, float& t, float& z, float m2,
+                                          float l2, float t2, float z2) {
+  const float mn = fmaxf(m, m2);
+  if (mn != -INFINITY) l = l * hw_exp2((m - mn) * kLog2e) + l2 * hw_exp2((m2 - mn) * kLog2e);
+  m = mn;
+  t += t2;
+  z += z2;
+}
+
+__device__ __forceinline__ void lse_merge(floatx4& a, const floatx4& b) {
+  float m = a[0], l = a[1], t = a[2], z = a[3];
+  lse_merge(m, l, t, z, b[0], b[1], b[2], b[3]);
+  a = floatx4{m, l, t, z};
+}
+
+// ---------------------------------------------------------------- label scan
+__global__ __launch_bounds__(1024) void k_label_scan(const int32_t* __restrict__ labels, int N,
+                                                     int V, int ignore, int reduction_sum,
+                                                     const float* __restrict__ grad, Ctrl* ctrl,
+                                                     int32_t* flags, int CN, int nblocks) {
+  __shared__ int s_valid[1024], s_bad[1024];
+  const int tid = threadIdx.x;
+  for (int c = tid; c < nblocks; c += 1024) flags[c] = 0;
+  __syncthreads();
+  int nv = 0, nb = 0;
+  for (int i = tid; i < N; i += 1024) {
+    const int y = labels[i];
+    if (label_ok(y, ignore, V)) {
+      ++nv;
+      flags[i / CN] = 1;
+    } else if (y != ignore) {
+      ++nb;
+    }
+  }
+  s_valid[tid] = nv;
+  s_bad[tid] = nb;
+  __syncthreads();
+  for (int s = 512; s > 0; s >>= 1) {
+    if (tid < s) {
+      s_valid[tid] += s_valid[tid + s];
+      s_bad[tid] += s_bad[tid + s];
+    }
+    __syncthreads();
+  }
+  if (tid == 0) {
+    const int n_valid = s_valid[0];
+    const float D = reduction_sum ? 1.0f : static_cast<float>(n_valid > 0 ? n_valid : 1);
+    const float g = grad ? grad[0] : 1.0f;
+    ctrl->n_valid = n_valid;
+    ctrl->n_invalid = s_bad[0];
+    ctrl->scale_fwd = D;  // the loss is divided by D
+    ctrl->scale_bwd = g / D;
+  }
+}
+
+// ------------------------------------------------------------------ forward
+template <typename T>
+struct FwdArgs {
+  const T* X;
+  const T* W;
+  const int32_t* labels;
+  int N, H, V, ignore;
+  int tok_tiles, voc_tiles, splits, group_m;
+  int64_t n_pad;
+  floatx4* part;  // [splits][n_pad]: (m, l, z_y, sum z)
+};
+
+template <class C, bool SMOOTH>
+__global__ __launch_bounds__(C::NT) void k_fwd_lse(FwdArgs<typename C::Elem> a) {
+  typedef typename C::Elem T;
+  __shared__ __attribute__((aligned(16))) T lds[C::LDS_ELEMS];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave / C::WAVES_N, wn = wave % C::WAVES_N;
+  int tt, sp;
+  grouped_tile(xcd_remap(blockIdx.x, a.tok_tiles * a.splits), a.tok_tiles, a.splits, a.group_m,
+               tt, sp);
+  const int n0 = tt * C::BN;
+  const int vt_begin = static_cast<int>(static_cast<int64_t>(sp) * a.voc_tiles / a.splits);
+  const int vt_end = static_cast<int>(static_cast<int64_t>(sp + 1) * a.voc_tiles / a.splits);
+  const Opnd<T> A{a.W, a.H, a.V, a.H};  // rows: vocabulary
+  const Opnd<T> B{a.X, a.H, a.N, a.H};  // rows: tokens
+
+  int yv[C::FN];
+  float rm[C::FN], rl[C::FN], rt[C::FN], rz[C::FN];
+#pragma unroll
+  for (int fn = 0; fn < C::FN; ++fn) {
+    const int tok = n0 + wn * C::WTN + fn * 32 + (lane & 31);
+    const int y = tok < a.N ? a.labels[tok] : a.ignore;
+    yv[fn] = label_ok(y, a.ignore, a.V) ? y : -1;
+    rm[fn] = -INFINITY;
+    rl[fn] = rt[fn] = rz[fn] = 0.0f;
+  }
+
+  Acc<C> acc;
+  for (int vt = vt_begin; vt < vt_end; ++vt) {
+    const int m0 = vt * C::BM;
+    gemm_tile<C, true, true>(acc, A, B, m0, n0, a.H, lds, tid);
+    const int vbase = m0 + wm * C::WTM + 4 * (lane >> 5);
+    const bool full = m0 + C::BM <= a.V;
+#pragma unroll
+    for (int fn = 0; fn < C::FN; ++fn) {
+      float tmax = -INFINITY;
+#pragma unroll
+      for (int fm = 0; fm < C::FM; ++fm)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int v = vbase + fm * 32 + 8 * (i >> 2) + (i & 3);
+          if (full || v < a.V) tmax = fmaxf(tmax, acc.v[fm][fn][i]);
+        }
+      const float mnew = fmaxf(rm[fn], tmax);
+      if (mnew == -INFINITY) continue;  // nothing valid seen yet in this lane
+      float s = 0.0f, zs = 0.0f, tg = 0.0f;
+#pragma unroll
+      for (int fm = 0; fm < C::FM; ++fm)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int v = vbase + fm * 32 + 8 * (i >> 2) + (i & 3);
+          const float z = acc.v[fm][fn][i];
+          const bool ok = full || v < a.V;
+          s += ok ? hw_exp2((z - mnew) * kLog2e) : 0.0f;
+          if (SMOOTH) zs += ok ? z : 0.0f;
+          tg += (v == yv[fn]) ? z : 0.0f;
+        }
+      rl[fn] = rl[fn] * hw_exp2((rm[fn] - mnew) * kLog2e) + s;
+      rm[fn] = mnew;
+      rt[fn] += tg;
+      rz[fn] += zs;
+    }
+  }
+
+  // lanes l and l+32 hold the two halves of every 32-row block: merge them
+#pragma unroll
+  for (int fn = 0; fn < C::FN; ++fn) {
+    const float m2 = __shfl_xor(rm[fn], 32);
+    const float l2 = __shfl_xor(rl[fn], 32);
+    const float t2 = __shfl_xor(rt[fn], 32);
+    const float z2 = __shfl_xor(rz[fn], 32);
+    lse_merge(rm[fn], rl[fn], rt[fn], rz[fn], m2, l2, t2, z2);
+  }
+  // then the WAVES_M waves that share these token columns, in fixed order
+  floatx4* red = reinterpret_cast<floatx4*>(lds);  // [WAVES_M][BN]; LDS is free after gemm_tile
+  if (lane < 32) {
+#pragma unroll
+    for (int fn = 0; fn < C::FN; ++fn) {
+      floatx4 st = {rm[fn], rl[fn], rt[fn], rz[fn]};
+      red[wm * C::BN + wn * C::WTN + fn * 32 + lane] = st;
+    }
+  }
+  __syncthreads();
+  if (wm == 0 && lane < 32) {
+#pragma unroll
+    for (int fn = 0; fn < C::FN; ++fn) {
+      const int col = wn * C::WTN + fn * 32 + lane;
+      floatx4 st = red[col];
+      for (int w = 1; w < C::WAVES_M; ++w) {
+        const floatx4 o = red[w * C::BN + col];
+        lse_merge(st, o);
+      }
+      const int tok = n0 + col;
+      if (tok < a.N) a.part[static_cast<int64_t>(sp) * a.n_pad + tok] = st;
+    }
+  }
+}
+
+__global__ __launch_bounds__(kLossBlock) void k_lse_merge(
+    const floatx4* __restrict__ part, int splits, int64_t n_pad, const int32_t* __restrict__ labels,
+    int N, int V, int ignore, float eps, float* __restrict__ lse, float* __restrict__ blockloss) {
+  __shared__ float s_red[kLossBlock];
+  const int tok = blockIdx.x * kLossBlock + threadIdx.x;
+  float term = 0.0f;
+  if (tok < N) {
+    const int y = labels[tok];
+    if (label_ok(y, ignore, V)) {
+      floatx4 st = part[tok];
+      for (int s = 1; s < splits; ++s) {
+        const floatx4 o = part[static_cast<int64_t>(s) * n_pad + tok];
+        lse_merge(st, o);
+      }
+      const float L = st[0] + hw_log2(st[1]) * kLn2;
+      lse[tok] = L;
+      term = L - (1.0f - eps) * st[2];
+      if (eps != 0.0f) term -= (eps / static_cast<float>(V)) * st[3];
+    } else {
+      lse[tok] = NAN;
+    }
+  }
+  s_red[threadIdx.x] = term;
+  __syncthreads();
+  for (int s = kLossBlock / 2; s > 0; s >>= 1) {
+    if (threadIdx.x < s) s_red[threadIdx.x] += s_red[threadIdx.x + s];
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) blockloss[blockIdx.x] = s_red[0];
+}
+
+__global__ __launch_bounds__(256) void k_loss_final(const float* __restrict__ blockloss,
+                                                    int nblocks, const Ctrl* __restrict__ ctrl,
+                                                    float* __restrict__ loss) {
+  __shared__ float s_red[256];
+  float acc = 0.0f;
+  for (int b = threadIdx.x; b < nblocks; b += 256) acc += blockloss[b];
+  s_red[threadIdx.x] = acc;
+  __syncthreads();
+  for (int s = 128; s > 0; s >>= 1) {
+    if (threadIdx.x < s) s_red[threadIdx.x] += s_red[threadIdx.x + s];
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) loss[0] = ctrl->n_invalid > 0 ? NAN : s_red[0] / ctrl->scale_fwd;
+}
+
+__global__ void k_fill_zero(float* __restrict__ p, int64_t n) {
+  for (int64_t i = blockIdx.x * static_cast<int64_t>(blockDim.x) + threadIdx.x; i < n;
+       i += static_cast<int64_t>(gridDim.x) * blockDim.x)
+    p[i] = 0.0f;
+}
+
+// ------------------------------------------------------------ backward: dZ
+template <typename T>
+struct DzArgs {
+  const T* X;  // X + tok0 * H
+  const T* W;  // W + voc0 * H
+  const int32_t* labels;  // labels + tok0
+  const float* lse;       // lse + tok0
+  int ntok, nvoc, voc0, H, V, ignore;
+  float eps;
+  int voc_tiles, tok_tiles, group_m;
+  T* dz;
+  int64_t ldz;
+  const int32_t* flag;  // this token block's "has a valid label" flag
+};
+
+__device__ __forceinline__ void store4(float* p, float a, float b, float c, float d) {
+  floatx4 v = {a, b, c, d};
+  *reinterpret_cast<floatx4*>(p) = v;
+}
+__device__ __forceinline__ void store4(bf16* p, float a, float b, float c, float d) {
+  typedef bf16 bf16x4 __attribute__((ext_vector_type(4)));
+  bf16x4 v = {static_cast<bf16>(a), static_cast<bf16>(b), static_cast<bf16>(c),
+              static_cast<bf16>(d)};
+  *reinterpret_cast<bf16x4*>(p) = v;
+}
+
+template <class C>
+__global__ __launch_bounds__(C::NT) void k_bwd_dz(DzArgs<typename C::Elem> a) {
+  typedef typename C::Elem T;
+  if (*a.flag == 0) return;  // every label of this token block is ignored
+  __shared__ __attribute__((aligned(16))) T lds[C::LDS_ELEMS];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave / C::WAVES_N, wn = wave % C::WAVES_N;
+  int vt, tt;
+  grouped_tile(xcd_remap(blockIdx.x, a.voc_tiles * a.tok_tiles), a.voc_tiles, a.tok_tiles,
+               a.group_m, vt, tt);
+  const int m0 = vt * C::BM, n0 = tt * C::BN;
+  const Opnd<T> A{a.W, a.H, a.nvoc, a.H};
+  const Opnd<T> B{a.X, a.H, a.ntok, a.H};
+  Acc<C> acc;
+  gemm_tile<C, true, true>(acc, A, B, m0, n0, a.H, lds, tid);
+
+  const float eps_v = a.eps / static_cast<float>(a.V);
+  const float one_m_eps = 1.0f - a.eps;
+#pragma unroll
+  for (int fn = 0; fn < C::FN; ++fn) {
+    const int tl = n0 + wn * C::WTN + fn * 32 + (lane & 31);
+    const int y = tl < a.ntok ? a.labels[tl] : a.ignore;
+    const bool valid = tl < a.ntok && label_ok(y, a.ignore, a.V);
+    const float L = valid ? a.lse[tl] : 0.0f;
+    const int yl = valid ? y - a.voc0 : -1;  // label as a block-local column
+    T* row = a.dz + static_cast<int64_t>(tl) * a.ldz;
+#pragma unroll
+    for (int fm = 0; fm < C::FM; ++fm) {
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int v0 = m0 + wm * C::WTM + fm * 32 + 8 * g + 4 * (lane >> 5);
+        float d[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int v = v0 + q;
+          const float z = acc.v[fm][fn][4 * g + q];
+          float p = hw_exp2((z - L) * kLog2e) - eps_v;
+          if (v == yl) p -= one_m_eps;
+          d[q] = (valid && v < a.nvoc) ? p : 0.0f;
+        }
+        store4(row + v0, d[0], d[1], d[2], d[3]);
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------- backward: dW and dX
+template <typename T>
+struct GradArgs {
+  Opnd<T> A;  // dZ^T (dW) or dZ (dX)
+  Opnd<T> B;  // X^T (dW) or W^T (dX), both MN-major
+  int K;      // contraction length covered by the tile loop
+  int m_valid, n_valid;
+  int tm_tiles, tn_tiles, group_m;
+  float* out;  // first output row of this block
+  int64_t ldo;
+  const Ctrl* ctrl;
+  int accumulate;
+  const int32_t* flag;
+};
+
+template <class C, bool A_KMAJOR>
+__global__ __launch_bounds__(C::NT) void k_bwd_grad(GradArgs<typename C::Elem> a) {
+  typedef typename C::Elem T;
+  __shared__ __attribute__((aligned(16))) T lds[C::LDS_ELEMS];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave / C::WAVES_N, wn = wave % C::WAVES_N;
+  int tm, tn;
+  grouped_tile(xcd_remap(blockIdx.x, a.tm_tiles * a.tn_tiles), a.tm_tiles, a.tn_tiles, a.group_m,
+               tm, tn);
+  const int m0 = tm * C::BM, n0 = tn * C::BN;
+  const bool skip = (*a.flag == 0);  // all labels of the token block ignored: dZ = 0
+  if (skip && a.accumulate) return;
+  Acc<C> acc;
+  if (skip) {
+#pragma unroll
+    for (int fm = 0; fm < C::FM; ++fm)
+#pragma unroll
+      for (int fn = 0; fn < C::FN; ++fn)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) acc.v[fm][fn][i] = 0.0f;
+  } else {
+    gemm_tile<C, A_KMAJOR, false>(acc, a.A, a.B, m0, n0, a.K, lds, tid);
+  }
+  const float s = a.ctrl->scale_bwd;
+#pragma unroll
+  for (int fm = 0; fm < C::FM; ++fm) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int m = m0 + wm * C::WTM + fm * 32 + 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3);
+      if (m >= a.m_valid) continue;
+      float* orow = a.out + static_cast<int64_t>(m) * a.ldo;
+#pragma unroll
+      for (int fn = 0; fn < C::FN; ++fn) {
+        const int n = n0 + wn * C::WTN + fn * 32 + (lane & 31);
+        if (n < a.n_valid) {
+          const float v = s * acc.v[fm][fn][i];
+          orow[n] = a.accumulate ? orow[n] + v : v;
+        }
+      }
+    }
+  }
+}
+
+// ------------------------------------------------------------- launching
+template <typename T>
+struct ShapeOf;
+template <>
+struct ShapeOf<bf16> {
+  typedef Cfg<ShapeBf16, bf16> C;
+};
+template <>
+struct ShapeOf<float> {
+  typedef Cfg<ShapeF32, float> C;
+};
+
+int cdiv_i(int64_t a, int64_t b) { return static_cast<int>((a + b - 1) / b); }
+
+#define FCE_CHECK_LAUNCH()                      \
+  do {                                          \
+    hipError_t e_ = hipGetLastError();          \
+    if (e_ != hipSuccess) return e_;            \
+  } while (0)
+
+template <typename T>
+hipError_t run_forward(const Plan& p, const T* X, const T* W, const int32_t* labels, int ignore,
+                       float eps, float* loss, float* lse, char* ws, hipStream_t st,
+                       KernelTimer* timer) {
+  typedef typename ShapeOf<T>::C C;
+  Ctrl* ctrl = reinterpret_cast<Ctrl*>(ws + p.off_ctrl);
+  float* blockloss = reinterpret_cast<float*>(ws + p.off_blockloss);
+  floatx4* part = reinterpret_cast<floatx4*>(ws + p.off_part);
+  const int N = static_cast<int>(p.N), H = static_cast<int>(p.H), V = static_cast<int>(p.V);
+  if (N > 0) {
+    FwdArgs<T> fa{X, W, labels, N, H, V, ignore,
+                  static_cast<int>(p.fwd_tok_tiles), static_cast<int>(p.fwd_voc_tiles),
+                  static_cast<int>(p.fwd_splits), 1, p.n_pad, part};
+    // one XCD (32 CUs) covers gm token tiles x all splits
+    fa.group_m = static_cast<int>(std::max<int64_t>(1, 32 / std::max<int64_t>(p.fwd_splits, 1)));
+    const int grid = fa.tok_tiles * fa.splits;
+    const double flops = 2.0 * static_cast<double>(p.N) * p.V * p.H;
+    timer->begin("fwd_lse", flops, st);
+    if (eps != 0.0f)
+      k_fwd_lse<C, true><<<grid, C::NT, 0, st>>>(fa);
+    else
+      k_fwd_lse<C, false><<<grid, C::NT, 0, st>>>(fa);
+    FCE_CHECK_LAUNCH();
+    timer->end(st);
+    timer->begin("lse_merge", 0.0, st);
+    k_lse_merge<<<cdiv_i(N, kLossBlock), kLossBlock, 0, st>>>(part, fa.splits, p.n_pad, labels, N,
+                                                              V, ignore, eps, lse, blockloss);
+    FCE_CHECK_LAUNCH();
+    timer->end(st);
+  }
+  timer->begin("loss_final", 0.0, st);
+  k_loss_final<<<1, 256, 0, st>>>(blockloss, N > 0 ? static_cast<int>(p.n_loss_blocks) : 0, ctrl,
+                                  loss);
+  FCE_CHECK_LAUNCH();
+  timer->end(st);
+  return hipSuccess;
+}
+
+template <typename T>
+hipError_t run_backward(const Plan& p, const T* X, const T* W, const int32_t* labels, int ignore,
+                        float eps, const float* lse, float* dX, float* dW, char* ws,
+                        hipStream_t st, KernelTimer* timer) {
+  typedef typename ShapeOf<T>::C C;
+  const Ctrl* ctrl = reinterpret_cast<const Ctrl*>(ws + p.off_ctrl);
+  const int32_t* flags = reinterpret_cast<const int32_t*>(ws + p.off_flags);
+  T* dz = reinterpret_cast<T*>(ws + p.off_scratch);
+  const int64_t N = p.N, H = p.H, V = p.V;
+  if (N == 0) {
+    timer->begin("fill_zero", 0.0, st);
+    k_fill_zero<<<1024, 256, 0, st>>>(dW, V * H);
+    FCE_CHECK_LAUNCH();
+    timer->end(st);
+    return hipSuccess;
+  }
+  const int h_tiles = cdiv_i(H, C::BN);
+  for (int64_t ia = 0; ia < p.a; ++ia) {
+    const int64_t tok0 = ia * p.CN;
+    const int ntok = static_cast<int>(std::min(p.CN, N - tok0));
+    const int tok_tiles = cdiv_i(ntok, C::BN);
+    for (int64_t ib = 0; ib < p.b; ++ib) {
+      const int64_t voc0 = ib * p.CV;
+      const int nvoc = static_cast<int>(std::min(p.CV, V - voc0));
+      const int voc_tiles = cdiv_i(nvoc, C::BM);
+      const int nvoc_cov = voc_tiles * C::BM;  // columns of the block written by k_bwd_dz
+      const double blk_flops = 2.0 * static_cast<double>(ntok) * nvoc * H;
+
+      DzArgs<T> da{X + tok0 * H, W + voc0 * H, labels + tok0, lse + tok0, ntok, nvoc,
+                   static_cast<int>(voc0), static_cast<int>(H), static_cast<int>(V), ignore, eps,
+                   voc_tiles, tok_tiles, 4, dz, p.ldz, flags + ia};
+      timer->begin("bwd_dz", blk_flops, st);
+      k_bwd_dz<C><<<voc_tiles * tok_tiles, C::NT, 0, st>>>(da);
+      FCE_CHECK_LAUNCH();
+      timer->end(st);
+
+      // dW[voc0 : voc0+nvoc] (=|+=) s * dZ^T X[tok0 : tok0+ntok]
+      GradArgs<T> gw;
+      gw.A = Opnd<T>{dz, p.ldz, nvoc, ntok};                         // (v, t) at dz[t*ldz + v]
+      gw.B = Opnd<T>{X + tok0 * H, H, static_cast<int>(H), ntok};    // (h, t) at X[t*H + h]
+      gw.K = ntok;
+      gw.m_valid = nvoc;
+      gw.n_valid = static_cast<int>(H);
+      gw.tm_tiles = voc_tiles;
+      gw.tn_tiles = h_tiles;
+      gw.group_m = 2;
+      gw.out = dW + voc0 * H;
+      gw.ldo = H;
+      gw.ctrl = ctrl;
+      gw.accumulate = ia > 0;
+      gw.flag = flags + ia;
+      timer->begin("bwd_dw", blk_flops, st);
+      k_bwd_grad<C, false><<<voc_tiles * h_tiles, C::NT, 0, st>>>(gw);
+      FCE_CHECK_LAUNCH();
+      timer->end(st);
+
+      // dX[tok0 : tok0+ntok] (=|+=) s * dZ W[voc0 : voc0+nvoc]
+      GradArgs<T> gx;
+      gx.A = Opnd<T>{dz, p.ldz, ntok, nvoc_cov};                      // (t, v) at dz[t*ldz + v]
+      gx.B = Opnd<T>{W + voc0 * H, H, static_cast<int>(H), nvoc};     // (h, v) at W[v*H + h]
+      gx.K = nvoc_cov;
+      gx.m_valid = ntok;
+      gx.n_valid = static_cast<int>(H);
+      gx.tm_tiles = tok_tiles;
+      gx.tn_tiles = h_tiles;
+      gx.group_m = 2;
+      gx.out = dX + tok0 * H;
+      gx.ldo = H;
+      gx.ctrl = ctrl;
+      gx.accumulate = ib > 0;
+      gx.flag = flags + ia;
+      timer->begin("bwd_dx", blk_flops, st);
+      k_bwd_grad<C, true><<<tok_tiles * h_tiles, C::NT, 0, st>>>(gx);
+      FCE_CHECK_LAUNCH();
+      timer->end(st);
+    }
+  }
+  return hipSuccess;
+}
+
+}  // namespace
+
+hipError_t launch_label_scan(const Plan& p, const int32_t* labels, int ignore, int reduction_sum,
+                             const float* grad, char* ws, hipStream_t st, KernelTimer* timer) {
+  Ctrl* ctrl = reinterpret_cast<Ctrl*>(ws + p.off_ctrl);
+  int32_t* flags = reinterpret_cast<int32_t*>(ws + p.off_flags);
+  timer->begin("label_scan", 0.0, st);
+  k_label_scan<<<1, 1024, 0, st>>>(labels, static_cast<int>(p.N), static_cast<int>(p.V), ignore,
+                                   reduction_sum, grad, ctrl, flags, static_cast<int>(p.CN),
+                                   static_cast<int>(std::max<int64_t>(p.a, 1)));
+  FCE_CHECK_LAUNCH();
+  timer->end(st);
+  return hipSuccess;
+}
+
+hipError_t launch_forward(const Plan& p, const void* X, const void* W, const int32_t* labels,
+                          int ignore, float eps, float* loss, float* lse, char* ws, hipStream_t st,
+                          KernelTimer* timer) {
+  if (p.dtype == Dtype::BF16)
+    return run_forward<bf16>(p, static_cast<const bf16*>(X), static_cast<const bf16*>(W), labels,
+                             ignore, eps, loss, lse, ws, st, timer);
+  return run_forward<float>(p, static_cast<const float*>(X), static_cast<const float*>(W), labels,
+                            ignore, eps, loss, lse, ws, st, timer);
+}
+
+hipError_t launch_backward(const Plan& p, const void* X, const void* W, const int32_t* labels,
+                           int ignore, float eps, const float* lse, float* dX, float* dW, char* ws,
+                           hipStream_t st, KernelTimer* timer) {
+  if (p.dtype == Dtype::BF16)
+    return run_backward<bf16>(p, static_cast<const bf16*>(X), static_cast<const bf16*>(W), labels,
+                              ignore, eps, lse, dX, dW, ws, st, timer);
+  return run_backward<float>(p, static_cast<const float*>(X), static_cast<const float*>(W), labels,
+                             ignore, eps, lse, dX, dW, ws, st, timer);
+}
+
+}  // namespace fce

@@ -1,0 +1,178 @@
+// Planner for fused linear cross-entropy.
+//
+// Backward block shape.  The pages chunk over tokens only: each chunk of C
+// tokens produces a C x V logit slice, then dX_c = dZ_c W and dW += dZ_c^T X_c
+// ("Chunked and Fused Cross-Entropy", llms.blog, "Mathematical Mechanics",
+// steps 1 and 4; lesson 27, "Trick 2").  Every token chunk after the first
+// re-reads and re-writes the whole fp32 dW (8 V H bytes), which on MI355X
+// makes the dW product bandwidth-bound for C <= 1024.  The planner keeps the
+// pages' logit-space budget of chunk x V elements but lets the block be
+// C_N tokens x C_V vocabulary columns: vocabulary blocks re-read dX (N x H)
+// instead of dW (V x H), which is an order of magnitude smaller at the
+// large-vocabulary shapes.  The shape is picked by a simple time model
+// (MFMA work with wave quantisation over 256 CUs plus fp32 RMW bytes).
+#include "fce_plan.h"
+
+#include <algorithm>
+#include <cmath>
+#include <limits>
+
+#include "fce_tiles.h"
+
+namespace fce {
+namespace {
+
+constexpr size_t kAlign = 256;
+
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+int64_t round_up(int64_t a, int64_t b) { return cdiv(a, b) * b; }
+
+// Modelled time of one backward schedule, in seconds.  Only the ranking of
+// candidates matters.
+double model_time(const Plan& p, int64_t CN, int64_t CV, int64_t a, int64_t b) {
+  const double peak = (p.dtype == Dtype::BF16) ? 2.5e15 : 1.5e14;
+  const double bw = 5.0e12;
+  const double t = static_cast<double>(p.tile);
+  const double per_cu = peak / kNumCUs;
+  auto waves = [](int64_t tiles) { return static_cast<double>(cdiv(tiles, kNumCUs)); };
+  const int64_t h_tiles = cdiv(p.H, p.tile);
+  double time = 0.0;
+  for (int64_t ia = 0; ia < a; ++ia) {
+    const int64_t cn = std::min(CN, p.N - ia * CN);
+    const int64_t tn = cdiv(cn, p.tile);
+    for (int64_t ib = 0; ib < b; ++ib) {
+      const int64_t cv = std::min(CV, p.V - ib * CV);
+      const int64_t tv = cdiv(cv, p.tile);
+      time += waves(tn * tv) * 2.0 * t * t * static_cast<double>(p.H) / per_cu;      // recompute
+      time += waves(tv * h_tiles) * 2.0 * t * t * static_cast<double>(tn * p.tile) / per_cu;  // dW
+      time += waves(tn * h_tiles) * 2.0 * t * t * static_cast<double>(tv * p.tile) / per_cu;  // dX
+    }
+  }
+  const double rmw = 4.0 * static_cast<double>(p.V * p.H) * static_cast<double>(2 * a - 1) +
+                     4.0 * static_cast<double>(p.N * p.H) * static_cast<double>(2 * b - 1);
+  return time + rmw / bw;
+}
+
+}  // namespace
+
+bool make_plan(int64_t N, int64_t H, int64_t V, Dtype dtype, int64_t chunk, Schedule sched,
+               Plan* out) {
+  if (!out || N < 0 || H < 1 || V < 1 || chunk < 1) return false;
+  // Index arithmetic inside the kernels uses 64-bit row offsets, but tile
+  // coordinates are 32-bit: keep every extent comfortably inside int32.
+  const int64_t lim = static_cast<int64_t>(1) << 30;
+  if (N >= lim || H >= lim || V >= lim) return false;
+  Plan p;
+  p.N = N;
+  p.H = H;
+  p.V = V;
+  p.dtype = dtype;
+  p.elem_bytes = (dtype == Dtype::BF16) ? 2 : 4;
+  const int64_t BM = (dtype == Dtype::BF16) ? ShapeBf16::BM : ShapeF32::BM;
+  const int64_t BN = (dtype == Dtype::BF16) ? ShapeBf16::BN : ShapeF32::BN;
+  p.tile = std::max(BM, BN);
+
+  // ---- forward grid: minimise ceil(tiles/CUs) * vocab tiles per split
+  p.fwd_tok_tiles = cdiv(N, BN);
+  p.fwd_voc_tiles = cdiv(V, BM);
+  p.n_pad = std::max<int64_t>(p.fwd_tok_tiles, 1) * BN;
+  if (N > 0) {
+    int64_t best = 1;
+    double best_cost = std::numeric_limits<double>::infinity();
+    const int64_t smax = std::min<int64_t>(p.fwd_voc_tiles, 4 * kNumCUs);
+    for (int64_t s = 1; s <= smax; ++s) {
+      const double cost = static_cast<double>(cdiv(p.fwd_tok_tiles * s, kNumCUs)) *
+                          static_cast<double>(cdiv(p.fwd_voc_tiles, s));
+      if (cost < best_cost - 1e-9) {
+        best_cost = cost;
+        best = s;
+      }
+    }
+    p.fwd_splits = best;
+  } else {
+    p.fwd_splits = 1;
+  }
+
+  // ---- backward block
+  const int64_t G = p.tile;
+  const double budget = static_cast<double>(chunk) * static_cast<double>(V);
+  const int64_t Vp = round_up(V, G);
+  if (N == 0) {
+    p.CN = G;
+    p.CV = Vp;
+    p.a = 0;
+    p.b = 1;
+  } else if (chunk >= N) {
+    p.CN = round_up(N, G);
+    p.CV = Vp;
+    p.a = 1;
+    p.b = 1;
+  } else {
+    auto vocab_split = [&](int64_t CN, int64_t* CV, int64_t* b) {
+      int64_t cv_max = static_cast<int64_t>(std::floor(budget / static_cast<double>(CN) / G)) * G;
+      cv_max = std::max(cv_max, G);  // never below one tile
+      *b = cdiv(V, cv_max);
+      *CV = round_up(cdiv(V, *b), G);
+    };
+    if (sched == Schedule::Token) {
+      p.CN = round_up(chunk, G);
+      p.a = cdiv(N, p.CN);
+      p.CV = Vp;
+      p.b = 1;
+    } else if (sched == Schedule::Vocab) {
+      p.CN = round_up(N, G);
+      p.a = 1;
+      vocab_split(p.CN, &p.CV, &p.b);
+    } else if (sched == Schedule::Auto) {
+      double best = std::numeric_limits<double>::infinity();
+      const int64_t amax = cdiv(N, G);
+      for (int64_t a = 1; a <= amax; ++a) {
+        const int64_t CN = round_up(cdiv(N, a), G);
+        const int64_t aa = cdiv(N, CN);
+        if (aa != a) continue;  // same block height as a smaller a
+        int64_t CV, b;
+        vocab_split(CN, &CV, &b);
+        const double t = model_time(p, CN, CV, aa, b);
+        if (t < best * (1.0 - 1e-9)) {
+          best = t;
+          p.CN = CN;
+          p.CV = CV;
+          p.a = aa;
+          p.b = b;
+        }
+      }
+    } else {
+      return false;
+    }
+  }
+  p.scratch_rows = p.CN;
+  p.ldz = p.CV;
+  p.grad_rmw_bytes = (N == 0) ? 4 * V * H
+                              : 4 * V * H * (2 * p.a - 1) + 4 * N * H * (2 * p.b - 1);
+
+  // ---- workspace layout
+  size_t off = 0;
+  p.off_ctrl = off;
+  off = align_up(off + sizeof(Ctrl));
+  p.off_flags = off;
+  off = align_up(off + sizeof(int32_t) * static_cast<size_t>(std::max<int64_t>(p.a, 1)));
+  p.off_part = off;
+  p.partial_bytes = static_cast<size_t>(p.fwd_splits) * static_cast<size_t>(p.n_pad) * 16u;
+  off = align_up(off + p.partial_bytes);
+  p.n_loss_blocks = cdiv(std::max<int64_t>(N, 1), kLossBlock);
+  p.off_blockloss = off;
+  off = align_up(off + sizeof(float) * static_cast<size_t>(p.n_loss_blocks));
+  p.off_lse = off;
+  off = align_up(off + sizeof(float) * static_cast<size_t>(std::max<int64_t>(N, 1)));
+  p.off_scratch = off;
+  p.scratch_bytes = (N == 0) ? 0
+                             : static_cast<size_t>(p.scratch_rows) * static_cast<size_t>(p.ldz) *
+                                   static_cast<size_t>(p.elem_bytes);
+  off = align_up(off + p.scratch_bytes);
+  p.total = off;
+  *out = p;
+  return true;
+}
+
+}  // namespace fce

@@ -1,0 +1,53 @@
+// Host-side planning of a fused linear cross-entropy call: tile grid of the
+// forward reduction, shape of the backward logit block, workspace layout.
+// Pure C++ (no HIP), so it can be unit-tested and sanitised on the host.
+#pragma once
+
+#include <cstddef>
+#include <cstdint>
+
+namespace fce {
+
+enum class Dtype : int { F32 = 0, BF16 = 1 };
+enum class Schedule : int { Auto = 0, Token = 1, Vocab = 2 };
+
+struct Plan {
+  int64_t N = 0, H = 0, V = 0;
+  Dtype dtype = Dtype::BF16;
+  int64_t elem_bytes = 2;
+
+  // forward: token tiles x vocabulary splits, each split walks a range of vocab tiles
+  int64_t fwd_tok_tiles = 0;
+  int64_t fwd_voc_tiles = 0;
+  int64_t fwd_splits = 0;
+  int64_t n_pad = 0;  // fwd_tok_tiles * BN: row pitch of the partials
+
+  // backward logit block: C_N tokens x C_V vocabulary columns
+  int64_t tile = 0;  // padding granularity of both block dimensions
+  int64_t CN = 0, CV = 0;
+  int64_t a = 0, b = 0;  // number of token blocks, vocabulary blocks
+  int64_t scratch_rows = 0, ldz = 0;
+
+  // workspace layout (byte offsets, 256-byte aligned)
+  size_t off_ctrl = 0, off_flags = 0, off_part = 0, off_blockloss = 0, off_lse = 0,
+         off_scratch = 0, total = 0;
+  size_t scratch_bytes = 0, partial_bytes = 0;
+  int64_t n_loss_blocks = 0;
+  int64_t grad_rmw_bytes = 0;
+};
+
+// Layout of the small control block at the start of the workspace.
+struct Ctrl {
+  int32_t n_valid;
+  int32_t n_invalid;
+  float scale_fwd;  // 1 / D
+  float scale_bwd;  // g / D
+};
+
+constexpr int kLossBlock = 256;  // tokens per block of the loss reduction
+
+// Returns false if the arguments are invalid (shapes, chunk, overflow).
+bool make_plan(int64_t N, int64_t H, int64_t V, Dtype dtype, int64_t chunk, Schedule sched,
+               Plan* out);
+
+}  // namespace fce

@@ -1,0 +1,155 @@
+"""Host-side checks of the C-ABI library (no GPU needed).
+
+The library loads, exports every function include/fce.h declares, plans
+consistently, and rejects bad arguments with its status codes before
+touching the device (fake device pointers are never dereferenced here)."""
+import ctypes
+import json
+import math
+import os
+import re
+
+import pytest
+
+import linear_cross_entropy_ce_amd as fce
+from linear_cross_entropy_ce_amd import _binding as B
+from linear_cross_entropy_ce_amd import memory
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+GOLDEN = os.path.join(ROOT, "tests", "golden")
+
+
+def _declared_functions():
+    text = open(os.path.join(ROOT, "include", "fce.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(fce_[a-z_]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_function():
+    lib = B.load_library()
+    names = _declared_functions()
+    assert len(names) >= 9
+    for n in names:
+        assert hasattr(lib, n), n
+    assert set(B.EXPORTED) == set(names)
+
+
+def test_status_strings():
+    for s in range(-7, 1):
+        assert B.status_string(s) and B.status_string(s) != "unknown status"
+
+
+FAKE = 0x10000  # 16-byte aligned, never dereferenced by the validation path
+
+
+def _fwd(N=64, H=64, V=100, dtype=B.FCE_BF16, eps=0.0, red=B.FCE_MEAN, chunk=16,
+         sched=B.SCHED_AUTO, X=FAKE, W=FAKE, labels=FAKE, loss=FAKE, lse=FAKE, ws=FAKE,
+         ws_bytes=None):
+    lib = B.load_library()
+    if ws_bytes is None:
+        ws_bytes = max(lib.fce_workspace_size(max(N, 0), max(H, 1), max(V, 1), dtype if dtype in (0, 1) else 1,
+                                              max(chunk, 1), sched if sched in (0, 1, 2) else 0), 1)
+    return lib.fce_forward(X, W, labels, N, H, V, dtype, -100, eps, red, chunk, sched, loss, lse,
+                           ws, ws_bytes, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(N=-1), B.FCE_ERR_SHAPE), (dict(H=0), B.FCE_ERR_SHAPE), (dict(V=0), B.FCE_ERR_SHAPE),
+    (dict(W=None), B.FCE_ERR_NULL), (dict(X=None), B.FCE_ERR_NULL),
+    (dict(labels=None), B.FCE_ERR_NULL), (dict(ws=None), B.FCE_ERR_NULL),
+    (dict(loss=None), B.FCE_ERR_NULL), (dict(lse=None), B.FCE_ERR_NULL),
+    (dict(dtype=7), B.FCE_ERR_ARG), (dict(red=3), B.FCE_ERR_ARG), (dict(sched=9), B.FCE_ERR_ARG),
+    (dict(chunk=0), B.FCE_ERR_ARG), (dict(eps=1.0), B.FCE_ERR_ARG), (dict(eps=-0.1), B.FCE_ERR_ARG),
+    (dict(eps=float("nan")), B.FCE_ERR_ARG),
+    (dict(H=60), B.FCE_ERR_ALIGN), (dict(H=62, dtype=B.FCE_F32), B.FCE_ERR_ALIGN),
+    (dict(W=FAKE + 8), B.FCE_ERR_ALIGN), (dict(X=FAKE + 2), B.FCE_ERR_ALIGN),
+    (dict(ws=FAKE + 4), B.FCE_ERR_ALIGN), (dict(ws_bytes=100), B.FCE_ERR_WORKSPACE),
+])
+def test_forward_rejects_bad_arguments(kw, status):
+    assert _fwd(**kw) == status
+
+
+def test_backward_and_fused_reject_bad_arguments():
+    lib = B.load_library()
+    ws = lib.fce_workspace_size(64, 64, 100, 1, 16, 0)
+    # dW missing
+    assert lib.fce_backward(FAKE, FAKE, FAKE, 64, 64, 100, 1, -100, 0.0, 0, 16, 0, FAKE, None,
+                            FAKE, None, FAKE, ws, None) == B.FCE_ERR_NULL
+    # misaligned dX
+    assert lib.fce_backward(FAKE, FAKE, FAKE, 64, 64, 100, 1, -100, 0.0, 0, 16, 0, FAKE, None,
+                            FAKE + 4, FAKE, FAKE, ws, None) == B.FCE_ERR_ALIGN
+    assert lib.fce_fused_fwd_bwd(FAKE, FAKE, FAKE, 64, 64, 100, 1, -100, 0.0, 0, 16, 0, FAKE,
+                                 FAKE, FAKE, FAKE, ws - 1, None) == B.FCE_ERR_WORKSPACE
+    assert lib.fce_fused_fwd_bwd(FAKE, FAKE, FAKE, 64, 64, 100, 1, -100, 0.5, 0, 16, 0, None,
+                                 FAKE, FAKE, FAKE, ws, None) == B.FCE_ERR_NULL
+    n = ctypes.c_int32(0)
+    assert lib.fce_get_label_errors(None, ctypes.byref(n), None) == B.FCE_ERR_NULL
+
+
+@pytest.mark.parametrize("N,H,V,dtype,chunk", [
+    (8192, 4096, 128256, 1, 1024), (8192, 4096, 128256, 1, 256), (4096, 2048, 32000, 1, 1024),
+    (16384, 3584, 152064, 1, 1024), (32768, 2304, 256000, 1, 1024), (256, 128, 4096, 0, 1024),
+    (777, 264, 5003, 1, 100), (1, 8, 1, 1, 1), (0, 8, 10, 1, 4), (5000, 64, 300, 0, 7)])
+@pytest.mark.parametrize("sched", ["auto", "token", "vocab"])
+def test_plan_invariants(N, H, V, dtype, chunk, sched):
+    p = fce.fce_plan(N, H, V, dtype, chunk, B.SCHEDULES[sched])
+    tile = 256 if dtype == 1 else 128
+    eb = 2 if dtype == 1 else 4
+    assert p["workspace_bytes"] == fce.fce_workspace_size(N, H, V, dtype, chunk, B.SCHEDULES[sched])
+    CN, CV, a, b = p["block_tokens"], p["block_vocab"], p["n_token_blocks"], p["n_vocab_blocks"]
+    assert CN % tile == 0 and CV % tile == 0
+    if N == 0:
+        assert a == 0 and p["scratch_bytes"] == 0
+        return
+    assert a * CN >= N and (a - 1) * CN < N
+    assert b * CV >= V and (b - 1) * CV < V
+    assert p["scratch_bytes"] == CN * CV * eb
+    if chunk >= N:
+        assert a == 1 and b == 1
+    elif sched == "token":
+        assert b == 1 and CN == -(-chunk // tile) * tile
+    else:
+        # the block never exceeds the chunk x V budget (at least one tile pair)
+        assert CN * CV <= max(chunk * V, tile * tile) or CV == tile
+        if sched == "vocab":
+            assert a == 1
+    assert p["grad_rmw_bytes"] == 4 * V * H * (2 * a - 1) + 4 * N * H * (2 * b - 1)
+    assert p["workspace_bytes"] >= p["scratch_bytes"] + p["partial_bytes"]
+
+
+def test_plan_rejects_bad_arguments():
+    lib = B.load_library()
+    info = B.PlanInfo()
+    assert lib.fce_plan(10, 8, 10, 1, 0, 0, ctypes.byref(info)) == B.FCE_ERR_ARG
+    assert lib.fce_plan(-1, 8, 10, 1, 4, 0, ctypes.byref(info)) == B.FCE_ERR_SHAPE
+    assert lib.fce_plan(10, 8, 10, 1, 4, 0, None) == B.FCE_ERR_NULL
+    assert lib.fce_workspace_size(10, 8, 10, 5, 4, 0) == 0
+
+
+# ------------------------------------------------------------ memory figures
+def _figures():
+    return json.load(open(os.path.join(GOLDEN, "memory_figures.json")))
+
+
+@pytest.mark.parametrize("fig", _figures()["figures"], ids=lambda f: f["cite"][:60])
+def test_memory_figures_printed_on_the_pages(fig):
+    b = memory.logit_space_bytes(fig["rows"], fig["V"], fig["bytes"], fig["copies"])
+    assert round(b / 1e9, fig["digits"]) == pytest.approx(fig["printed_GB"], abs=1e-9), fig["cite"]
+
+
+def test_element_counts_printed_on_the_pages():
+    for e in _figures()["element_counts"]:
+        assert e["rows"] * e["V"] == e["printed"], e["cite"]
+
+
+def test_token_schedule_scratch_is_one_chunk():
+    # The fully fused path holds one chunk of logits: 1024 x 128,256 bf16.
+    c = _figures()["chunk_scratch"]
+    p = fce.fce_plan(c["N"], c["H"], c["V"], B.FCE_BF16, c["chunk"], B.SCHED_TOKEN)
+    assert p["scratch_bytes"] == c["bytes"]
+    assert round(p["scratch_bytes"] / 1e9, 2) == 0.26
+    # and the automatic block shape stays within the same budget
+    p = fce.fce_plan(c["N"], c["H"], c["V"], B.FCE_BF16, c["chunk"], B.SCHED_AUTO)
+    assert p["scratch_bytes"] <= c["bytes"]
+    rep = memory.report(c["N"], c["V"], 2, p["scratch_bytes"])
+    assert math.isclose(rep["naive_3x_bytes"] / 1e9, 6.3, abs_tol=0.05)
