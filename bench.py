@@ -1,0 +1,205 @@
+"""Benchmark of the fused linear cross-entropy forward+backward on one MI355X.
+
+One step = one fce_fused_fwd_bwd call over one synthetic batch (label scan,
+forward logit tiles with the on-chip LSE reduction, LSE merge and loss, then
+the backward recompute, dW and dX products for every logit block).  Inputs
+and outputs are resident in device memory before the timed region.
+
+Prints ONE JSON line on stdout; progress goes to stderr.
+
+    python bench.py [--gpus 1] [--steps 20] [--warmup 3] [--workload 3]
+                    [--chunk 1024] [--schedule auto] [--cpu-sample-tokens 1024]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK = {"bf16": 2516.6, "fp32": 157.3}  # MI355X dense MFMA TFLOP/s (256 CUs x 2.4 GHz)
+HBM_PEAK_GBS = 8000.0
+CSRC = os.path.join(ROOT, "linear_cross_entropy_ce_amd", "csrc")
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def source_digest() -> str:
+    h = hashlib.sha256()
+    for name in sorted(os.listdir(CSRC)):
+        with open(os.path.join(CSRC, name), "rb") as f:
+            h.update(name.encode())
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def read_traffic(kernel: str, workload: str, launches_per_step: float):
+    """HBM bytes per launch of ``kernel`` from the committed rocprofv3 PMC
+    summary, or None when it is missing or was taken on other kernel sources."""
+    path = os.path.join(ROOT, "profiles", f"{kernel}_{workload}_traffic.json")
+    if not os.path.exists(path):
+        return None
+    try:
+        rec = json.load(open(path))
+    except (OSError, ValueError):
+        return None
+    if rec.get("source_sha256") != source_digest():
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(wl, inp, n_tokens: int):
+    """The fp64 oracle as it stands, on the first n_tokens rows of the same
+    workload (full vocabulary and hidden size)."""
+    import oracle.fce_oracle as orc
+    import workloads as wk
+
+    try:
+        from threadpoolctl import threadpool_info
+
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()
+                       if i.get("user_api") == "blas"] or [1])
+    except Exception:  # pragma: no cover
+        threads = os.cpu_count() or 1
+    n = min(n_tokens, wl.N)
+    X, y = inp.X[:n], inp.labels[:n]
+    t0 = time.perf_counter()
+    orc.linear_cross_entropy(X, inp.W, y, wk.IGNORE_INDEX, wl.label_smoothing, "mean")
+    dt = time.perf_counter() - t0
+    return {"value": n / dt, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"first {n} of {wl.N} tokens of {wl.name} (full V={wl.V}, H={wl.H}); "
+                      f"fp64 numpy, {6 * n * wl.V * wl.H / 1e12:.2f} TFLOP executed in {dt:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", type=int, default=3)
+    ap.add_argument("--chunk", type=int, default=1024)
+    ap.add_argument("--schedule", default="auto", choices=["auto", "token", "vocab"])
+    ap.add_argument("--cpu-sample-tokens", type=int, default=4096)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import linear_cross_entropy_ce_amd as fce
+    import workloads as wk
+
+    fce.load_library()
+    wl = wk.WORKLOADS[args.workload]
+    log(f"drawing inputs for {wl.name} (N={wl.N}, H={wl.H}, V={wl.V}, {wl.dtype})")
+    inp = wk.draw(wl)
+    X, W, y = wk.to_torch(inp, "cuda")
+    N, H, V = wl.N, wl.H, wl.V
+    chunk, sched = args.chunk, args.schedule
+    plan = fce.fce_plan(N, H, V, fce.FCE_BF16 if wl.dtype == "bf16" else fce.FCE_F32, chunk,
+                        fce.SCHEDULES[sched])
+    log(f"plan: {plan}")
+    ws = fce.workspace_for(N, H, V, X.dtype, chunk, sched)
+    loss = torch.empty(1, device="cuda")
+    dX = torch.empty((N, H), device="cuda")
+    dW = torch.empty((V, H), device="cuda")
+    eps = wl.label_smoothing
+
+    def step():
+        fce.fce_fused_fwd_bwd(X, W, y, loss, dX, dW, ws, wk.IGNORE_INDEX, eps, "mean", chunk, sched)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    log(f"warmup done, loss {loss.item():.6f}")
+
+    stream = torch.cuda.current_stream()
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    fce.fce_timing_enable(True)
+    torch.cuda.synchronize()
+    t_start.record(stream)
+    for _ in range(args.steps):
+        step()
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    kernels = fce.fce_timing_read()
+    fce.fce_timing_enable(False)
+    total_ms = t_start.elapsed_time(t_end)
+    ms = total_ms / args.steps
+    tokens_per_s = N / (ms / 1e3)
+    flops_step = 8.0 * N * V * H
+    peak = PEAK[wl.dtype]
+    tflops = flops_step / (ms / 1e3) / 1e12
+    log(f"{args.steps} steps: {ms:.3f} ms/step, {tokens_per_s:,.0f} tokens/s, "
+        f"{tflops:.1f} TFLOP/s = {100 * tflops / peak:.1f}% of {peak} TFLOP/s")
+
+    # dominant kernel: largest share of the timed region
+    kern = {}
+    for name, r in kernels.items():
+        avg = r["total_ms"] / max(r["launches"], 1)
+        kern[name] = {"launches_per_step": r["launches"] / args.steps,
+                      "ms_per_step": r["total_ms"] / args.steps, "avg_launch_ms": avg,
+                      "tflops": (r["flops"] / (r["total_ms"] / 1e3) / 1e12) if r["flops"] else None}
+        log(f"  {name:12s} {r['launches'] / args.steps:6.1f} launches/step "
+            f"{r['total_ms'] / args.steps:9.3f} ms/step  avg {avg * 1e3:9.1f} us"
+            + (f"  {kern[name]['tflops']:8.1f} TFLOP/s" if r["flops"] else ""))
+    dom = max(kern, key=lambda k: kern[k]["ms_per_step"])
+    dom_r = kernels[dom]
+    achieved = dom_r["flops"] / dom_r["launches"] / (dom_r["total_ms"] / dom_r["launches"] / 1e3) / 1e12
+    traffic = read_traffic(dom, wl.name, kern[dom]["launches_per_step"])
+    roofline = {"bound": "mfma", "kernel": dom, "achieved": round(achieved, 2), "peak": peak,
+                "unit": "TFLOP/s", "frac": round(achieved / peak, 4), "traffic": traffic}
+
+    mem = {"logit_scratch_bytes": plan["scratch_bytes"],
+           "naive_logits_bytes": N * V * (2 if wl.dtype == "bf16" else 4),
+           "naive_3x_bytes": 3 * N * V * (2 if wl.dtype == "bf16" else 4),
+           "chunk_tile_bound_bytes": chunk * V * (2 if wl.dtype == "bf16" else 4)}
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        log(f"timing the CPU oracle on {args.cpu_sample_tokens} tokens ...")
+        cpu = cpu_baseline(wl, inp, args.cpu_sample_tokens)
+        log(f"  {cpu}")
+
+    out = {
+        "metric": "tokens/s + % bf16 MFMA peak, fused CE fwd+bwd, N=8192 H=4096 V=128256",
+        "value": round(tokens_per_s, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": wl.dtype,
+        "data": "synthetic",
+        "config": {"workload": f"{wl.name} fused CE fwd+bwd N={N} H={H} V={V}",
+                   "N": N, "H": H, "V": V, "chunk": chunk, "schedule": sched,
+                   "block_tokens": plan["block_tokens"], "block_vocab": plan["block_vocab"],
+                   "label_smoothing": eps, "ignored_tokens": wl.n_ignored,
+                   "parallelism": "single GPU"},
+        "pct_peak_bf16_mfma": round(100 * tflops / peak, 2),
+        "tflops_8NVH": round(tflops, 2),
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "kernels": kern,
+        "memory": mem,
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()
