@@ -131,7 +131,25 @@ __device__ __forceinline__ void transpose_block(const u32x4 (&in)[4], u32x4 (&ou
   }
 }
 
-// Global -> register -> LDS staging of one ROWS x BK operand tile.
+// Buffer resource covering `bytes` from `base` (gfx9 raw buffer: stride 0,
+// word 3 = 0x00020000).  Loads at offsets >= the record count return zero,
+// which supplies the zero fill of ragged tiles without branches.  The count
+// is clamped to 2^31 - 1 so that kOOB below is always out of range.
+constexpr uint32_t kOOB = 0x80000000u;
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int64_t bytes) {
+  const int64_t n = bytes < 0 ? 0 : (bytes > 0x7fffffff ? 0x7fffffff : bytes);
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, static_cast<int>(n),
+                                           0x00020000);
+}
+
+__device__ __forceinline__ u32x4 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+}
+
+// Global -> register -> LDS staging of one ROWS x BK operand tile.  Each K
+// step gets a buffer descriptor based at the step's first element, so all
+// per-lane offsets are small constants of the tile.
 template <class C, int ROWS, bool KMAJOR>
 struct Loader;
 
@@ -144,23 +162,28 @@ struct Loader<C, ROWS, true> {
   static constexpr int NREG = ROWS / RSTEP;
   static_assert(C::NT % VPR == 0 && ROWS % RSTEP == 0, "K-major loader geometry");
   u32x4 r[NREG];
-  const T* base;
+  const T* tile;     // element (mn0, 0)
+  int64_t rows_left; // valid rows from mn0
+  uint32_t off0, rstep_bytes;
   int row0, kv;
 
   __device__ __forceinline__ void init(const Opnd<T>& op, int mn0, int tid) {
     kv = (tid % VPR) * VEC;
     row0 = tid / VPR;
-    base = op.p + static_cast<int64_t>(mn0 + row0) * op.ld + kv;
+    tile = op.p + static_cast<int64_t>(mn0) * op.ld;
+    rows_left = op.mn_ext - mn0;
+    off0 = static_cast<uint32_t>((row0 * op.ld + kv) * static_cast<int64_t>(sizeof(T)));
+    rstep_bytes = static_cast<uint32_t>(RSTEP * op.ld * static_cast<int64_t>(sizeof(T)));
   }
-  __device__ __forceinline__ void load(const Opnd<T>& op, int mn0, int k0) {
-    const bool kok = k0 + kv < op.k_ext;
+  // `live` false turns every load into an out-of-range (zero, no traffic) access
+  __device__ __forceinline__ void load(const Opnd<T>& op, int k0, bool live = true) {
+    const __amdgpu_buffer_rsrc_t rs =
+        make_rsrc(tile + k0, (rows_left * op.ld - k0) * static_cast<int64_t>(sizeof(T)));
+    // a ragged last K step parks the lanes past k_ext beyond the record count
+    // (kOOB + i * rstep stays below 2^32 and above every valid count)
+    const uint32_t off = (live && k0 + kv < op.k_ext) ? off0 : kOOB;
 #pragma unroll
-    for (int i = 0; i < NREG; ++i) {
-      const bool ok = kok && (mn0 + row0 + i * RSTEP < op.mn_ext);
-      u32x4 v = {0u, 0u, 0u, 0u};
-      if (ok) v = *reinterpret_cast<const u32x4*>(base + static_cast<int64_t>(i * RSTEP) * op.ld + k0);
-      r[i] = v;
-    }
+    for (int i = 0; i < NREG; ++i) r[i] = buf_load16(rs, off + i * rstep_bytes);
   }
   __device__ __forceinline__ void store(T* lds) const {
 #pragma unroll
@@ -180,27 +203,30 @@ struct Loader<C, ROWS, false> {
   static_assert(C::NT % BPR == 0 && (C::BK / VEC) % KSTEP == 0 && NBLK >= 1,
                 "MN-major loader geometry");
   u32x4 r[NREG];
-  const T* base;
+  const T* tile;  // element (mn0, k = 0)
+  int mn0;
+  uint32_t off0, ld_bytes;
   int mb, kb0;
 
-  __device__ __forceinline__ void init(const Opnd<T>& op, int mn0, int tid) {
+  __device__ __forceinline__ void init(const Opnd<T>& op, int mn0_, int tid) {
+    mn0 = mn0_;
     mb = (tid % BPR) * VEC;
     kb0 = (tid / BPR) * VEC;
-    base = op.p + static_cast<int64_t>(kb0) * op.ld + mn0 + mb;
+    tile = op.p + mn0;
+    ld_bytes = static_cast<uint32_t>(op.ld * static_cast<int64_t>(sizeof(T)));
+    off0 = static_cast<uint32_t>((kb0 * op.ld + mb) * static_cast<int64_t>(sizeof(T)));
   }
-  __device__ __forceinline__ void load(const Opnd<T>& op, int mn0, int k0) {
-    const bool mok = mn0 + mb < op.mn_ext;
+  __device__ __forceinline__ void load(const Opnd<T>& op, int k0, bool live = true) {
+    // rows k >= k_ext lie past the record count and read as zero; columns
+    // past mn_ext only feed output columns that are never stored
+    const __amdgpu_buffer_rsrc_t rs =
+        make_rsrc(tile + static_cast<int64_t>(k0) * op.ld,
+                  live ? ((op.k_ext - k0) * op.ld - mn0) * static_cast<int64_t>(sizeof(T)) : 0);
 #pragma unroll
-    for (int b = 0; b < NBLK; ++b) {
+    for (int b = 0; b < NBLK; ++b)
 #pragma unroll
-      for (int rr = 0; rr < VEC; ++rr) {
-        const int kk = b * KSTEP * VEC + rr;
-        const bool ok = mok && (k0 + kb0 + kk < op.k_ext);
-        u32x4 v = {0u, 0u, 0u, 0u};
-        if (ok) v = *reinterpret_cast<const u32x4*>(base + static_cast<int64_t>(k0 + kk) * op.ld);
-        r[b * VEC + rr] = v;
-      }
-    }
+      for (int rr = 0; rr < VEC; ++rr)
+        r[b * VEC + rr] = buf_load16(rs, off0 + (b * KSTEP * VEC + rr) * ld_bytes);
   }
   __device__ __forceinline__ void store(T* lds) const {
 #pragma unroll
@@ -222,15 +248,33 @@ struct Acc {
   floatx16 v[C::FM][C::FN];
 };
 
+// Instruction-group masks of __builtin_amdgcn_sched_group_barrier.
+constexpr int kSchedVALU = 0x0002, kSchedMFMA = 0x0008, kSchedVMEMRead = 0x0020,
+              kSchedDSRead = 0x0100, kSchedDSWrite = 0x0200;
+
 // One BM x BN output tile: acc = A[m0:m0+BM, 0:K] . B[n0:n0+BN, 0:K]^T.
-// LDS holds two stages; global loads of step k+1 are in flight while the
-// MFMAs of step k run.  Ends with a barrier, so LDS may be reused after it.
+//
+// Pipeline per BK-deep tile (two LDS stages, two register sets of MFMA
+// fragments): the global loads of tile t+1 are issued during the first
+// 16-deep sub-step of tile t; every sub-step reads the next sub-step's
+// fragments from LDS while its own MFMAs run; the last sub-step writes tile
+// t+1 into the other LDS stage between its MFMAs; one barrier per tile.
+// The interleaving is pinned with scheduling-group barriers so the MFMA
+// pipe is never left waiting on an LDS round trip it could have overlapped.
+// Ends with a barrier, so LDS may be reused after it.
 template <class C, bool A_KMAJOR, bool B_KMAJOR>
 __device__ __forceinline__ void gemm_tile(Acc<C>& acc, const Opnd<typename C::Elem>& A,
                                           const Opnd<typename C::Elem>& B, int m0, int n0, int K,
                                           typename C::Elem* lds, int tid) {
   typedef typename C::Elem T;
   typedef typename C::Tr Tr;
+  constexpr int KS = C::BK / 16;
+  constexpr int NMMA = C::FM * C::FN;  // MFMA instructions per sub-step (bf16)
+  constexpr int NFRAG = C::FM + C::FN;
+  typedef Loader<C, C::BM, A_KMAJOR> LA;
+  typedef Loader<C, C::BN, B_KMAJOR> LB;
+  constexpr int NVMEM = LA::NREG + LB::NREG;
+  static_assert(KS % 2 == 0, "fragment sets alternate within a tile");
 #pragma unroll
   for (int fm = 0; fm < C::FM; ++fm)
 #pragma unroll
@@ -240,12 +284,12 @@ __device__ __forceinline__ void gemm_tile(Acc<C>& acc, const Opnd<typename C::El
   const int nk = (K + C::BK - 1) / C::BK;
   if (nk <= 0) return;
 
-  Loader<C, C::BM, A_KMAJOR> la;
-  Loader<C, C::BN, B_KMAJOR> lb;
+  LA la;
+  LB lb;
   la.init(A, m0, tid);
   lb.init(B, n0, tid);
-  la.load(A, m0, 0);
-  lb.load(B, n0, 0);
+  la.load(A, 0);
+  lb.load(B, 0);
   la.store(lds);
   lb.store(lds + C::A_ELEMS);
   __syncthreads();
@@ -256,32 +300,71 @@ __device__ __forceinline__ void gemm_tile(Acc<C>& acc, const Opnd<typename C::El
   const int a_off = (wm * C::WTM + frow) * C::LDK + fk;
   const int b_off = (wn * C::WTN + frow) * C::LDK + fk;
 
+  typename Tr::Frag fa[2][C::FM], fb[2][C::FN];
+  auto read_frags = [&](int set, const T* As, int k16) {
+    const T* Bs = As + C::A_ELEMS;
+#pragma unroll
+    for (int f = 0; f < (C::FM > C::FN ? C::FM : C::FN); ++f) {
+      if (f < C::FM) fa[set][f] = Tr::frag(As + a_off + f * 32 * C::LDK + k16 * 16);
+      if (f < C::FN) fb[set][f] = Tr::frag(Bs + b_off + f * 32 * C::LDK + k16 * 16);
+    }
+  };
+  auto mma_set = [&](int set) {
+#pragma unroll
+    for (int fm = 0; fm < C::FM; ++fm)
+#pragma unroll
+      for (int fn = 0; fn < C::FN; ++fn) Tr::mma(acc.v[fm][fn], fa[set][fm], fb[set][fn]);
+  };
+  const bool pin = sizeof(T) == 2;  // pin the bf16 interleaving; fp32 is left to the compiler
+
+  read_frags(0, lds, 0);
   for (int kt = 0; kt < nk; ++kt) {
     const T* As = lds + (kt & 1) * C::STAGE;
-    const T* Bs = As + C::A_ELEMS;
-    const bool more = kt + 1 < nk;
-    if (more) {
-      la.load(A, m0, (kt + 1) * C::BK);
-      lb.load(B, n0, (kt + 1) * C::BK);
-    }
+    T* nxt = lds + ((kt + 1) & 1) * C::STAGE;
+    // prefetch tile kt+1; past the last tile the loads are out of range (no
+    // traffic) and the stores fill an LDS stage nobody reads
+    const bool live = kt + 1 < nk;
+    la.load(A, (kt + 1) * C::BK, live);
+    lb.load(B, (kt + 1) * C::BK, live);
 #pragma unroll
-    for (int k16 = 0; k16 < C::BK / 16; ++k16) {
-      typename Tr::Frag a[C::FM], b[C::FN];
+    for (int k16 = 0; k16 < KS; ++k16) {
+      const int cur = k16 & 1;
+      if (k16 + 1 < KS) read_frags(cur ^ 1, As, k16 + 1);
+      mma_set(cur);
+      if (k16 + 1 == KS) {
+        la.store(nxt);
+        lb.store(nxt + C::A_ELEMS);
+      }
+      if (pin) {
+        if (k16 == 0) {
 #pragma unroll
-      for (int fm = 0; fm < C::FM; ++fm) a[fm] = Tr::frag(As + a_off + fm * 32 * C::LDK + k16 * 16);
+          for (int g = 0; g < NFRAG; ++g) {
+            __builtin_amdgcn_sched_group_barrier(kSchedMFMA, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(kSchedDSRead, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(kSchedVMEMRead, NVMEM / NFRAG, 0);
+          }
+          __builtin_amdgcn_sched_group_barrier(kSchedMFMA, NMMA - NFRAG, 0);
+        } else if (k16 + 1 < KS) {
 #pragma unroll
-      for (int fn = 0; fn < C::FN; ++fn) b[fn] = Tr::frag(Bs + b_off + fn * 32 * C::LDK + k16 * 16);
+          for (int g = 0; g < NFRAG; ++g) {
+            __builtin_amdgcn_sched_group_barrier(kSchedMFMA, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(kSchedDSRead, 1, 0);
+          }
+          __builtin_amdgcn_sched_group_barrier(kSchedMFMA, NMMA - NFRAG, 0);
+        } else {
 #pragma unroll
-      for (int fm = 0; fm < C::FM; ++fm)
-#pragma unroll
-        for (int fn = 0; fn < C::FN; ++fn) Tr::mma(acc.v[fm][fn], a[fm], b[fn]);
-    }
-    if (more) {
-      T* nxt = lds + ((kt + 1) & 1) * C::STAGE;
-      la.store(nxt);
-      lb.store(nxt + C::A_ELEMS);
+          for (int g = 0; g < NMMA / 2; ++g) {
+            __builtin_amdgcn_sched_group_barrier(kSchedMFMA, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(kSchedVALU, 8, 0);
+            __builtin_amdgcn_sched_group_barrier(kSchedDSWrite, 2, 0);
+          }
+          __builtin_amdgcn_sched_group_barrier(kSchedMFMA, NMMA / 2, 0);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
     }
     __syncthreads();
+    read_frags(0, nxt, 0);
   }
 }
 
