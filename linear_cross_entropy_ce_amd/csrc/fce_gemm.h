@@ -7,8 +7,12 @@
 //   (M for the MFMA "A" operand, N for "B"), k along the contraction.
 //   K-major:  element (mn, k) at p[mn * ld + k]   (k contiguous)
 //   MN-major: element (mn, k) at p[k * ld + mn]   (mn contiguous)
-//   Both are staged into LDS as [mn][k] rows of BK elements (plus 16 bytes of
-//   padding), so the MFMA fragment reads are identical for every layout.
+//   Both are staged into LDS as [mn][k] rows of BK elements (128 bytes: eight
+//   16-byte chunks), so the MFMA fragment reads are identical for every
+//   layout.  Chunk c of row r sits at chunk c ^ swz(r), swz(r) = (r ^ r>>3) & 7,
+//   which keeps every 8-lane group of the three access patterns on distinct
+//   banks: fragment reads (8 consecutive rows, one chunk), K-major stores (one
+//   row, 8 chunks) and transposed MN-major stores (rows 8 apart, one chunk).
 //   MN-major tiles are transposed in registers, VEC x VEC at a time, between
 //   the 16-byte global loads and the 16-byte LDS stores.
 //
@@ -48,8 +52,9 @@ template <>
 struct Traits<bf16> {
   static constexpr int VEC = 8;  // elements per 16-byte vector
   typedef bf16x8 Frag;
-  __device__ __forceinline__ static Frag frag(const bf16* p) {
-    return *reinterpret_cast<const bf16x8*>(p);
+  // row: LDS row base; x: (first chunk of the fragment) ^ swz(row), in bytes / 16
+  __device__ __forceinline__ static Frag frag(const char* row, int x) {
+    return *reinterpret_cast<const bf16x8*>(row + (x << 4));
   }
   __device__ __forceinline__ static void mma(floatx16& c, const Frag& a, const Frag& b) {
     c = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
@@ -65,10 +70,11 @@ struct Traits<float> {
   struct Frag {
     floatx4 lo, hi;
   };
-  __device__ __forceinline__ static Frag frag(const float* p) {
+  // the 8 floats span two chunks: x and x ^ 1 (the first chunk is even)
+  __device__ __forceinline__ static Frag frag(const char* row, int x) {
     Frag f;
-    f.lo = *reinterpret_cast<const floatx4*>(p);
-    f.hi = *reinterpret_cast<const floatx4*>(p + 4);
+    f.lo = *reinterpret_cast<const floatx4*>(row + (x << 4));
+    f.hi = *reinterpret_cast<const floatx4*>(row + ((x ^ 1) << 4));
     return f;
   }
   __device__ __forceinline__ static void mma(floatx16& c, const Frag& a, const Frag& b) {
@@ -91,13 +97,14 @@ struct Cfg {
   static constexpr int BM = S::BM, BN = S::BN, BK = S::BK;
   static constexpr int WAVES_M = S::WAVES_M, WAVES_N = S::WAVES_N, NT = S::NT;
   static constexpr int VEC = Tr::VEC;
-  static constexpr int LDK = BK + VEC;  // LDS row pitch (elements): 16 bytes of padding
+  static constexpr int LDK = BK;  // LDS row pitch (elements): 128 bytes, swizzled
   static constexpr int WTM = BM / WAVES_M, WTN = BN / WAVES_N;
   static constexpr int FM = WTM / 32, FN = WTN / 32;
   static constexpr int A_ELEMS = BM * LDK, B_ELEMS = BN * LDK;
   static constexpr int STAGE = A_ELEMS + B_ELEMS;
   static constexpr int LDS_ELEMS = 2 * STAGE;
   static_assert(BK % 16 == 0 && WTM % 32 == 0 && WTN % 32 == 0, "tile shape");
+  static_assert(BK * sizeof(T) == 128, "LDS rows are eight 16-byte chunks");
   static_assert(LDS_ELEMS * sizeof(T) <= 160 * 1024, "gfx950 LDS is 160 KiB per workgroup");
 };
 
@@ -108,6 +115,9 @@ struct Opnd {
   int mn_ext;  // vectors starting at or beyond this mn are read as zero
   int k_ext;   // k at or beyond this are read as zero (K-major: multiple of VEC)
 };
+
+// Chunk swizzle of LDS row r.
+__device__ __forceinline__ int swz(int r) { return (r ^ (r >> 3)) & 7; }
 
 __device__ __forceinline__ void transpose_block(const u32x4 (&in)[8], u32x4 (&out)[8]) {
   // 8x8 of 16-bit: in[r] holds row r (k), element c in word c/2, half c%2.
@@ -161,7 +171,7 @@ struct Loader<C, ROWS, true> {
   static constexpr int RSTEP = C::NT / VPR;    // rows between a thread's vectors
   static constexpr int NREG = ROWS / RSTEP;
   static_assert(C::NT % VPR == 0 && ROWS % RSTEP == 0, "K-major loader geometry");
-  u32x4 r[NREG];
+  typedef u32x4 Regs[NREG];
   const T* tile;     // element (mn0, 0)
   int64_t rows_left; // valid rows from mn0
   uint32_t off0, rstep_bytes;
@@ -176,7 +186,7 @@ struct Loader<C, ROWS, true> {
     rstep_bytes = static_cast<uint32_t>(RSTEP * op.ld * static_cast<int64_t>(sizeof(T)));
   }
   // `live` false turns every load into an out-of-range (zero, no traffic) access
-  __device__ __forceinline__ void load(const Opnd<T>& op, int k0, bool live = true) {
+  __device__ __forceinline__ void load(Regs& r, const Opnd<T>& op, int k0, bool live = true) const {
     const __amdgpu_buffer_rsrc_t rs =
         make_rsrc(tile + k0, (rows_left * op.ld - k0) * static_cast<int64_t>(sizeof(T)));
     // a ragged last K step parks the lanes past k_ext beyond the record count
@@ -185,10 +195,14 @@ struct Loader<C, ROWS, true> {
 #pragma unroll
     for (int i = 0; i < NREG; ++i) r[i] = buf_load16(rs, off + i * rstep_bytes);
   }
-  __device__ __forceinline__ void store(T* lds) const {
+  __device__ __forceinline__ void store(const Regs& r, T* lds) const {
+    char* base = reinterpret_cast<char*>(lds);
+    const int c = kv / VEC;
 #pragma unroll
-    for (int i = 0; i < NREG; ++i)
-      *reinterpret_cast<u32x4*>(lds + (row0 + i * RSTEP) * C::LDK + kv) = r[i];
+    for (int i = 0; i < NREG; ++i) {
+      const int row = row0 + i * RSTEP;
+      *reinterpret_cast<u32x4*>(base + row * 128 + ((c ^ swz(row)) << 4)) = r[i];
+    }
   }
 };
 
@@ -202,7 +216,7 @@ struct Loader<C, ROWS, false> {
   static constexpr int NREG = NBLK * VEC;
   static_assert(C::NT % BPR == 0 && (C::BK / VEC) % KSTEP == 0 && NBLK >= 1,
                 "MN-major loader geometry");
-  u32x4 r[NREG];
+  typedef u32x4 Regs[NREG];
   const T* tile;  // element (mn0, k = 0)
   int mn0;
   uint32_t off0, ld_bytes;
@@ -216,7 +230,7 @@ struct Loader<C, ROWS, false> {
     ld_bytes = static_cast<uint32_t>(op.ld * static_cast<int64_t>(sizeof(T)));
     off0 = static_cast<uint32_t>((kb0 * op.ld + mb) * static_cast<int64_t>(sizeof(T)));
   }
-  __device__ __forceinline__ void load(const Opnd<T>& op, int k0, bool live = true) {
+  __device__ __forceinline__ void load(Regs& r, const Opnd<T>& op, int k0, bool live = true) const {
     // rows k >= k_ext lie past the record count and read as zero; columns
     // past mn_ext only feed output columns that are never stored
     const __amdgpu_buffer_rsrc_t rs =
@@ -228,17 +242,20 @@ struct Loader<C, ROWS, false> {
       for (int rr = 0; rr < VEC; ++rr)
         r[b * VEC + rr] = buf_load16(rs, off0 + (b * KSTEP * VEC + rr) * ld_bytes);
   }
-  __device__ __forceinline__ void store(T* lds) const {
+  __device__ __forceinline__ void store(const Regs& r, T* lds) const {
 #pragma unroll
     for (int b = 0; b < NBLK; ++b) {
       u32x4 in[VEC], out[VEC];
 #pragma unroll
       for (int rr = 0; rr < VEC; ++rr) in[rr] = r[b * VEC + rr];
       transpose_block(in, out);
-      const int kcol = kb0 + b * KSTEP * VEC;
+      const int c = (kb0 + b * KSTEP * VEC) / VEC;
+      char* base = reinterpret_cast<char*>(lds);
 #pragma unroll
-      for (int j = 0; j < VEC; ++j)
-        *reinterpret_cast<u32x4*>(lds + (mb + j) * C::LDK + kcol) = out[j];
+      for (int j = 0; j < VEC; ++j) {
+        const int row = mb + j;
+        *reinterpret_cast<u32x4*>(base + row * 128 + ((c ^ swz(row)) << 4)) = out[j];
+      }
     }
   }
 };
@@ -258,10 +275,10 @@ constexpr int kSchedVALU = 0x0002, kSchedMFMA = 0x0008, kSchedVMEMRead = 0x0020,
 // fragments): the global loads of tile t+1 are issued during the first
 // 16-deep sub-step of tile t; every sub-step reads the next sub-step's
 // fragments from LDS while its own MFMAs run; the last sub-step writes tile
-// t+1 into the other LDS stage between its MFMAs; one barrier per tile.
-// The interleaving is pinned with scheduling-group barriers so the MFMA
-// pipe is never left waiting on an LDS round trip it could have overlapped.
-// Ends with a barrier, so LDS may be reused after it.
+// t+1 into the other LDS stage between its MFMAs; one barrier per tile.  The
+// interleaving is pinned with scheduling-group barriers so the MFMA pipe is
+// not left waiting on an LDS round trip it could have overlapped.  Ends with
+// a barrier, so LDS may be reused after it.
 template <class C, bool A_KMAJOR, bool B_KMAJOR>
 __device__ __forceinline__ void gemm_tile(Acc<C>& acc, const Opnd<typename C::Elem>& A,
                                           const Opnd<typename C::Elem>& B, int m0, int n0, int K,
@@ -288,25 +305,38 @@ __device__ __forceinline__ void gemm_tile(Acc<C>& acc, const Opnd<typename C::El
   LB lb;
   la.init(A, m0, tid);
   lb.init(B, n0, tid);
-  la.load(A, 0);
-  lb.load(B, 0);
-  la.store(lds);
-  lb.store(lds + C::A_ELEMS);
+  typename LA::Regs ra;
+  typename LB::Regs rb;
+  la.load(ra, A, 0);
+  lb.load(rb, B, 0);
+  la.store(ra, lds);
+  lb.store(rb, lds + C::A_ELEMS);
   __syncthreads();
 
   const int lane = tid & 63, wave = tid >> 6;
   const int wm = wave / C::WAVES_N, wn = wave % C::WAVES_N;
-  const int frow = lane & 31, fk = (lane >> 5) * 8;
-  const int a_off = (wm * C::WTM + frow) * C::LDK + fk;
-  const int b_off = (wn * C::WTN + frow) * C::LDK + fk;
+  // Fragment f of sub-step k16 covers k = 16*k16 + 8*(lane/32) .. +8 of row
+  // base + 32*f + lane%32: its first chunk is k16*CPS + (lane/32)*CPH.
+  constexpr int CPH = 8 * static_cast<int>(sizeof(T)) / 16;  // chunks per half fragment
+  constexpr int CPS = 2 * CPH;                                // chunks per sub-step
+  const int hl = lane >> 5;
+  const int a_row = wm * C::WTM + (lane & 31);
+  const int b_row = wn * C::WTN + (lane & 31);
+  int ax[C::FM], bx[C::FN];  // (first chunk of sub-step 0) ^ swizzle, per fragment row
+#pragma unroll
+  for (int f = 0; f < C::FM; ++f) ax[f] = (hl * CPH) ^ swz(a_row + 32 * f);
+#pragma unroll
+  for (int f = 0; f < C::FN; ++f) bx[f] = (hl * CPH) ^ swz(b_row + 32 * f);
 
   typename Tr::Frag fa[2][C::FM], fb[2][C::FN];
   auto read_frags = [&](int set, const T* As, int k16) {
-    const T* Bs = As + C::A_ELEMS;
+    const char* Ab = reinterpret_cast<const char*>(As);
+    const char* Bb = reinterpret_cast<const char*>(As + C::A_ELEMS);
 #pragma unroll
     for (int f = 0; f < (C::FM > C::FN ? C::FM : C::FN); ++f) {
-      if (f < C::FM) fa[set][f] = Tr::frag(As + a_off + f * 32 * C::LDK + k16 * 16);
-      if (f < C::FN) fb[set][f] = Tr::frag(Bs + b_off + f * 32 * C::LDK + k16 * 16);
+      // k16 * CPS only touches chunk bits above the lane's own, so XOR composes
+      if (f < C::FM) fa[set][f] = Tr::frag(Ab + (a_row + 32 * f) * 128, ax[f] ^ (k16 * CPS));
+      if (f < C::FN) fb[set][f] = Tr::frag(Bb + (b_row + 32 * f) * 128, bx[f] ^ (k16 * CPS));
     }
   };
   auto mma_set = [&](int set) {
@@ -324,16 +354,16 @@ __device__ __forceinline__ void gemm_tile(Acc<C>& acc, const Opnd<typename C::El
     // prefetch tile kt+1; past the last tile the loads are out of range (no
     // traffic) and the stores fill an LDS stage nobody reads
     const bool live = kt + 1 < nk;
-    la.load(A, (kt + 1) * C::BK, live);
-    lb.load(B, (kt + 1) * C::BK, live);
+    la.load(ra, A, (kt + 1) * C::BK, live);
+    lb.load(rb, B, (kt + 1) * C::BK, live);
 #pragma unroll
     for (int k16 = 0; k16 < KS; ++k16) {
       const int cur = k16 & 1;
       if (k16 + 1 < KS) read_frags(cur ^ 1, As, k16 + 1);
       mma_set(cur);
       if (k16 + 1 == KS) {
-        la.store(nxt);
-        lb.store(nxt + C::A_ELEMS);
+        la.store(ra, nxt);
+        lb.store(rb, nxt + C::A_ELEMS);
       }
       if (pin) {
         if (k16 == 0) {

@@ -361,22 +361,35 @@ __global__ __launch_bounds__(C::NT) void k_bwd_grad(GradArgs<typename C::Elem> a
     gemm_tile<C, A_KMAJOR, false>(acc, a.A, a.B, m0, n0, a.K, lds, tid);
   }
   const float s = a.ctrl->scale_bwd;
+  // Output element (fm, fn, i) of this lane: row m0 + rbase + 32 fm + 8 (i/4) + (i%4),
+  // column n0 + cbase + 32 fn.  Per 32-row slab fm, all loads of the old values
+  // are issued before any use, so their latencies overlap.
+  const int rbase = wm * C::WTM + 4 * (lane >> 5);
+  const int cbase = wn * C::WTN + (lane & 31);
+  const bool full = m0 + C::BM <= a.m_valid && n0 + C::BN <= a.n_valid;
+  float* tile = a.out + static_cast<int64_t>(m0) * a.ldo + n0;
 #pragma unroll
   for (int fm = 0; fm < C::FM; ++fm) {
+    float old[C::FN][16];
+    bool ok[C::FN][16];
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int m = m0 + wm * C::WTM + fm * 32 + 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3);
-      if (m >= a.m_valid) continue;
-      float* orow = a.out + static_cast<int64_t>(m) * a.ldo;
+    for (int fn = 0; fn < C::FN; ++fn)
 #pragma unroll
-      for (int fn = 0; fn < C::FN; ++fn) {
-        const int n = n0 + wn * C::WTN + fn * 32 + (lane & 31);
-        if (n < a.n_valid) {
-          const float v = s * acc.v[fm][fn][i];
-          orow[n] = a.accumulate ? orow[n] + v : v;
-        }
+      for (int i = 0; i < 16; ++i) {
+        const int r = rbase + fm * 32 + 8 * (i >> 2) + (i & 3);
+        const int c = cbase + fn * 32;
+        ok[fn][i] = full || (m0 + r < a.m_valid && n0 + c < a.n_valid);
+        old[fn][i] = 0.0f;
+        if (a.accumulate && ok[fn][i]) old[fn][i] = tile[static_cast<int64_t>(r) * a.ldo + c];
       }
-    }
+#pragma unroll
+    for (int fn = 0; fn < C::FN; ++fn)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int r = rbase + fm * 32 + 8 * (i >> 2) + (i & 3);
+        const int c = cbase + fn * 32;
+        if (ok[fn][i]) tile[static_cast<int64_t>(r) * a.ldo + c] = old[fn][i] + s * acc.v[fm][fn][i];
+      }
   }
 }
 

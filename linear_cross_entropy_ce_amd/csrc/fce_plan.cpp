@@ -125,21 +125,30 @@ bool make_plan(int64_t N, int64_t H, int64_t V, Dtype dtype, int64_t chunk, Sche
       p.a = 1;
       vocab_split(p.CN, &p.CV, &p.b);
     } else if (sched == Schedule::Auto) {
+      // Candidates: every block height, and for each the fewest vocabulary
+      // blocks the budget allows plus a few more (a narrower block can fill
+      // the 256 CUs with fewer partial waves).
       double best = std::numeric_limits<double>::infinity();
       const int64_t amax = cdiv(N, G);
       for (int64_t a = 1; a <= amax; ++a) {
         const int64_t CN = round_up(cdiv(N, a), G);
         const int64_t aa = cdiv(N, CN);
         if (aa != a) continue;  // same block height as a smaller a
-        int64_t CV, b;
-        vocab_split(CN, &CV, &b);
-        const double t = model_time(p, CN, CV, aa, b);
-        if (t < best * (1.0 - 1e-9)) {
-          best = t;
-          p.CN = CN;
-          p.CV = CV;
-          p.a = aa;
-          p.b = b;
+        int64_t CV0, b0;
+        vocab_split(CN, &CV0, &b0);
+        for (int64_t b = b0; b <= b0 + 8; ++b) {
+          const int64_t CV = round_up(cdiv(V, b), G);
+          if (CV > CV0 && b != b0) continue;
+          const int64_t bb = cdiv(V, CV);
+          if (bb != b) continue;  // same block width as a smaller b
+          const double t = model_time(p, CN, CV, aa, bb);
+          if (t < best * (1.0 - 1e-9)) {
+            best = t;
+            p.CN = CN;
+            p.CV = CV;
+            p.a = aa;
+            p.b = bb;
+          }
         }
       }
     } else {
@@ -147,7 +156,11 @@ bool make_plan(int64_t N, int64_t H, int64_t V, Dtype dtype, int64_t chunk, Sche
     }
   }
   p.scratch_rows = p.CN;
+  // Row pitch of the dZ block: a pitch that is a multiple of 1 KiB puts the
+  // same column of every row on the same memory channel, so pad such pitches
+  // by one 128-byte line.
   p.ldz = p.CV;
+  if ((p.ldz * p.elem_bytes) % 1024 == 0) p.ldz += 128 / p.elem_bytes;
   p.grad_rmw_bytes = (N == 0) ? 4 * V * H
                               : 4 * V * H * (2 * p.a - 1) + 4 * N * H * (2 * p.b - 1);
 
