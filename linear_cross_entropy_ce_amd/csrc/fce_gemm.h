@@ -147,6 +147,12 @@ __device__ __forceinline__ void transpose_block(const u32x4 (&in)[4], u32x4 (&ou
 // is clamped to 2^31 - 1 so that kOOB below is always out of range.
 constexpr uint32_t kOOB = 0x80000000u;
 
+// s_waitcnt immediate that waits for vmcnt <= n (gfx9 encoding: vmcnt in
+// bits 3:0 and 15:14) and leaves expcnt / lgkmcnt unconstrained.
+__host__ __device__ constexpr int vmcnt_imm(int n) {
+  return (n & 0xF) | ((n >> 4) << 14) | (0x7 << 4) | (0xF << 8);
+}
+
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int64_t bytes) {
   const int64_t n = bytes < 0 ? 0 : (bytes > 0x7fffffff ? 0x7fffffff : bytes);
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, static_cast<int>(n),
@@ -282,7 +288,8 @@ constexpr int kSchedVALU = 0x0002, kSchedMFMA = 0x0008, kSchedVMEMRead = 0x0020,
 template <class C, bool A_KMAJOR, bool B_KMAJOR>
 __device__ __forceinline__ void gemm_tile(Acc<C>& acc, const Opnd<typename C::Elem>& A,
                                           const Opnd<typename C::Elem>& B, int m0, int n0, int K,
-                                          typename C::Elem* lds, int tid) {
+                                          typename C::Elem* lds0, typename C::Elem* lds1,
+                                          int tid) {
   typedef typename C::Elem T;
   typedef typename C::Tr Tr;
   constexpr int KS = C::BK / 16;
@@ -309,8 +316,8 @@ __device__ __forceinline__ void gemm_tile(Acc<C>& acc, const Opnd<typename C::El
   typename LB::Regs rb;
   la.load(ra, A, 0);
   lb.load(rb, B, 0);
-  la.store(ra, lds);
-  lb.store(rb, lds + C::A_ELEMS);
+  la.store(ra, lds0);
+  lb.store(rb, lds0 + C::A_ELEMS);
   __syncthreads();
 
   const int lane = tid & 63, wave = tid >> 6;
@@ -347,10 +354,10 @@ __device__ __forceinline__ void gemm_tile(Acc<C>& acc, const Opnd<typename C::El
   };
   const bool pin = sizeof(T) == 2;  // pin the bf16 interleaving; fp32 is left to the compiler
 
-  read_frags(0, lds, 0);
+  read_frags(0, lds0, 0);
   for (int kt = 0; kt < nk; ++kt) {
-    const T* As = lds + (kt & 1) * C::STAGE;
-    T* nxt = lds + ((kt + 1) & 1) * C::STAGE;
+    const T* As = (kt & 1) ? lds1 : lds0;
+    T* nxt = (kt & 1) ? lds0 : lds1;
     // prefetch tile kt+1; past the last tile the loads are out of range (no
     // traffic) and the stores fill an LDS stage nobody reads
     const bool live = kt + 1 < nk;
@@ -395,6 +402,266 @@ __device__ __forceinline__ void gemm_tile(Acc<C>& acc, const Opnd<typename C::El
     }
     __syncthreads();
     read_frags(0, nxt, 0);
+  }
+}
+
+// ===================================================== bf16 DMA main loop
+// gfx950 path for bf16: operand tiles go straight from global memory into LDS
+// with buffer_load_dwordx4 ... lds (lane l of a wave lands at M0 + 16 l), so
+// no registers stage them and nothing is transposed in registers.
+//
+// LDS layouts (per stage, BK = 32):
+//   K-major operand:  [ROWS][32] bf16, 64-byte rows of four 16-byte chunks;
+//                     chunk c of row r at chunk c ^ ((r >> 1) & 3).
+//   MN-major operand: [32][ROWS] bf16, untransposed rows of k; 16-byte chunk c
+//                     of row k at chunk c ^ 2 (k % 4).
+// Fragment reads: K-major with ds_read_b128; MN-major with two
+// ds_read_b64_tr_b16, whose 16-lane transpose hands lane l the 8 consecutive
+// k of column l % 32 (the same fragment a K-major read gives).  Both swizzles
+// keep every 16-lane phase of those reads on distinct banks.
+// Pipeline: STAGES LDS stages; the loads of tile t+STAGES-1 are issued at the
+// start of tile t, so each tile's data has STAGES-2 tiles of MFMA work to
+// land before the barrier that publishes it.
+
+template <int ROWS, bool KMAJOR>
+struct DmaOperand;
+
+typedef short shortx4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+
+template <int ROWS>
+struct DmaOperand<ROWS, true> {
+  static constexpr int BK = 32, NT = 256;
+  static constexpr int BYTES = ROWS * BK * 2;       // per stage
+  static constexpr int NI = BYTES / (NT * 16);      // DMA instructions per thread per tile
+  static constexpr int ROWS_PER_I = NT * 16 / 64;   // 64 rows per instruction round
+  const bf16* tile;
+  int64_t rows_left;
+  uint32_t voff0, istep;
+  int kc;  // k offset of this thread's chunk
+
+  __device__ __forceinline__ void init(const Opnd<bf16>& op, int mn0, int tid) {
+    const int row = tid >> 2;              // (16 tid) / 64
+    const int c = (tid & 3) ^ ((row >> 1) & 3);
+    kc = c * 8;
+    tile = op.p + static_cast<int64_t>(mn0) * op.ld;
+    rows_left = op.mn_ext - mn0;
+    voff0 = static_cast<uint32_t>((row * op.ld + kc) * 2);
+    istep = static_cast<uint32_t>(ROWS_PER_I * op.ld * 2);
+  }
+  __device__ __forceinline__ void load(char* stage, int wave, const Opnd<bf16>& op, int k0,
+                                       bool live) const {
+    const __amdgpu_buffer_rsrc_t rs = make_rsrc(tile + k0, (rows_left * op.ld - k0) * 2);
+    const uint32_t off = (live && k0 + kc < op.k_ext) ? voff0 : kOOB;
+#pragma unroll
+    for (int i = 0; i < NI; ++i)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          rs, (lds_ptr_t)(stage + i * NT * 16 + wave * 1024), 16, off + i * istep, 0, 0, 0);
+  }
+};
+
+template <int ROWS>
+struct DmaOperand<ROWS, false> {
+  static constexpr int BK = 32, NT = 256;
+  static constexpr int ROWB = ROWS * 2;              // bytes per k-row
+  static constexpr int BYTES = BK * ROWB;
+  static constexpr int NI = BYTES / (NT * 16);
+  static constexpr int KROWS_PER_I = NT * 16 / ROWB;
+  static_assert(ROWB % 1024 == 0 || 1024 % ROWB == 0, "k-rows tile the 1 KiB DMA blocks");
+  const bf16* tile;
+  int mn0;
+  uint32_t voff0, istep;
+
+  __device__ __forceinline__ void init(const Opnd<bf16>& op, int mn0_, int tid) {
+    mn0 = mn0_;
+    const int krow = (tid * 16) / ROWB;
+    const int pchunk = ((tid * 16) % ROWB) / 16;
+    const int c = pchunk ^ (2 * (krow & 3));
+    tile = op.p + mn0;
+    voff0 = static_cast<uint32_t>((krow * op.ld + c * 8) * 2);
+    istep = static_cast<uint32_t>(KROWS_PER_I * op.ld * 2);
+  }
+  __device__ __forceinline__ void load(char* stage, int wave, const Opnd<bf16>& op, int k0,
+                                       bool live) const {
+    // rows k >= k_ext lie past the record count and read as zero
+    const __amdgpu_buffer_rsrc_t rs =
+        make_rsrc(tile + static_cast<int64_t>(k0) * op.ld,
+                  live ? ((op.k_ext - k0) * op.ld - mn0) * static_cast<int64_t>(2) : 0);
+#pragma unroll
+    for (int i = 0; i < NI; ++i)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          rs, (lds_ptr_t)(stage + i * NT * 16 + wave * 1024), 16, voff0 + i * istep, 0, 0, 0);
+  }
+};
+
+// Per-lane fragment addressing of one operand (relative to the stage base).
+template <int ROWS, bool KMAJOR>
+struct FragAddr;
+
+template <int ROWS>
+struct FragAddr<ROWS, true> {
+  int off[2];  // byte offset of fragment 0 for sub-steps 0 and 1
+  __device__ __forceinline__ void init(int wave_base, int lane) {
+    const int r = wave_base + (lane & 31);
+    const int x = (lane >> 5) ^ ((r >> 1) & 3);
+    off[0] = r * 64 + 16 * x;
+    off[1] = r * 64 + 16 * (x ^ 2);
+  }
+  __device__ __forceinline__ bf16x8 read(const char* stage, int f, int k16) const {
+    return *reinterpret_cast<const bf16x8*>(stage + off[k16] + f * 32 * 64);
+  }
+};
+
+template <int ROWS>
+struct FragAddr<ROWS, false> {
+  static constexpr int ROWB = ROWS * 2;
+  int off[4];  // byte offset for fragments f = 0..3 (sub-step 0, half 0)
+  __device__ __forceinline__ void init(int wave_base, int lane) {
+    const int gq = lane >> 4, a = lane & 15;
+    const int kr0 = 8 * (gq >> 1) + (a >> 2);
+    const int g = 2 * (a >> 2);  // swizzle of row kr0 + 4h + 16 k16 (all = kr0 mod 4)
+    const int mnoff = 16 * (gq & 1) + 4 * (a & 3);
+#pragma unroll
+    for (int f = 0; f < 4; ++f) {
+      const int mn = wave_base + 32 * f + mnoff;
+      off[f] = kr0 * ROWB + 16 * ((mn >> 3) ^ g) + (mn & 7) * 2;
+    }
+  }
+  __device__ __forceinline__ bf16x8 read(const char* stage, int f, int k16) const {
+    const char* p = stage + off[f] + k16 * 16 * ROWB;
+    const shortx4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) shortx4*)(p));
+    const shortx4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (__attribute__((address_space(3))) shortx4*)(p + 4 * ROWB));
+    const shortx4 v[2] = {lo, hi};
+    return __builtin_bit_cast(bf16x8, v);
+  }
+};
+
+// The four LDS stages of the DMA pipeline.  They are distinct objects so the
+// compiler can tell a DMA into one stage from a read of another (it tracks
+// LDS-DMA completion per object); kernels declare them with
+// FCE_DMA_STAGES(name) and hand them over as a DmaStages.
+struct DmaStages {
+  char* s[4];
+};
+#define FCE_DMA_STAGES(name)                                                      \
+  __shared__ __attribute__((aligned(16))) char name##0[32768], name##1[32768],    \
+      name##2[32768], name##3[32768];                                             \
+  const ::fce::DmaStages name = {{name##0, name##1, name##2, name##3}}
+
+// Waits for this wave's LDS reads and all but the newest `n` vector-memory
+// operations, then joins the workgroup barrier.  (__syncthreads would also
+// drain every in-flight prefetch.)
+template <int N>
+__device__ __forceinline__ void barrier_after_vmcnt() {
+  __builtin_amdgcn_s_waitcnt(vmcnt_imm(N) & ~(0xF << 8));  // and lgkmcnt(0)
+  __builtin_amdgcn_s_barrier();
+}
+
+// One 256 x 256 bf16 output tile with 4 waves of 128 x 128 (2 x 2), the
+// operands in any layout, via the 4-stage DMA pipeline.  The K loop is
+// unrolled by the stage count so every stage reference is static.  Ends with
+// all DMA drained and a barrier, so the stages may be reused after it.
+template <class C, bool A_KMAJOR, bool B_KMAJOR>
+__device__ __forceinline__ void gemm_tile_dma(Acc<C>& acc, const Opnd<bf16>& A,
+                                              const Opnd<bf16>& B, int m0, int n0, int K,
+                                              const DmaStages& st, int tid) {
+  static_assert(C::BM == 256 && C::BN == 256 && C::NT == 256 && C::FM == 4 && C::FN == 4,
+                "DMA main loop geometry");
+  constexpr int S = 4;  // stages
+  constexpr int BK = 32;
+  constexpr int B_OFF = 256 * BK * 2;
+  typedef DmaOperand<256, A_KMAJOR> DA;
+  typedef DmaOperand<256, B_KMAJOR> DB;
+  constexpr int NL = DA::NI + DB::NI;  // DMA instructions per thread per tile
+#pragma unroll
+  for (int fm = 0; fm < 4; ++fm)
+#pragma unroll
+    for (int fn = 0; fn < 4; ++fn)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) acc.v[fm][fn][i] = 0.0f;
+  const int nk = (K + BK - 1) / BK;
+  if (nk <= 0) return;
+
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave / 2, wn = wave % 2;
+  DA da;
+  DB db;
+  da.init(A, m0, tid);
+  db.init(B, n0, tid);
+  FragAddr<256, A_KMAJOR> fa_addr;
+  FragAddr<256, B_KMAJOR> fb_addr;
+  fa_addr.init(wm * 128, lane);
+  fb_addr.init(wn * 128, lane);
+
+  auto issue = [&](char* stage, int kt) {
+    const bool live = kt < nk;
+    da.load(stage, wave, A, kt * BK, live);
+    db.load(stage + B_OFF, wave, B, kt * BK, live);
+  };
+  bf16x8 fa[2][4], fb[2][4];
+  auto read = [&](int set, const char* stage, int k16) {
+#pragma unroll
+    for (int f = 0; f < 4; ++f) {
+      fa[set][f] = fa_addr.read(stage, f, k16);
+      fb[set][f] = fb_addr.read(stage + B_OFF, f, k16);
+    }
+  };
+  auto mma = [&](int set) {
+#pragma unroll
+    for (int fm = 0; fm < 4; ++fm)
+#pragma unroll
+      for (int fn = 0; fn < 4; ++fn)
+        acc.v[fm][fn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[set][fm], fb[set][fn],
+                                                                acc.v[fm][fn], 0, 0, 0);
+  };
+  // Tile kt lives in stage kt % 4.  Trip step for tile kt in stage `cur`:
+  // prefetch tile kt+3 into the stage of tile kt-1 (free since the previous
+  // barrier), read sub-step 1 of tile kt, MFMA sub-step 0, publish tile kt+1
+  // (wait for this thread's DMA of it, barrier), read its sub-step 0, MFMA
+  // sub-step 1.
+  auto step = [&](int kt, char* cur, char* nxt, char* prv) {
+    issue(prv, kt + S - 1);
+    read(1, cur, 1);
+    mma(0);
+    barrier_after_vmcnt<NL * (S - 2)>();
+    read(0, nxt, 0);
+    mma(1);
+  };
+
+  issue(st.s[0], 0);
+  issue(st.s[1], 1);
+  issue(st.s[2], 2);
+  barrier_after_vmcnt<NL * (S - 2)>();
+  read(0, st.s[0], 0);
+  // Four tiles per trip.  When the tile count is not a multiple of four the
+  // last trip runs on tiles past the end, whose stages hold the zeros of
+  // out-of-range loads: their MFMAs add exact zeros.
+  for (int kt = 0; kt < nk; kt += S) {
+    step(kt, st.s[0], st.s[1], st.s[3]);
+    step(kt + 1, st.s[1], st.s[2], st.s[0]);
+    step(kt + 2, st.s[2], st.s[3], st.s[1]);
+    step(kt + 3, st.s[3], st.s[0], st.s[2]);
+  }
+  // the prefetches past the last tile still write (zeros) into LDS: drain them
+  barrier_after_vmcnt<0>();
+}
+
+// bf16 tiles take the DMA pipeline over the four stages, fp32 tiles the
+// register-staged one over stage 0 (which is large enough for both of its
+// LDS buffers).
+template <class C, bool A_KMAJOR, bool B_KMAJOR>
+__device__ __forceinline__ void gemm_any(Acc<C>& acc, const Opnd<typename C::Elem>& A,
+                                         const Opnd<typename C::Elem>& B, int m0, int n0, int K,
+                                         const DmaStages& st, int tid) {
+  if constexpr (sizeof(typename C::Elem) == 2) {
+    gemm_tile_dma<C, A_KMAJOR, B_KMAJOR>(acc, A, B, m0, n0, K, st, tid);
+  } else {
+    typedef typename C::Elem T;
+    static_assert(C::STAGE * sizeof(T) <= 32768, "an fp32 stage fits one DMA stage");
+    gemm_tile<C, A_KMAJOR, B_KMAJOR>(acc, A, B, m0, n0, K, reinterpret_cast<T*>(st.s[0]),
+                                     reinterpret_cast<T*>(st.s[1]), tid);
   }
 }
 

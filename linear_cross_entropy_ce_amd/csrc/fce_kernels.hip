@@ -104,7 +104,7 @@ struct FwdArgs {
 template <class C, bool SMOOTH>
 __global__ __launch_bounds__(C::NT) void k_fwd_lse(FwdArgs<typename C::Elem> a) {
   typedef typename C::Elem T;
-  __shared__ __attribute__((aligned(16))) T lds[C::LDS_ELEMS];
+  FCE_DMA_STAGES(lds);
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave / C::WAVES_N, wn = wave % C::WAVES_N;
   int tt, sp;
@@ -130,7 +130,7 @@ __global__ __launch_bounds__(C::NT) void k_fwd_lse(FwdArgs<typename C::Elem> a) 
   Acc<C> acc;
   for (int vt = vt_begin; vt < vt_end; ++vt) {
     const int m0 = vt * C::BM;
-    gemm_tile<C, true, true>(acc, A, B, m0, n0, a.H, lds, tid);
+    gemm_any<C, true, true>(acc, A, B, m0, n0, a.H, lds, tid);
     const int vbase = m0 + wm * C::WTM + 4 * (lane >> 5);
     const bool full = m0 + C::BM <= a.V;
 #pragma unroll
@@ -174,7 +174,8 @@ __global__ __launch_bounds__(C::NT) void k_fwd_lse(FwdArgs<typename C::Elem> a) 
     lse_merge(rm[fn], rl[fn], rt[fn], rz[fn], m2, l2, t2, z2);
   }
   // then the WAVES_M waves that share these token columns, in fixed order
-  floatx4* red = reinterpret_cast<floatx4*>(lds);  // [WAVES_M][BN]; LDS is free after gemm_tile
+  static_assert(C::WAVES_M * C::BN * sizeof(floatx4) <= 32768, "reduction fits one stage");
+  floatx4* red = reinterpret_cast<floatx4*>(lds.s[0]);  // [WAVES_M][BN]; free after gemm_any
   if (lane < 32) {
 #pragma unroll
     for (int fn = 0; fn < C::FN; ++fn) {
@@ -280,7 +281,7 @@ template <class C>
 __global__ __launch_bounds__(C::NT) void k_bwd_dz(DzArgs<typename C::Elem> a) {
   typedef typename C::Elem T;
   if (*a.flag == 0) return;  // every label of this token block is ignored
-  __shared__ __attribute__((aligned(16))) T lds[C::LDS_ELEMS];
+  FCE_DMA_STAGES(lds);
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave / C::WAVES_N, wn = wave % C::WAVES_N;
   int vt, tt;
@@ -290,7 +291,7 @@ __global__ __launch_bounds__(C::NT) void k_bwd_dz(DzArgs<typename C::Elem> a) {
   const Opnd<T> A{a.W, a.H, a.nvoc, a.H};
   const Opnd<T> B{a.X, a.H, a.ntok, a.H};
   Acc<C> acc;
-  gemm_tile<C, true, true>(acc, A, B, m0, n0, a.H, lds, tid);
+  gemm_any<C, true, true>(acc, A, B, m0, n0, a.H, lds, tid);
 
   const float eps_v = a.eps / static_cast<float>(a.V);
   const float one_m_eps = 1.0f - a.eps;
@@ -340,7 +341,7 @@ struct GradArgs {
 template <class C, bool A_KMAJOR>
 __global__ __launch_bounds__(C::NT) void k_bwd_grad(GradArgs<typename C::Elem> a) {
   typedef typename C::Elem T;
-  __shared__ __attribute__((aligned(16))) T lds[C::LDS_ELEMS];
+  FCE_DMA_STAGES(lds);
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave / C::WAVES_N, wn = wave % C::WAVES_N;
   int tm, tn;
@@ -358,7 +359,7 @@ __global__ __launch_bounds__(C::NT) void k_bwd_grad(GradArgs<typename C::Elem> a
 #pragma unroll
         for (int i = 0; i < 16; ++i) acc.v[fm][fn][i] = 0.0f;
   } else {
-    gemm_tile<C, A_KMAJOR, false>(acc, a.A, a.B, m0, n0, a.K, lds, tid);
+    gemm_any<C, A_KMAJOR, false>(acc, a.A, a.B, m0, n0, a.K, lds, tid);
   }
   const float s = a.ctrl->scale_bwd;
   // Output element (fm, fn, i) of this lane: row m0 + rbase + 32 fm + 8 (i/4) + (i%4),
