@@ -412,13 +412,15 @@ __device__ __forceinline__ void gemm_tile(Acc<C>& acc, const Opnd<typename C::El
 //
 // LDS layouts (per stage, BK = 32):
 //   K-major operand:  [ROWS][32] bf16, 64-byte rows of four 16-byte chunks;
-//                     chunk c of row r at chunk c ^ ((r >> 1) & 3).
+//                     chunk c of row r at chunk c ^ ((r >> 2) & 3).
 //   MN-major operand: [32][ROWS] bf16, untransposed rows of k; 16-byte chunk c
-//                     of row k at chunk c ^ 2 (k % 4).
+//                     of row k at chunk c ^ 4 (k % 4).
 // Fragment reads: K-major with ds_read_b128; MN-major with two
 // ds_read_b64_tr_b16, whose 16-lane transpose hands lane l the 8 consecutive
-// k of column l % 32 (the same fragment a K-major read gives).  Both swizzles
-// keep every 16-lane phase of those reads on distinct banks.
+// k of column l % 32 (the same fragment a K-major read gives).  With 64 banks
+// of 4 bytes, the swizzles put the 16 lanes of a b128 phase (16 consecutive
+// rows) and the 32 lanes of a b64 phase (4 k-rows x 32 contiguous bytes x 2
+// column groups) on distinct banks.
 // Pipeline: STAGES LDS stages; the loads of tile t+STAGES-1 are issued at the
 // start of tile t, so each tile's data has STAGES-2 tiles of MFMA work to
 // land before the barrier that publishes it.
@@ -442,7 +444,7 @@ struct DmaOperand<ROWS, true> {
 
   __device__ __forceinline__ void init(const Opnd<bf16>& op, int mn0, int tid) {
     const int row = tid >> 2;              // (16 tid) / 64
-    const int c = (tid & 3) ^ ((row >> 1) & 3);
+    const int c = (tid & 3) ^ ((row >> 2) & 3);
     kc = c * 8;
     tile = op.p + static_cast<int64_t>(mn0) * op.ld;
     rows_left = op.mn_ext - mn0;
@@ -476,7 +478,7 @@ struct DmaOperand<ROWS, false> {
     mn0 = mn0_;
     const int krow = (tid * 16) / ROWB;
     const int pchunk = ((tid * 16) % ROWB) / 16;
-    const int c = pchunk ^ (2 * (krow & 3));
+    const int c = pchunk ^ (4 * (krow & 3));
     tile = op.p + mn0;
     voff0 = static_cast<uint32_t>((krow * op.ld + c * 8) * 2);
     istep = static_cast<uint32_t>(KROWS_PER_I * op.ld * 2);
@@ -503,7 +505,7 @@ struct FragAddr<ROWS, true> {
   int off[2];  // byte offset of fragment 0 for sub-steps 0 and 1
   __device__ __forceinline__ void init(int wave_base, int lane) {
     const int r = wave_base + (lane & 31);
-    const int x = (lane >> 5) ^ ((r >> 1) & 3);
+    const int x = (lane >> 5) ^ ((r >> 2) & 3);
     off[0] = r * 64 + 16 * x;
     off[1] = r * 64 + 16 * (x ^ 2);
   }
@@ -519,7 +521,7 @@ struct FragAddr<ROWS, false> {
   __device__ __forceinline__ void init(int wave_base, int lane) {
     const int gq = lane >> 4, a = lane & 15;
     const int kr0 = 8 * (gq >> 1) + (a >> 2);
-    const int g = 2 * (a >> 2);  // swizzle of row kr0 + 4h + 16 k16 (all = kr0 mod 4)
+    const int g = 4 * (a >> 2);  // swizzle of row kr0 + 4h + 16 k16 (all = kr0 mod 4)
     const int mnoff = 16 * (gq & 1) + 4 * (a & 3);
 #pragma unroll
     for (int f = 0; f < 4; ++f) {
@@ -621,13 +623,32 @@ __device__ __forceinline__ void gemm_tile_dma(Acc<C>& acc, const Opnd<bf16>& A,
   // barrier), read sub-step 1 of tile kt, MFMA sub-step 0, publish tile kt+1
   // (wait for this thread's DMA of it, barrier), read its sub-step 0, MFMA
   // sub-step 1.
+  // LDS read instructions per fragment set: one b128 per K-major fragment,
+  // two b64 transpose reads per MN-major fragment.
+  constexpr int NR = 4 * (A_KMAJOR ? 1 : 2) + 4 * (B_KMAJOR ? 1 : 2);
+  constexpr int RG = (NR + 7) / 8, LG = (NL + 7) / 8;  // per-group sizes (groups may run short)
+  // Pin the order: the reads of the next fragment set (and the DMA issue)
+  // go between the first eight MFMAs of the current set, so both fragment
+  // sets stay live and no MFMA waits on an LDS round trip.
+  auto pin = [&](bool with_dma) {
+#pragma unroll
+    for (int g = 0; g < 8; ++g) {
+      __builtin_amdgcn_sched_group_barrier(kSchedMFMA, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(kSchedDSRead, RG, 0);
+      if (with_dma) __builtin_amdgcn_sched_group_barrier(kSchedVMEMRead, LG, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(kSchedMFMA, 8, 0);
+    __builtin_amdgcn_sched_barrier(0);
+  };
   auto step = [&](int kt, char* cur, char* nxt, char* prv) {
     issue(prv, kt + S - 1);
     read(1, cur, 1);
     mma(0);
+    pin(true);
     barrier_after_vmcnt<NL * (S - 2)>();
     read(0, nxt, 0);
     mma(1);
+    pin(false);
   };
 
   issue(st.s[0], 0);
