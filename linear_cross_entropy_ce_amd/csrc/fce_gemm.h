@@ -425,18 +425,19 @@ __device__ __forceinline__ void gemm_tile(Acc<C>& acc, const Opnd<typename C::El
 // start of tile t, so each tile's data has STAGES-2 tiles of MFMA work to
 // land before the barrier that publishes it.
 
-template <int ROWS, bool KMAJOR>
+template <int ROWS, bool KMAJOR, int NT_>
 struct DmaOperand;
 
 typedef short shortx4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
-template <int ROWS>
-struct DmaOperand<ROWS, true> {
-  static constexpr int BK = 32, NT = 256;
+template <int ROWS, int NT_>
+struct DmaOperand<ROWS, true, NT_> {
+  static constexpr int BK = 32, NT = NT_;
   static constexpr int BYTES = ROWS * BK * 2;       // per stage
   static constexpr int NI = BYTES / (NT * 16);      // DMA instructions per thread per tile
-  static constexpr int ROWS_PER_I = NT * 16 / 64;   // 64 rows per instruction round
+  static constexpr int ROWS_PER_I = NT * 16 / 64;   // rows per instruction round
+  static_assert(NI >= 1 && BYTES % (NT * 16) == 0, "K-major DMA geometry");
   const bf16* tile;
   int64_t rows_left;
   uint32_t voff0, istep;
@@ -453,7 +454,18 @@ struct DmaOperand<ROWS, true> {
   }
   __device__ __forceinline__ void load(char* stage, int wave, const Opnd<bf16>& op, int k0,
                                        bool live) const {
-    const __amdgpu_buffer_rsrc_t rs = make_rsrc(tile + k0, (rows_left * op.ld - k0) * 2);
+    load_rows(stage, wave, op, tile, rows_left, k0, live);
+  }
+  // The same load for the tile whose first row is mn0 (any tile of `op`).
+  __device__ __forceinline__ void load_at(char* stage, int wave, const Opnd<bf16>& op, int mn0,
+                                          int k0, bool live) const {
+    load_rows(stage, wave, op, op.p + static_cast<int64_t>(mn0) * op.ld, op.mn_ext - mn0, k0,
+              live);
+  }
+  __device__ __forceinline__ void load_rows(char* stage, int wave, const Opnd<bf16>& op,
+                                            const bf16* tile_, int64_t rows_left_, int k0,
+                                            bool live) const {
+    const __amdgpu_buffer_rsrc_t rs = make_rsrc(tile_ + k0, (rows_left_ * op.ld - k0) * 2);
     const uint32_t off = (live && k0 + kc < op.k_ext) ? voff0 : kOOB;
 #pragma unroll
     for (int i = 0; i < NI; ++i)
@@ -462,14 +474,15 @@ struct DmaOperand<ROWS, true> {
   }
 };
 
-template <int ROWS>
-struct DmaOperand<ROWS, false> {
-  static constexpr int BK = 32, NT = 256;
+template <int ROWS, int NT_>
+struct DmaOperand<ROWS, false, NT_> {
+  static constexpr int BK = 32, NT = NT_;
   static constexpr int ROWB = ROWS * 2;              // bytes per k-row
   static constexpr int BYTES = BK * ROWB;
   static constexpr int NI = BYTES / (NT * 16);
   static constexpr int KROWS_PER_I = NT * 16 / ROWB;
   static_assert(ROWB % 1024 == 0 || 1024 % ROWB == 0, "k-rows tile the 1 KiB DMA blocks");
+  static_assert(NI >= 1 && BYTES % (NT * 16) == 0, "MN-major DMA geometry");
   const bf16* tile;
   int mn0;
   uint32_t voff0, istep;
@@ -497,11 +510,11 @@ struct DmaOperand<ROWS, false> {
 };
 
 // Per-lane fragment addressing of one operand (relative to the stage base).
-template <int ROWS, bool KMAJOR>
+template <int ROWS, bool KMAJOR, int NF>
 struct FragAddr;
 
-template <int ROWS>
-struct FragAddr<ROWS, true> {
+template <int ROWS, int NF>
+struct FragAddr<ROWS, true, NF> {
   int off[2];  // byte offset of fragment 0 for sub-steps 0 and 1
   __device__ __forceinline__ void init(int wave_base, int lane) {
     const int r = wave_base + (lane & 31);
@@ -514,17 +527,17 @@ struct FragAddr<ROWS, true> {
   }
 };
 
-template <int ROWS>
-struct FragAddr<ROWS, false> {
+template <int ROWS, int NF>
+struct FragAddr<ROWS, false, NF> {
   static constexpr int ROWB = ROWS * 2;
-  int off[4];  // byte offset for fragments f = 0..3 (sub-step 0, half 0)
+  int off[NF];  // byte offset for fragments f = 0..NF-1 (sub-step 0, half 0)
   __device__ __forceinline__ void init(int wave_base, int lane) {
     const int gq = lane >> 4, a = lane & 15;
     const int kr0 = 8 * (gq >> 1) + (a >> 2);
     const int g = 4 * (a >> 2);  // swizzle of row kr0 + 4h + 16 k16 (all = kr0 mod 4)
     const int mnoff = 16 * (gq & 1) + 4 * (a & 3);
 #pragma unroll
-    for (int f = 0; f < 4; ++f) {
+    for (int f = 0; f < NF; ++f) {
       const int mn = wave_base + 32 * f + mnoff;
       off[f] = kr0 * ROWB + 16 * ((mn >> 3) ^ g) + (mn & 7) * 2;
     }
@@ -560,112 +573,182 @@ __device__ __forceinline__ void barrier_after_vmcnt() {
   __builtin_amdgcn_s_barrier();
 }
 
-// One 256 x 256 bf16 output tile with 4 waves of 128 x 128 (2 x 2), the
-// operands in any layout, via the 4-stage DMA pipeline.  The K loop is
-// unrolled by the stage count so every stage reference is static.  Ends with
-// all DMA drained and a barrier, so the stages may be reused after it.
+// The per-wave machinery of the DMA pipeline for one BM x BN tile shape:
+// operand DMA, fragment reads, MFMAs and the pinned interleaving of one
+// 32-deep K step.  Any wave layout C::WAVES_M x C::WAVES_N whose wave tile is
+// a multiple of 32 x 32; 256 or 512 threads.
 template <class C, bool A_KMAJOR, bool B_KMAJOR>
-__device__ __forceinline__ void gemm_tile_dma(Acc<C>& acc, const Opnd<bf16>& A,
-                                              const Opnd<bf16>& B, int m0, int n0, int K,
-                                              const DmaStages& st, int tid) {
-  static_assert(C::BM == 256 && C::BN == 256 && C::NT == 256 && C::FM == 4 && C::FN == 4,
-                "DMA main loop geometry");
-  constexpr int S = 4;  // stages
-  constexpr int BK = 32;
-  constexpr int B_OFF = 256 * BK * 2;
-  typedef DmaOperand<256, A_KMAJOR> DA;
-  typedef DmaOperand<256, B_KMAJOR> DB;
-  constexpr int NL = DA::NI + DB::NI;  // DMA instructions per thread per tile
-#pragma unroll
-  for (int fm = 0; fm < 4; ++fm)
-#pragma unroll
-    for (int fn = 0; fn < 4; ++fn)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) acc.v[fm][fn][i] = 0.0f;
-  const int nk = (K + BK - 1) / BK;
-  if (nk <= 0) return;
+struct DmaEngine {
+  static constexpr int S = 4, BK = 32;
+  static constexpr int B_OFF = C::BM * BK * 2;
+  static constexpr int FM = C::FM, FN = C::FN;
+  typedef DmaOperand<C::BM, A_KMAJOR, C::NT> DA;
+  typedef DmaOperand<C::BN, B_KMAJOR, C::NT> DB;
+  static constexpr int NL = DA::NI + DB::NI;  // DMA instructions per thread per K tile
+  // LDS read instructions per fragment set: one b128 per K-major fragment,
+  // two b64 transpose reads per MN-major fragment
+  static constexpr int NR = FM * (A_KMAJOR ? 1 : 2) + FN * (B_KMAJOR ? 1 : 2);
+  static constexpr int NMMA = FM * FN;         // MFMAs per 16-deep sub-step
+  static constexpr int NG = NMMA / 2;          // interleave groups (first half of the MFMAs)
+  static constexpr int RG = (NR + NG - 1) / NG, LG = (NL + NG - 1) / NG;
+  static_assert(C::BM * BK * 2 + C::BN * BK * 2 <= 32768, "one K tile per 32 KiB stage");
 
-  const int lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wm = wave / 2, wn = wave % 2;
   DA da;
   DB db;
-  da.init(A, m0, tid);
-  db.init(B, n0, tid);
-  FragAddr<256, A_KMAJOR> fa_addr;
-  FragAddr<256, B_KMAJOR> fb_addr;
-  fa_addr.init(wm * 128, lane);
-  fb_addr.init(wn * 128, lane);
+  FragAddr<C::BM, A_KMAJOR, FM> fa_addr;
+  FragAddr<C::BN, B_KMAJOR, FN> fb_addr;
+  bf16x8 fa[2][FM], fb[2][FN];
+  int wave;
 
-  auto issue = [&](char* stage, int kt) {
-    const bool live = kt < nk;
-    da.load(stage, wave, A, kt * BK, live);
-    db.load(stage + B_OFF, wave, B, kt * BK, live);
-  };
-  bf16x8 fa[2][4], fb[2][4];
-  auto read = [&](int set, const char* stage, int k16) {
+  __device__ __forceinline__ void init(const Opnd<bf16>& A, const Opnd<bf16>& B, int m0, int n0,
+                                       int tid) {
+    const int lane = tid & 63;
+    wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wm = wave / C::WAVES_N, wn = wave % C::WAVES_N;
+    da.init(A, m0, tid);
+    db.init(B, n0, tid);
+    fa_addr.init(wm * C::WTM, lane);
+    fb_addr.init(wn * C::WTN, lane);
+  }
+  __device__ __forceinline__ void read(int set, const char* stage, int k16) {
 #pragma unroll
-    for (int f = 0; f < 4; ++f) {
-      fa[set][f] = fa_addr.read(stage, f, k16);
-      fb[set][f] = fb_addr.read(stage + B_OFF, f, k16);
+    for (int f = 0; f < (FM > FN ? FM : FN); ++f) {
+      if (f < FM) fa[set][f] = fa_addr.read(stage, f, k16);
+      if (f < FN) fb[set][f] = fb_addr.read(stage + B_OFF, f, k16);
     }
-  };
-  auto mma = [&](int set) {
+  }
+  __device__ __forceinline__ void mma(Acc<C>& acc, int set) {
 #pragma unroll
-    for (int fm = 0; fm < 4; ++fm)
+    for (int fm = 0; fm < FM; ++fm)
 #pragma unroll
-      for (int fn = 0; fn < 4; ++fn)
+      for (int fn = 0; fn < FN; ++fn)
         acc.v[fm][fn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[set][fm], fb[set][fn],
                                                                 acc.v[fm][fn], 0, 0, 0);
-  };
-  // Tile kt lives in stage kt % 4.  Trip step for tile kt in stage `cur`:
-  // prefetch tile kt+3 into the stage of tile kt-1 (free since the previous
-  // barrier), read sub-step 1 of tile kt, MFMA sub-step 0, publish tile kt+1
-  // (wait for this thread's DMA of it, barrier), read its sub-step 0, MFMA
-  // sub-step 1.
-  // LDS read instructions per fragment set: one b128 per K-major fragment,
-  // two b64 transpose reads per MN-major fragment.
-  constexpr int NR = 4 * (A_KMAJOR ? 1 : 2) + 4 * (B_KMAJOR ? 1 : 2);
-  constexpr int RG = (NR + 7) / 8, LG = (NL + 7) / 8;  // per-group sizes (groups may run short)
+  }
   // Pin the order: the reads of the next fragment set (and the DMA issue)
-  // go between the first eight MFMAs of the current set, so both fragment
+  // go between the first half of the current set's MFMAs, so both fragment
   // sets stay live and no MFMA waits on an LDS round trip.
-  auto pin = [&](bool with_dma) {
+  __device__ __forceinline__ static void pin(bool with_dma) {
 #pragma unroll
-    for (int g = 0; g < 8; ++g) {
+    for (int g = 0; g < NG; ++g) {
       __builtin_amdgcn_sched_group_barrier(kSchedMFMA, 1, 0);
       __builtin_amdgcn_sched_group_barrier(kSchedDSRead, RG, 0);
       if (with_dma) __builtin_amdgcn_sched_group_barrier(kSchedVMEMRead, LG, 0);
     }
-    __builtin_amdgcn_sched_group_barrier(kSchedMFMA, 8, 0);
+    __builtin_amdgcn_sched_group_barrier(kSchedMFMA, NMMA - NG, 0);
     __builtin_amdgcn_sched_barrier(0);
-  };
-  auto step = [&](int kt, char* cur, char* nxt, char* prv) {
-    issue(prv, kt + S - 1);
+  }
+  // One K tile in stage `cur`: prefetch (issue_next) into the stage of the
+  // previous tile (free since the previous barrier), read sub-step 1, MFMA
+  // sub-step 0, publish the next tile (wait for this thread's DMA of it,
+  // barrier), read its sub-step 0, MFMA sub-step 1.
+  template <class Issue>
+  __device__ __forceinline__ void step(Acc<C>& acc, const char* cur, const char* nxt,
+                                       Issue&& issue_next) {
+    issue_next();
     read(1, cur, 1);
-    mma(0);
+    mma(acc, 0);
     pin(true);
     barrier_after_vmcnt<NL * (S - 2)>();
     read(0, nxt, 0);
-    mma(1);
+    mma(acc, 1);
     pin(false);
-  };
+  }
+};
 
+template <class C>
+__device__ __forceinline__ void zero_acc(Acc<C>& acc) {
+#pragma unroll
+  for (int fm = 0; fm < C::FM; ++fm)
+#pragma unroll
+    for (int fn = 0; fn < C::FN; ++fn)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) acc.v[fm][fn][i] = 0.0f;
+}
+
+// One BM x BN bf16 output tile, operands in any layout, through the 4-stage
+// DMA pipeline.  The K loop is unrolled by the stage count so every stage
+// reference is static.  When the tile count is not a multiple of four the
+// last trip runs on tiles past the end, whose stages hold the zeros of
+// out-of-range loads: their MFMAs add exact zeros.  Ends with all DMA
+// drained and a barrier, so the stages may be reused after it.
+template <class C, bool A_KMAJOR, bool B_KMAJOR>
+__device__ __forceinline__ void gemm_tile_dma(Acc<C>& acc, const Opnd<bf16>& A,
+                                              const Opnd<bf16>& B, int m0, int n0, int K,
+                                              const DmaStages& st, int tid) {
+  typedef DmaEngine<C, A_KMAJOR, B_KMAJOR> E;
+  constexpr int S = E::S, BK = E::BK;
+  zero_acc(acc);
+  const int nk = (K + BK - 1) / BK;
+  if (nk <= 0) return;
+  E e;
+  e.init(A, B, m0, n0, tid);
+  auto issue = [&](char* stage, int kt) {
+    const bool live = kt < nk;
+    e.da.load(stage, e.wave, A, kt * BK, live);
+    e.db.load(stage + E::B_OFF, e.wave, B, kt * BK, live);
+  };
   issue(st.s[0], 0);
   issue(st.s[1], 1);
   issue(st.s[2], 2);
-  barrier_after_vmcnt<NL * (S - 2)>();
-  read(0, st.s[0], 0);
-  // Four tiles per trip.  When the tile count is not a multiple of four the
-  // last trip runs on tiles past the end, whose stages hold the zeros of
-  // out-of-range loads: their MFMAs add exact zeros.
+  barrier_after_vmcnt<E::NL * (S - 2)>();
+  e.read(0, st.s[0], 0);
   for (int kt = 0; kt < nk; kt += S) {
-    step(kt, st.s[0], st.s[1], st.s[3]);
-    step(kt + 1, st.s[1], st.s[2], st.s[0]);
-    step(kt + 2, st.s[2], st.s[3], st.s[1]);
-    step(kt + 3, st.s[3], st.s[0], st.s[2]);
+    e.step(acc, st.s[0], st.s[1], [&] { issue(st.s[3], kt + 3); });
+    e.step(acc, st.s[1], st.s[2], [&] { issue(st.s[0], kt + 4); });
+    e.step(acc, st.s[2], st.s[3], [&] { issue(st.s[1], kt + 5); });
+    e.step(acc, st.s[3], st.s[0], [&] { issue(st.s[2], kt + 6); });
   }
   // the prefetches past the last tile still write (zeros) into LDS: drain them
+  barrier_after_vmcnt<0>();
+}
+
+// Consecutive BM-row M tiles mt_begin .. mt_end-1 (K-major A, full K each)
+// against one BN-column N tile of K-major B, as ONE stream of K tiles: the
+// DMA for the next M tile's first K tiles is issued while the current one
+// finishes, so the pipeline never drains between M tiles.  After each M tile
+// epi(acc, m0) consumes the accumulators (registers only; LDS stays with the
+// pipeline) and they restart from zero.  Needs K % 128 == 0 (M tile
+// boundaries on the unrolled-by-four trip).  Ends with all DMA drained and a
+// barrier.
+template <class C, class Epi>
+__device__ __forceinline__ void gemm_stream_dma(const Opnd<bf16>& A, const Opnd<bf16>& B,
+                                                int mt_begin, int mt_end, int n0, int K,
+                                                const DmaStages& st, int tid, Epi&& epi) {
+  typedef DmaEngine<C, true, true> E;
+  constexpr int S = E::S, BK = E::BK;
+  const int nk = K / BK;
+  const int total = (mt_end - mt_begin) * nk;
+  Acc<C> acc;
+  zero_acc(acc);
+  if (total <= 0) return;
+  E e;
+  e.init(A, B, mt_begin * C::BM, n0, tid);
+  // stream position g = (M tile index) * nk + (K tile index)
+  auto issue = [&](char* stage, int g) {
+    const bool live = g < total;
+    const int gg = live ? g : 0;
+    const int k0 = (gg % nk) * BK;
+    e.da.load_at(stage, e.wave, A, (mt_begin + gg / nk) * C::BM, k0, live);
+    e.db.load(stage + E::B_OFF, e.wave, B, k0, live);
+  };
+  issue(st.s[0], 0);
+  issue(st.s[1], 1);
+  issue(st.s[2], 2);
+  barrier_after_vmcnt<E::NL * (S - 2)>();
+  e.read(0, st.s[0], 0);
+  for (int mt = mt_begin; mt < mt_end; ++mt) {
+    const int base = (mt - mt_begin) * nk;
+    for (int kt = 0; kt < nk; kt += S) {
+      const int g = base + kt;
+      e.step(acc, st.s[0], st.s[1], [&] { issue(st.s[3], g + 3); });
+      e.step(acc, st.s[1], st.s[2], [&] { issue(st.s[0], g + 4); });
+      e.step(acc, st.s[2], st.s[3], [&] { issue(st.s[1], g + 5); });
+      e.step(acc, st.s[3], st.s[0], [&] { issue(st.s[2], g + 6); });
+    }
+    epi(acc, mt * C::BM);
+    zero_acc(acc);
+  }
   barrier_after_vmcnt<0>();
 }
 

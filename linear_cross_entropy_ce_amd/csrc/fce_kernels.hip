@@ -127,10 +127,9 @@ __global__ __launch_bounds__(C::NT) void k_fwd_lse(FwdArgs<typename C::Elem> a) 
     rl[fn] = rt[fn] = rz[fn] = 0.0f;
   }
 
-  Acc<C> acc;
-  for (int vt = vt_begin; vt < vt_end; ++vt) {
-    const int m0 = vt * C::BM;
-    gemm_any<C, true, true>(acc, A, B, m0, n0, a.H, lds, tid);
+  // Running (max, sum-exp, target logit, logit sum) update of one logit tile
+  // whose rows are the vocabulary entries m0 .. m0+BM-1.
+  auto lse_update = [&](const Acc<C>& acc, int m0) {
     const int vbase = m0 + wm * C::WTM + 4 * (lane >> 5);
     const bool full = m0 + C::BM <= a.V;
 #pragma unroll
@@ -161,6 +160,18 @@ __global__ __launch_bounds__(C::NT) void k_fwd_lse(FwdArgs<typename C::Elem> a) 
       rm[fn] = mnew;
       rt[fn] += tg;
       rz[fn] += zs;
+    }
+  };
+  if (sizeof(T) == 2 && a.H % 128 == 0) {
+    // bf16: all vocabulary tiles of this split as one DMA stream
+    if constexpr (sizeof(T) == 2)
+      gemm_stream_dma<C>(A, B, vt_begin, vt_end, n0, a.H, lds, tid, lse_update);
+  } else {
+    Acc<C> acc;
+    for (int vt = vt_begin; vt < vt_end; ++vt) {
+      const int m0 = vt * C::BM;
+      gemm_any<C, true, true>(acc, A, B, m0, n0, a.H, lds, tid);
+      lse_update(acc, m0);
     }
   }
 
