@@ -13,7 +13,6 @@ Prints ONE JSON line on stdout; progress goes to stderr.
 from __future__ import annotations
 
 import argparse
-import hashlib
 import json
 import os
 import sys
@@ -24,20 +23,10 @@ sys.path.insert(0, ROOT)
 
 PEAK = {"bf16": 2516.6, "fp32": 157.3}  # MI355X dense MFMA TFLOP/s (256 CUs x 2.4 GHz)
 HBM_PEAK_GBS = 8000.0
-CSRC = os.path.join(ROOT, "linear_cross_entropy_ce_amd", "csrc")
 
 
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
-
-
-def source_digest() -> str:
-    h = hashlib.sha256()
-    for name in sorted(os.listdir(CSRC)):
-        with open(os.path.join(CSRC, name), "rb") as f:
-            h.update(name.encode())
-            h.update(f.read())
-    return h.hexdigest()[:16]
 
 
 def read_traffic(kernel: str, workload: str, launches_per_step: float):
@@ -50,6 +39,8 @@ def read_traffic(kernel: str, workload: str, launches_per_step: float):
         rec = json.load(open(path))
     except (OSError, ValueError):
         return None
+    from linear_cross_entropy_ce_amd.profiling import source_digest
+
     if rec.get("source_sha256") != source_digest():
         return None
     return rec.get("hbm_bytes_per_launch")
