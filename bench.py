@@ -5,10 +5,16 @@ forward logit tiles with the on-chip LSE reduction, LSE merge and loss, then
 the backward recompute, dW and dX products for every logit block).  Inputs
 and outputs are resident in device memory before the timed region.
 
+Besides the headline step it times, outside the headline figure: the
+forward and backward entry points on their own, the same step at the other
+chunk sizes and with the token-chunk schedule, and (as context) a naive
+torch step that materialises the logits.
+
 Prints ONE JSON line on stdout; progress goes to stderr.
 
     python bench.py [--gpus 1] [--steps 20] [--warmup 3] [--workload 3]
-                    [--chunk 1024] [--schedule auto] [--cpu-sample-tokens 1024]
+                    [--chunk 1024] [--schedule auto] [--cpu-sample-tokens 4096]
+                    [--sweep-chunks 256,512] [--no-naive] [--no-cpu-baseline]
 """
 from __future__ import annotations
 
@@ -59,6 +65,12 @@ def cpu_baseline(wl, inp, n_tokens: int):
                        if i.get("user_api") == "blas"] or [1])
     except Exception:  # pragma: no cover
         threads = os.cpu_count() or 1
+    model = "unknown CPU"
+    try:
+        with open("/proc/cpuinfo") as f:
+            model = next(l.split(":", 1)[1].strip() for l in f if l.startswith("model name"))
+    except (OSError, StopIteration):
+        pass
     n = min(n_tokens, wl.N)
     X, y = inp.X[:n], inp.labels[:n]
     t0 = time.perf_counter()
@@ -66,7 +78,51 @@ def cpu_baseline(wl, inp, n_tokens: int):
     dt = time.perf_counter() - t0
     return {"value": n / dt, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
             "sample": f"first {n} of {wl.N} tokens of {wl.name} (full V={wl.V}, H={wl.H}); "
-                      f"fp64 numpy, {6 * n * wl.V * wl.H / 1e12:.2f} TFLOP executed in {dt:.1f} s"}
+                      f"fp64 numpy on {model}, {6 * n * wl.V * wl.H / 1e12:.2f} TFLOP executed in {dt:.1f} s"}
+
+
+def time_steps(torch, fn, steps, stream):
+    """Total and per-step milliseconds of ``steps`` calls, from events on ``stream``."""
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    torch.cuda.synchronize()
+    ev[0].record(stream)
+    for i in range(steps):
+        fn()
+        ev[i + 1].record(stream)
+    torch.cuda.synchronize()
+    per = [ev[i].elapsed_time(ev[i + 1]) for i in range(steps)]
+    return ev[0].elapsed_time(ev[-1]), per
+
+
+def naive_torch(torch, X, W, y, eps, steps):
+    """Context only: logits materialised by a torch GEMM, torch's cross-entropy
+    in fp32, autograd backward.  Time per step and peak bytes above the inputs."""
+    import torch.nn.functional as F
+
+    Xp = X.detach().clone().requires_grad_(True)
+    Wp = W.detach().clone().requires_grad_(True)
+    y64 = y.long()
+
+    def step():
+        Xp.grad = None
+        Wp.grad = None
+        z = Xp @ Wp.t()
+        loss = F.cross_entropy(z.float(), y64, ignore_index=-100, label_smoothing=eps)
+        loss.backward()
+
+    step()
+    torch.cuda.synchronize()
+    Xp.grad = None
+    Wp.grad = None
+    base = torch.cuda.memory_allocated()
+    torch.cuda.reset_peak_memory_stats()
+    total, per = time_steps(torch, step, steps, torch.cuda.current_stream())
+    peak = torch.cuda.max_memory_allocated() - base
+    del Xp, Wp
+    torch.cuda.empty_cache()
+    return {"what": "torch GEMM X @ W^T (bf16) + F.cross_entropy on fp32 logits + autograd; context only",
+            "ms_per_step": round(total / steps, 3), "steps": steps,
+            "peak_bytes_above_inputs": int(peak)}
 
 
 def main():
@@ -79,6 +135,9 @@ def main():
     ap.add_argument("--schedule", default="auto", choices=["auto", "token", "vocab"])
     ap.add_argument("--cpu-sample-tokens", type=int, default=4096)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--sweep-chunks", default="256,512")
+    ap.add_argument("--side-steps", type=int, default=10)
+    ap.add_argument("--no-naive", action="store_true")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -101,39 +160,40 @@ def main():
     plan = fce.fce_plan(N, H, V, fce.FCE_BF16 if wl.dtype == "bf16" else fce.FCE_F32, chunk,
                         fce.SCHEDULES[sched])
     log(f"plan: {plan}")
+    base_alloc = torch.cuda.memory_allocated()
+    torch.cuda.reset_peak_memory_stats()
     ws = fce.workspace_for(N, H, V, X.dtype, chunk, sched)
     loss = torch.empty(1, device="cuda")
+    lse = torch.empty(N, device="cuda")
     dX = torch.empty((N, H), device="cuda")
     dW = torch.empty((V, H), device="cuda")
+    out_bytes = 4 * (1 + N + N * H + V * H)
     eps = wl.label_smoothing
+    stream = torch.cuda.current_stream()
 
-    def step():
+    def step(ws=ws, chunk=chunk, sched=sched):
         fce.fce_fused_fwd_bwd(X, W, y, loss, dX, dW, ws, wk.IGNORE_INDEX, eps, "mean", chunk, sched)
 
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
+    # everything the step allocated beyond inputs and outputs: the workspace only
+    peak_delta = torch.cuda.max_memory_allocated() - base_alloc - out_bytes
     log(f"warmup done, loss {loss.item():.6f}")
 
-    stream = torch.cuda.current_stream()
-    t_start = torch.cuda.Event(enable_timing=True)
-    t_end = torch.cuda.Event(enable_timing=True)
     fce.fce_timing_enable(True)
-    torch.cuda.synchronize()
-    t_start.record(stream)
-    for _ in range(args.steps):
-        step()
-    t_end.record(stream)
-    torch.cuda.synchronize()
+    total_ms, per_step = time_steps(torch, step, args.steps, stream)
     kernels = fce.fce_timing_read()
     fce.fce_timing_enable(False)
-    total_ms = t_start.elapsed_time(t_end)
     ms = total_ms / args.steps
     tokens_per_s = N / (ms / 1e3)
     flops_step = 8.0 * N * V * H
     peak = PEAK[wl.dtype]
     tflops = flops_step / (ms / 1e3) / 1e12
-    log(f"{args.steps} steps: {ms:.3f} ms/step, {tokens_per_s:,.0f} tokens/s, "
+    srt = sorted(per_step)
+    med = srt[len(srt) // 2] if len(srt) % 2 else 0.5 * (srt[len(srt) // 2 - 1] + srt[len(srt) // 2])
+    log(f"{args.steps} steps: {ms:.3f} ms/step (median {med:.3f}, min {srt[0]:.3f}, "
+        f"max {srt[-1]:.3f}), {tokens_per_s:,.0f} tokens/s, "
         f"{tflops:.1f} TFLOP/s = {100 * tflops / peak:.1f}% of {peak} TFLOP/s")
 
     # dominant kernel: largest share of the timed region
@@ -153,7 +213,42 @@ def main():
     roofline = {"bound": "mfma", "kernel": dom, "achieved": round(achieved, 2), "peak": peak,
                 "unit": "TFLOP/s", "frac": round(achieved / peak, 4), "traffic": traffic}
 
+    # ---- outside the headline figure
+    side = {}
+    k2 = args.side_steps
+    fwd = lambda: fce.fce_forward(X, W, y, loss, lse, ws, wk.IGNORE_INDEX, eps, "mean", chunk, sched)
+    bwd = lambda: fce.fce_backward(X, W, y, lse, None, dX, dW, ws, wk.IGNORE_INDEX, eps, "mean",
+                                   chunk, sched)
+    fwd()
+    bwd()
+    t_f, _ = time_steps(torch, fwd, k2, stream)
+    t_b, _ = time_steps(torch, bwd, k2, stream)
+    side["fce_forward"] = {"ms": round(t_f / k2, 4), "tflops_2NVH": round(2 * N * V * H / (t_f / k2 / 1e3) / 1e12, 1)}
+    side["fce_backward"] = {"ms": round(t_b / k2, 4), "tflops_6NVH": round(6 * N * V * H / (t_b / k2 / 1e3) / 1e12, 1)}
+    log(f"  forward alone {t_f / k2:.3f} ms, backward alone {t_b / k2:.3f} ms")
+    sweep = {str(chunk) + "/" + sched: round(ms, 4)}
+    variants = [(int(c), sched) for c in args.sweep_chunks.split(",") if c and int(c) != chunk]
+    if sched != "token":
+        variants.append((chunk, "token"))
+    for c, sc in variants:
+        ws_c = fce.workspace_for(N, H, V, X.dtype, c, sc)
+        fn = lambda: step(ws_c, c, sc)
+        fn()
+        t_c, _ = time_steps(torch, fn, k2, stream)
+        sweep[f"{c}/{sc}"] = round(t_c / k2, 4)
+        log(f"  chunk {c} schedule {sc}: {t_c / k2:.3f} ms/step")
+        del ws_c
+    side["ms_per_step_by_chunk_schedule"] = sweep
+    if not args.no_naive:
+        try:
+            side["naive_torch"] = naive_torch(torch, X, W, y, eps, min(k2, 5))
+            log(f"  naive torch: {side['naive_torch']}")
+        except torch.cuda.OutOfMemoryError as e:  # pragma: no cover
+            side["naive_torch"] = {"error": str(e)[:200]}
+
     mem = {"logit_scratch_bytes": plan["scratch_bytes"],
+           "workspace_bytes": plan["workspace_bytes"],
+           "measured_peak_alloc_beyond_inputs_outputs": int(peak_delta),
            "naive_logits_bytes": N * V * (2 if wl.dtype == "bf16" else 4),
            "naive_3x_bytes": 3 * N * V * (2 if wl.dtype == "bf16" else 4),
            "chunk_tile_bound_bytes": chunk * V * (2 if wl.dtype == "bf16" else 4)}
@@ -172,6 +267,9 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(ms, 4),
+        "ms_per_step_median": round(med, 4),
+        "ms_per_step_min": round(srt[0], 4),
+        "ms_per_step_max": round(srt[-1], 4),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -188,6 +286,7 @@ def main():
         "cpu_baseline": cpu,
         "kernels": kern,
         "memory": mem,
+        "side": side,
     }
     print(json.dumps(out), flush=True)
 

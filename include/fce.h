@@ -141,6 +141,12 @@ fce_status fce_get_label_errors(const void* workspace, int32_t* host_count, hipS
 /* Static description of a status code. */
 const char* fce_status_string(fce_status status);
 
+/* The HIP runtime's description of the last HIP error behind an
+ * FCE_ERR_HIP returned to the calling thread, or "none".  The string is
+ * static (owned by the HIP runtime); the record is per thread and is
+ * overwritten by the next such error. */
+const char* fce_last_hip_error(void);
+
 /* Per-kernel timing.  While enabled, every kernel the library launches is
  * bracketed by HIP events on the caller's stream.  fce_timing_read
  * synchronises on the recorded events, fills up to `cap` entries and resets

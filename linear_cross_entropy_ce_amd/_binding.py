@@ -33,13 +33,17 @@ SCHEDULES = {"auto": SCHED_AUTO, "token": SCHED_TOKEN, "vocab": SCHED_VOCAB}
 REDUCTIONS = {"mean": FCE_MEAN, "sum": FCE_SUM}
 
 EXPORTED = ("fce_workspace_size", "fce_plan", "fce_forward", "fce_backward", "fce_fused_fwd_bwd",
-            "fce_get_label_errors", "fce_status_string", "fce_timing_enable", "fce_timing_read")
+            "fce_get_label_errors", "fce_status_string", "fce_last_hip_error",
+            "fce_timing_enable", "fce_timing_read")
 
 
 class FceError(RuntimeError):
     def __init__(self, status: int, where: str):
         self.status = status
-        super().__init__(f"{where}: {status_string(status)} (status {status})")
+        msg = f"{where}: {status_string(status)} (status {status})"
+        if status == FCE_ERR_HIP:
+            msg += f": {load_library().fce_last_hip_error().decode()}"
+        super().__init__(msg)
 
 
 class PlanInfo(ctypes.Structure):
@@ -69,6 +73,13 @@ def load_library(path: str = LIB_PATH):
     if not os.path.exists(path):
         raise ImportError(f"{path} is missing: build it with "
                           f"`python -m linear_cross_entropy_ce_amd.build`")
+    # torch wheels carry their own HIP runtime.  Load it first, so that
+    # libfce.so binds to the same runtime that owns torch's memory and
+    # streams instead of pulling in a second one.
+    try:
+        import torch  # noqa: F401
+    except ImportError:
+        pass
     lib = ctypes.CDLL(path)
     i64, u64, i32, f32, vp = ctypes.c_int64, ctypes.c_size_t, ctypes.c_int32, ctypes.c_float, ctypes.c_void_p
     lib.fce_workspace_size.restype = u64
@@ -86,6 +97,8 @@ def load_library(path: str = LIB_PATH):
     lib.fce_get_label_errors.argtypes = [vp, ctypes.POINTER(i32), vp]
     lib.fce_status_string.restype = ctypes.c_char_p
     lib.fce_status_string.argtypes = [i32]
+    lib.fce_last_hip_error.restype = ctypes.c_char_p
+    lib.fce_last_hip_error.argtypes = []
     lib.fce_timing_enable.restype = i32
     lib.fce_timing_enable.argtypes = [i32]
     lib.fce_timing_read.restype = i32

@@ -16,6 +16,16 @@
 
 namespace {
 
+// Last HIP error a library call of this thread ran into (for
+// fce_last_hip_error); hipSuccess until one does.
+thread_local hipError_t t_last_hip = hipSuccess;
+
+fce_status from_hip(hipError_t e) {
+  if (e == hipSuccess) return FCE_OK;
+  t_last_hip = e;
+  return FCE_ERR_HIP;
+}
+
 using fce::Dtype;
 using fce::Plan;
 using fce::Schedule;
@@ -78,12 +88,12 @@ fce::KernelTimer* timer() {
 
 fce_status check_device() {
   int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess) return FCE_ERR_HIP;
+  if (hipError_t e = hipGetDevice(&dev); e != hipSuccess) return from_hip(e);
   if (dev < 0 || dev >= 64) return FCE_ERR_DEVICE;
   std::lock_guard<std::mutex> lock(g_arch_mu);
   if (g_arch_ok[dev] == 0) {
     hipDeviceProp_t prop;
-    if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return FCE_ERR_HIP;
+    if (hipError_t e = hipGetDeviceProperties(&prop, dev); e != hipSuccess) return from_hip(e);
     g_arch_ok[dev] = (std::strncmp(prop.gcnArchName, "gfx950", 6) == 0) ? 1 : -1;
   }
   return g_arch_ok[dev] == 1 ? FCE_OK : FCE_ERR_DEVICE;
@@ -113,7 +123,6 @@ fce_status validate(const void* X, const void* W, const int32_t* labels, int64_t
   return FCE_OK;
 }
 
-fce_status from_hip(hipError_t e) { return e == hipSuccess ? FCE_OK : FCE_ERR_HIP; }
 
 }  // namespace
 
@@ -226,9 +235,10 @@ fce_status fce_get_label_errors(const void* workspace, int32_t* host_count, hipS
   if (workspace == nullptr || host_count == nullptr) return FCE_ERR_NULL;
   const fce::Ctrl* ctrl = static_cast<const fce::Ctrl*>(workspace);
   fce::Ctrl h;
-  if (hipMemcpyAsync(&h, ctrl, sizeof(h), hipMemcpyDeviceToHost, stream) != hipSuccess)
-    return FCE_ERR_HIP;
-  if (hipStreamSynchronize(stream) != hipSuccess) return FCE_ERR_HIP;
+  if (hipError_t e = hipMemcpyAsync(&h, ctrl, sizeof(h), hipMemcpyDeviceToHost, stream);
+      e != hipSuccess)
+    return from_hip(e);
+  if (hipError_t e = hipStreamSynchronize(stream); e != hipSuccess) return from_hip(e);
   *host_count = h.n_invalid;
   return FCE_OK;
 }
@@ -245,6 +255,10 @@ const char* fce_status_string(fce_status status) {
     case FCE_ERR_HIP: return "HIP runtime error or kernel launch failure";
   }
   return "unknown status";
+}
+
+const char* fce_last_hip_error(void) {
+  return t_last_hip == hipSuccess ? "none" : hipGetErrorString(t_last_hip);
 }
 
 fce_status fce_timing_enable(int enable) {

@@ -16,8 +16,11 @@
 //   MN-major tiles are transposed in registers, VEC x VEC at a time, between
 //   the 16-byte global loads and the 16-byte LDS stores.
 //
-//   32x32 MFMA accumulator layout (wave64): element i of lane l holds
-//   row 8*(i/4) + 4*(l/32) + (i%4), column l%32 of the 32x32 block.
+//   Accumulator layouts (wave64).  fp32, 32x32 blocks: element i of lane l
+//   holds row 8*(i/4) + 4*(l/32) + (i%4), column l%32.  bf16, 16x16 blocks
+//   (v_mfma_f32_16x16x32_bf16): element i of lane l holds row 4*(l/16) + i,
+//   column l%16.  Either way a lane owns groups of 4 consecutive rows of one
+//   column; AccMap below names them.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -45,20 +48,17 @@ __device__ __forceinline__ float hw_log2(float x) { return __builtin_amdgcn_logf
 template <typename T>
 struct Traits;
 
-// bf16: one v_mfma_f32_32x32x16_bf16 per 16-deep K step.  Lane l supplies
-// row l%32 and the 8 consecutive k at 8*(l/32) of that step, for A and B
-// alike, so the hardware's own k order inside the instruction is irrelevant.
+// bf16: 16x16 output blocks of v_mfma_f32_16x16x32_bf16, one per 32-deep K
+// tile.  Lane l supplies row (or column) l%16 and the 8 consecutive k at
+// 8*(l/16), for A and B alike, so the hardware's own k order inside the
+// instruction is irrelevant.  (At equal FLOPs this instruction holds a
+// higher clock under the power limit than the 32x32x16 one.)  The MFMA
+// main loop for bf16 is the DMA pipeline further down.
 template <>
 struct Traits<bf16> {
   static constexpr int VEC = 8;  // elements per 16-byte vector
-  typedef bf16x8 Frag;
-  // row: LDS row base; x: (first chunk of the fragment) ^ swz(row), in bytes / 16
-  __device__ __forceinline__ static Frag frag(const char* row, int x) {
-    return *reinterpret_cast<const bf16x8*>(row + (x << 4));
-  }
-  __device__ __forceinline__ static void mma(floatx16& c, const Frag& a, const Frag& b) {
-    c = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
-  }
+  static constexpr int MB = 16, NB = 16;
+  typedef floatx4 AccT;
 };
 
 // fp32: eight v_mfma_f32_32x32x2_f32 per 16-deep K step.  Instruction j
@@ -67,6 +67,8 @@ struct Traits<bf16> {
 template <>
 struct Traits<float> {
   static constexpr int VEC = 4;
+  static constexpr int MB = 32, NB = 32;
+  typedef floatx16 AccT;
   struct Frag {
     floatx4 lo, hi;
   };
@@ -99,11 +101,13 @@ struct Cfg {
   static constexpr int VEC = Tr::VEC;
   static constexpr int LDK = BK;  // LDS row pitch (elements): 128 bytes, swizzled
   static constexpr int WTM = BM / WAVES_M, WTN = BN / WAVES_N;
-  static constexpr int FM = WTM / 32, FN = WTN / 32;
+  static constexpr int MB = Tr::MB, NB = Tr::NB;  // MFMA output block
+  static constexpr int FM = WTM / MB, FN = WTN / NB;
+  static constexpr int NV = MB * NB / 64;         // accumulator values per lane per block
   static constexpr int A_ELEMS = BM * LDK, B_ELEMS = BN * LDK;
   static constexpr int STAGE = A_ELEMS + B_ELEMS;
   static constexpr int LDS_ELEMS = 2 * STAGE;
-  static_assert(BK % 16 == 0 && WTM % 32 == 0 && WTN % 32 == 0, "tile shape");
+  static_assert(BK % 16 == 0 && WTM % MB == 0 && WTN % NB == 0, "tile shape");
   static_assert(BK * sizeof(T) == 128, "LDS rows are eight 16-byte chunks");
   static_assert(LDS_ELEMS * sizeof(T) <= 160 * 1024, "gfx950 LDS is 160 KiB per workgroup");
 };
@@ -153,10 +157,22 @@ __host__ __device__ constexpr int vmcnt_imm(int n) {
   return (n & 0xF) | ((n >> 4) << 14) | (0x7 << 4) | (0xF << 8);
 }
 
+// `base` and `bytes` must be uniform over the wave (they are moved to
+// scalar registers).
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int64_t bytes) {
-  const int64_t n = bytes < 0 ? 0 : (bytes > 0x7fffffff ? 0x7fffffff : bytes);
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, static_cast<int>(n),
-                                           0x00020000);
+  // clamp to [0, 2^31 - 1] with 32-bit compares (scalar ALU has no signed
+  // 64-bit less-than)
+  // (the empty asm keeps the halves apart in scalar registers, so the
+  // compares stay 32-bit scalar ones: there is no scalar 64-bit less-than)
+  const uint64_t u = static_cast<uint64_t>(bytes);
+  uint32_t uhi = static_cast<uint32_t>(u >> 32), ulo = static_cast<uint32_t>(u);
+  asm("" : "+s"(uhi), "+s"(ulo));
+  const uint32_t n = (uhi & 0x80000000u) ? 0u : ((uhi != 0u || ulo > 0x7fffffffu) ? 0x7fffffffu : ulo);
+  const uint64_t b = reinterpret_cast<uint64_t>(base);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(b));
+  const uint32_t hi = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(b >> 32));
+  void* bs = reinterpret_cast<void*>((static_cast<uint64_t>(hi) << 32) | lo);
+  return __builtin_amdgcn_make_buffer_rsrc(bs, 0, static_cast<int>(n), 0x00020000);
 }
 
 __device__ __forceinline__ u32x4 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
@@ -268,7 +284,20 @@ struct Loader<C, ROWS, false> {
 
 template <class C>
 struct Acc {
-  floatx16 v[C::FM][C::FN];
+  typename C::Tr::AccT v[C::FM][C::FN];
+};
+
+// Which output elements a lane holds: in block (fm, fn) of the wave tile,
+// value 4 g + q (g < NGRP, q < 4) is row fm * MB + row(lane, g) + q,
+// column fn * NB + col(lane).
+template <class C>
+struct AccMap {
+  static constexpr int MB = C::MB, NB = C::NB;
+  static constexpr int NGRP = C::NV / 4;  // groups of 4 consecutive rows
+  __device__ __forceinline__ static int row(int lane, int g) {
+    return 4 * (64 / NB) * g + 4 * (lane / NB);
+  }
+  __device__ __forceinline__ static int col(int lane) { return lane % NB; }
 };
 
 // Instruction-group masks of __builtin_amdgcn_sched_group_barrier.
@@ -304,7 +333,7 @@ __device__ __forceinline__ void gemm_tile(Acc<C>& acc, const Opnd<typename C::El
 #pragma unroll
     for (int fn = 0; fn < C::FN; ++fn)
 #pragma unroll
-      for (int i = 0; i < 16; ++i) acc.v[fm][fn][i] = 0.0f;
+      for (int i = 0; i < C::NV; ++i) acc.v[fm][fn][i] = 0.0f;
   const int nk = (K + C::BK - 1) / C::BK;
   if (nk <= 0) return;
 
@@ -412,15 +441,19 @@ __device__ __forceinline__ void gemm_tile(Acc<C>& acc, const Opnd<typename C::El
 //
 // LDS layouts (per stage, BK = 32):
 //   K-major operand:  [ROWS][32] bf16, 64-byte rows of four 16-byte chunks;
-//                     chunk c of row r at chunk c ^ ((r >> 2) & 3).
+//                     chunk c of row r at chunk c ^ km_swz(r).
 //   MN-major operand: [32][ROWS] bf16, untransposed rows of k; 16-byte chunk c
-//                     of row k at chunk c ^ 4 (k % 4).
-// Fragment reads: K-major with ds_read_b128; MN-major with two
-// ds_read_b64_tr_b16, whose 16-lane transpose hands lane l the 8 consecutive
-// k of column l % 32 (the same fragment a K-major read gives).  With 64 banks
-// of 4 bytes, the swizzles put the 16 lanes of a b128 phase (16 consecutive
-// rows) and the 32 lanes of a b64 phase (4 k-rows x 32 contiguous bytes x 2
-// column groups) on distinct banks.
+//                     of row k at chunk c ^ mn_swz(k).
+// Fragment reads (16x16x32 MFMA: lane l takes row l%16, k = 8 (l/16) .. +7):
+// K-major with one ds_read_b128; MN-major with two ds_read_b64_tr_b16.  In
+// each 16-lane group that instruction hands lane j element j%4 of the 8-byte
+// chunks addressed by lanes j/4 + 4q (q = 0..3), so lane a addressing k-row
+// 8 (l/16) + a/4 (then + 4) at column 4 (a%4) of the fragment gives lane j
+// the 8 consecutive k of column j, the same fragment a K-major read gives.
+// Both swizzles are free of LDS bank conflicts for these reads (measured with
+// SQ_LDS_BANK_CONFLICT); for the b64 transpose reads the reasoning is 64
+// banks of 4 bytes and 32-lane phases: k-rows 8G + q for two G and four q,
+// 32 contiguous bytes each, land on distinct banks.
 // Pipeline: STAGES LDS stages; the loads of tile t+STAGES-1 are issued at the
 // start of tile t, so each tile's data has STAGES-2 tiles of MFMA work to
 // land before the barrier that publishes it.
@@ -430,6 +463,17 @@ struct DmaOperand;
 
 typedef short shortx4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
+
+// Swizzle (in 16-byte chunks) of row `row` of a K-major LDS tile.  Chosen by
+// measurement (SQ_LDS_BANK_CONFLICT of ds_read_b128 with the 16x16 fragment
+// pattern below: zero for this one, about four conflict cycles per read for
+// the row bits (r >> 2) & 3, r & 3 or none).
+__host__ __device__ constexpr int km_swz(int row) { return (row >> 1) & 3; }
+
+// Swizzle (in 16-byte chunks) of k-row `krow` of an MN-major LDS tile.
+__host__ __device__ constexpr int mn_swz(int krow) {
+  return (4 * (krow & 3)) ^ (2 * ((krow >> 3) & 1));
+}
 
 template <int ROWS, int NT_>
 struct DmaOperand<ROWS, true, NT_> {
@@ -445,28 +489,32 @@ struct DmaOperand<ROWS, true, NT_> {
 
   __device__ __forceinline__ void init(const Opnd<bf16>& op, int mn0, int tid) {
     const int row = tid >> 2;              // (16 tid) / 64
-    const int c = (tid & 3) ^ ((row >> 2) & 3);
+    const int c = (tid & 3) ^ km_swz(row);
     kc = c * 8;
     tile = op.p + static_cast<int64_t>(mn0) * op.ld;
     rows_left = op.mn_ext - mn0;
     voff0 = static_cast<uint32_t>((row * op.ld + kc) * 2);
     istep = static_cast<uint32_t>(ROWS_PER_I * op.ld * 2);
   }
+  // kfull (a constant at every call): K is a whole number of 32-deep tiles,
+  // so no lane's chunk ever starts past k_ext and a dead load (live false)
+  // needs no per-lane offset: an empty descriptor returns its zeros.
   __device__ __forceinline__ void load(char* stage, int wave, const Opnd<bf16>& op, int k0,
-                                       bool live) const {
-    load_rows(stage, wave, op, tile, rows_left, k0, live);
+                                       bool live, bool kfull) const {
+    load_rows(stage, wave, op, tile, rows_left, k0, live, kfull);
   }
   // The same load for the tile whose first row is mn0 (any tile of `op`).
   __device__ __forceinline__ void load_at(char* stage, int wave, const Opnd<bf16>& op, int mn0,
-                                          int k0, bool live) const {
+                                          int k0, bool live, bool kfull) const {
     load_rows(stage, wave, op, op.p + static_cast<int64_t>(mn0) * op.ld, op.mn_ext - mn0, k0,
-              live);
+              live, kfull);
   }
   __device__ __forceinline__ void load_rows(char* stage, int wave, const Opnd<bf16>& op,
                                             const bf16* tile_, int64_t rows_left_, int k0,
-                                            bool live) const {
-    const __amdgpu_buffer_rsrc_t rs = make_rsrc(tile_ + k0, (rows_left_ * op.ld - k0) * 2);
-    const uint32_t off = (live && k0 + kc < op.k_ext) ? voff0 : kOOB;
+                                            bool live, bool kfull) const {
+    const int64_t count = (rows_left_ * op.ld - k0) * 2;
+    const __amdgpu_buffer_rsrc_t rs = make_rsrc(tile_ + k0, (kfull && !live) ? 0 : count);
+    const uint32_t off = kfull ? voff0 : ((live && k0 + kc < op.k_ext) ? voff0 : kOOB);
 #pragma unroll
     for (int i = 0; i < NI; ++i)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
@@ -481,23 +529,30 @@ struct DmaOperand<ROWS, false, NT_> {
   static constexpr int BYTES = BK * ROWB;
   static constexpr int NI = BYTES / (NT * 16);
   static constexpr int KROWS_PER_I = NT * 16 / ROWB;
+  // mn_swz has period 16 in the k-row: instructions 16 k-rows apart share the
+  // vector offset; with 8 k-rows per round, odd rounds need a second one
+  static constexpr int NV = (KROWS_PER_I % 16 == 0 || NI == 1) ? 1 : 2;
   static_assert(ROWB % 1024 == 0 || 1024 % ROWB == 0, "k-rows tile the 1 KiB DMA blocks");
   static_assert(NI >= 1 && BYTES % (NT * 16) == 0, "MN-major DMA geometry");
+  static_assert(ROWB >= 256 && KROWS_PER_I % 8 == 0, "swizzle geometry");
   const bf16* tile;
   int mn0;
-  uint32_t voff0, istep;
+  uint32_t voff[NV], istep;  // round v's offset; bytes per NV rounds of k-rows
 
   __device__ __forceinline__ void init(const Opnd<bf16>& op, int mn0_, int tid) {
     mn0 = mn0_;
-    const int krow = (tid * 16) / ROWB;
-    const int pchunk = ((tid * 16) % ROWB) / 16;
-    const int c = pchunk ^ (4 * (krow & 3));
     tile = op.p + mn0;
-    voff0 = static_cast<uint32_t>((krow * op.ld + c * 8) * 2);
-    istep = static_cast<uint32_t>(KROWS_PER_I * op.ld * 2);
+#pragma unroll
+    for (int v = 0; v < NV; ++v) {
+      const int byte = (v * NT + tid) * 16;  // position in the stage of round v
+      const int krow = byte / ROWB;
+      const int c = ((byte % ROWB) / 16) ^ mn_swz(krow);
+      voff[v] = static_cast<uint32_t>((krow * op.ld + c * 8) * 2);
+    }
+    istep = static_cast<uint32_t>(NV * KROWS_PER_I * op.ld * 2);
   }
   __device__ __forceinline__ void load(char* stage, int wave, const Opnd<bf16>& op, int k0,
-                                       bool live) const {
+                                       bool live, bool /*kfull*/) const {
     // rows k >= k_ext lie past the record count and read as zero
     const __amdgpu_buffer_rsrc_t rs =
         make_rsrc(tile + static_cast<int64_t>(k0) * op.ld,
@@ -505,45 +560,50 @@ struct DmaOperand<ROWS, false, NT_> {
 #pragma unroll
     for (int i = 0; i < NI; ++i)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          rs, (lds_ptr_t)(stage + i * NT * 16 + wave * 1024), 16, voff0 + i * istep, 0, 0, 0);
+          rs, (lds_ptr_t)(stage + i * NT * 16 + wave * 1024), 16,
+          voff[i % NV] + (i / NV) * istep, 0, 0, 0);
   }
 };
 
-// Per-lane fragment addressing of one operand (relative to the stage base).
+// Per-lane fragment addressing of one operand (relative to the stage base):
+// fragment f covers rows wave_base + 16 f .. +15 and the whole K tile.
 template <int ROWS, bool KMAJOR, int NF>
 struct FragAddr;
 
 template <int ROWS, int NF>
 struct FragAddr<ROWS, true, NF> {
-  int off[2];  // byte offset of fragment 0 for sub-steps 0 and 1
+  int off;  // byte offset of fragment 0
   __device__ __forceinline__ void init(int wave_base, int lane) {
-    const int r = wave_base + (lane & 31);
-    const int x = (lane >> 5) ^ ((r >> 2) & 3);
-    off[0] = r * 64 + 16 * x;
-    off[1] = r * 64 + 16 * (x ^ 2);
+    const int r = wave_base + (lane & 15);
+    const int x = (lane >> 4) ^ km_swz(r);
+    off = r * 64 + 16 * x;
   }
-  __device__ __forceinline__ bf16x8 read(const char* stage, int f, int k16) const {
-    return *reinterpret_cast<const bf16x8*>(stage + off[k16] + f * 32 * 64);
+  __device__ __forceinline__ bf16x8 read(const char* stage, int f) const {
+    // 16 f rows further down keep the same km_swz
+    return *reinterpret_cast<const bf16x8*>(stage + off + f * 16 * 64);
   }
 };
 
 template <int ROWS, int NF>
 struct FragAddr<ROWS, false, NF> {
   static constexpr int ROWB = ROWS * 2;
-  int off[NF];  // byte offset for fragments f = 0..NF-1 (sub-step 0, half 0)
+  static_assert((NF & (NF - 1)) == 0 && NF <= 8, "power-of-two fragment count");
+  int off0;  // byte offset of the first transpose read of fragment 0
   __device__ __forceinline__ void init(int wave_base, int lane) {
-    const int gq = lane >> 4, a = lane & 15;
-    const int kr0 = 8 * (gq >> 1) + (a >> 2);
-    const int g = 4 * (a >> 2);  // swizzle of row kr0 + 4h + 16 k16 (all = kr0 mod 4)
-    const int mnoff = 16 * (gq & 1) + 4 * (a & 3);
-#pragma unroll
-    for (int f = 0; f < NF; ++f) {
-      const int mn = wave_base + 32 * f + mnoff;
-      off[f] = kr0 * ROWB + 16 * ((mn >> 3) ^ g) + (mn & 7) * 2;
-    }
+    const int a = lane & 15;
+    const int krow = 8 * (lane >> 4) + (a >> 2);  // the second read is 4 k-rows on,
+    const int sw = mn_swz(krow);                  // with the same swizzle
+    const int mn = wave_base + 4 * (a & 3);
+    off0 = krow * ROWB + 16 * ((mn >> 3) ^ sw) + (mn & 7) * 2;
   }
-  __device__ __forceinline__ bf16x8 read(const char* stage, int f, int k16) const {
-    const char* p = stage + off[f] + k16 * 16 * ROWB;
+  // Fragment f sits 16 f columns on: with wave_base a multiple of 16 NF the
+  // chunk index gains 2 f without carries, and the swizzle (bits 1..3 of the
+  // chunk index) commutes with that, so its offset is off0 ^ 32 f.
+  __device__ __forceinline__ bf16x8 read(const char* stage, int f) const {
+    // one v_xor per read (volatile: not hoisted into a register per fragment)
+    int o = off0;
+    if (f != 0) asm volatile("v_xor_b32 %0, %1, %2" : "=v"(o) : "i"(32 * f), "v"(off0));
+    const char* p = stage + o;
     const shortx4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) shortx4*)(p));
     const shortx4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
         (__attribute__((address_space(3))) shortx4*)(p + 4 * ROWB));
@@ -574,10 +634,19 @@ __device__ __forceinline__ void barrier_after_vmcnt() {
 }
 
 // The per-wave machinery of the DMA pipeline for one BM x BN tile shape:
-// operand DMA, fragment reads, MFMAs and the pinned interleaving of one
-// 32-deep K step.  Any wave layout C::WAVES_M x C::WAVES_N whose wave tile is
-// a multiple of 32 x 32; 256 or 512 threads.
-template <class C, bool A_KMAJOR, bool B_KMAJOR>
+// operand DMA, fragment reads, MFMAs and their order within one 32-deep K
+// tile.  Any wave layout C::WAVES_M x C::WAVES_N whose wave tile is a
+// multiple of 16 x 16; 256 or 512 threads.
+//
+// Fragment registers: the operand with more fragments per wave ("rolling",
+// NRL of them) has ONE register set; the other ("double", NDB) has two.  The
+// MFMAs of a K tile run as NRL rows of NDB (row r uses rolling fragment r),
+// and rolling fragment r of the next K tile is read into its register as
+// soon as row r has issued, so the reads of the next tile overlap the
+// current tile's MFMAs without a second rolling set.  Scheduling barriers
+// between rows keep every read after the last use of the register it
+// overwrites.
+template <class C, bool A_KMAJOR, bool B_KMAJOR, bool KFULL>
 struct DmaEngine {
   static constexpr int S = 4, BK = 32;
   static constexpr int B_OFF = C::BM * BK * 2;
@@ -585,19 +654,17 @@ struct DmaEngine {
   typedef DmaOperand<C::BM, A_KMAJOR, C::NT> DA;
   typedef DmaOperand<C::BN, B_KMAJOR, C::NT> DB;
   static constexpr int NL = DA::NI + DB::NI;  // DMA instructions per thread per K tile
-  // LDS read instructions per fragment set: one b128 per K-major fragment,
-  // two b64 transpose reads per MN-major fragment
-  static constexpr int NR = FM * (A_KMAJOR ? 1 : 2) + FN * (B_KMAJOR ? 1 : 2);
-  static constexpr int NMMA = FM * FN;         // MFMAs per 16-deep sub-step
-  static constexpr int NG = NMMA / 2;          // interleave groups (first half of the MFMAs)
-  static constexpr int RG = (NR + NG - 1) / NG, LG = (NL + NG - 1) / NG;
+  static constexpr bool ROLL_A = FM >= FN;
+  static constexpr int NRL = ROLL_A ? FM : FN;  // rolling fragments = MFMA rows
+  static constexpr int NDB = ROLL_A ? FN : FM;  // double-buffered fragments = MFMAs per row
+  static_assert(C::MB == 16 && C::NB == 16 && NRL >= 2, "16x16 blocks, two rows at least");
   static_assert(C::BM * BK * 2 + C::BN * BK * 2 <= 32768, "one K tile per 32 KiB stage");
 
   DA da;
   DB db;
   FragAddr<C::BM, A_KMAJOR, FM> fa_addr;
   FragAddr<C::BN, B_KMAJOR, FN> fb_addr;
-  bf16x8 fa[2][FM], fb[2][FN];
+  bf16x8 fr[NRL], fd[2][NDB];
   int wave;
 
   __device__ __forceinline__ void init(const Opnd<bf16>& A, const Opnd<bf16>& B, int m0, int n0,
@@ -610,49 +677,68 @@ struct DmaEngine {
     fa_addr.init(wm * C::WTM, lane);
     fb_addr.init(wn * C::WTN, lane);
   }
-  __device__ __forceinline__ void read(int set, const char* stage, int k16) {
+  __device__ __forceinline__ bf16x8 read_a(const char* stage, int f) const {
+    return fa_addr.read(stage, f);
+  }
+  __device__ __forceinline__ bf16x8 read_b(const char* stage, int f) const {
+    return fb_addr.read(stage + B_OFF, f);
+  }
+  __device__ __forceinline__ void read_roll(const char* stage, int r) {
+    fr[r] = ROLL_A ? read_a(stage, r) : read_b(stage, r);
+  }
+  __device__ __forceinline__ void read_dbl(int set, const char* stage, int d) {
+    fd[set][d] = ROLL_A ? read_b(stage, d) : read_a(stage, d);
+  }
+  // Every fragment of the K tile in `stage` (double ones into set `set`).
+  __device__ __forceinline__ void read_all(int set, const char* stage) {
 #pragma unroll
-    for (int f = 0; f < (FM > FN ? FM : FN); ++f) {
-      if (f < FM) fa[set][f] = fa_addr.read(stage, f, k16);
-      if (f < FN) fb[set][f] = fb_addr.read(stage + B_OFF, f, k16);
+    for (int r = 0; r < NRL; ++r) read_roll(stage, r);
+#pragma unroll
+    for (int d = 0; d < NDB; ++d) read_dbl(set, stage, d);
+  }
+  __device__ __forceinline__ void mma_row(Acc<C>& acc, int set, int r) {
+#pragma unroll
+    for (int d = 0; d < NDB; ++d) {
+      const int fm = ROLL_A ? r : d, fn = ROLL_A ? d : r;
+      const bf16x8& a = ROLL_A ? fr[r] : fd[set][d];
+      const bf16x8& b = ROLL_A ? fd[set][d] : fr[r];
+      acc.v[fm][fn] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, acc.v[fm][fn], 0, 0, 0);
     }
   }
-  __device__ __forceinline__ void mma(Acc<C>& acc, int set) {
-#pragma unroll
-    for (int fm = 0; fm < FM; ++fm)
-#pragma unroll
-      for (int fn = 0; fn < FN; ++fn)
-        acc.v[fm][fn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[set][fm], fb[set][fn],
-                                                                acc.v[fm][fn], 0, 0, 0);
+  // The barrier that publishes the next K tile comes after the first HALF
+  // rows, so the LDS reads it waits for (lgkmcnt(0)) have half a tile of
+  // MFMAs to land.
+  static constexpr int HALF = NRL / 2;
+  // Row of the MFMA order before which double fragment d of the next tile is
+  // read (rows HALF .. NRL-1, spread evenly).
+  __device__ __forceinline__ static constexpr int dbl_row(int d) {
+    return HALF + (d * (NRL - HALF)) / NDB;
   }
-  // Pin the order: the reads of the next fragment set (and the DMA issue)
-  // go between the first half of the current set's MFMAs, so both fragment
-  // sets stay live and no MFMA waits on an LDS round trip.
-  __device__ __forceinline__ static void pin(bool with_dma) {
-#pragma unroll
-    for (int g = 0; g < NG; ++g) {
-      __builtin_amdgcn_sched_group_barrier(kSchedMFMA, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(kSchedDSRead, RG, 0);
-      if (with_dma) __builtin_amdgcn_sched_group_barrier(kSchedVMEMRead, LG, 0);
-    }
-    __builtin_amdgcn_sched_group_barrier(kSchedMFMA, NMMA - NG, 0);
-    __builtin_amdgcn_sched_barrier(0);
-  }
-  // One K tile in stage `cur`: prefetch (issue_next) into the stage of the
-  // previous tile (free since the previous barrier), read sub-step 1, MFMA
-  // sub-step 0, publish the next tile (wait for this thread's DMA of it,
-  // barrier), read its sub-step 0, MFMA sub-step 1.
-  template <class Issue>
-  __device__ __forceinline__ void step(Acc<C>& acc, const char* cur, const char* nxt,
-                                       Issue&& issue_next) {
+  // One K tile whose fragments are already in registers (double set SET):
+  // prefetch (issue_next) into the stage of the previous tile (free since the
+  // previous barrier), rows 0 .. HALF-1, publish the next tile (wait for this
+  // thread's DMA of it, barrier), read its rolling fragments 0 .. HALF-1
+  // (their rows are done), then rows HALF .. NRL-1, each preceded by the
+  // read of the rolling fragment the previous row freed.
+  template <int SET, class Issue>
+  __device__ __forceinline__ void step(Acc<C>& acc, const char* nxt, Issue&& issue_next) {
     issue_next();
-    read(1, cur, 1);
-    mma(acc, 0);
-    pin(true);
+#pragma unroll
+    for (int r = 0; r < HALF; ++r) mma_row(acc, SET, r);
+    __builtin_amdgcn_sched_barrier(0);
     barrier_after_vmcnt<NL * (S - 2)>();
-    read(0, nxt, 0);
-    mma(acc, 1);
-    pin(false);
+#pragma unroll
+    for (int r = 0; r < HALF; ++r) read_roll(nxt, r);
+#pragma unroll
+    for (int r = HALF; r < NRL; ++r) {
+      if (r > HALF) read_roll(nxt, r - 1);
+#pragma unroll
+      for (int d = 0; d < NDB; ++d)
+        if (dbl_row(d) == r) read_dbl(SET ^ 1, nxt, d);
+      mma_row(acc, SET, r);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    read_roll(nxt, NRL - 1);
   }
 };
 
@@ -663,20 +749,20 @@ __device__ __forceinline__ void zero_acc(Acc<C>& acc) {
 #pragma unroll
     for (int fn = 0; fn < C::FN; ++fn)
 #pragma unroll
-      for (int i = 0; i < 16; ++i) acc.v[fm][fn][i] = 0.0f;
+      for (int i = 0; i < C::NV; ++i) acc.v[fm][fn][i] = 0.0f;
 }
 
 // One BM x BN bf16 output tile, operands in any layout, through the 4-stage
 // DMA pipeline.  The K loop is unrolled by the stage count so every stage
-// reference is static.  When the tile count is not a multiple of four the
-// last trip runs on tiles past the end, whose stages hold the zeros of
-// out-of-range loads: their MFMAs add exact zeros.  Ends with all DMA
-// drained and a barrier, so the stages may be reused after it.
-template <class C, bool A_KMAJOR, bool B_KMAJOR>
+// reference and fragment set is static.  When the tile count is not a
+// multiple of four the last trip runs on tiles past the end, whose stages
+// hold the zeros of out-of-range loads: their MFMAs add exact zeros.  Ends
+// with all DMA drained and a barrier, so the stages may be reused after it.
+template <class C, bool A_KMAJOR, bool B_KMAJOR, bool KFULL>
 __device__ __forceinline__ void gemm_tile_dma(Acc<C>& acc, const Opnd<bf16>& A,
                                               const Opnd<bf16>& B, int m0, int n0, int K,
                                               const DmaStages& st, int tid) {
-  typedef DmaEngine<C, A_KMAJOR, B_KMAJOR> E;
+  typedef DmaEngine<C, A_KMAJOR, B_KMAJOR, KFULL> E;
   constexpr int S = E::S, BK = E::BK;
   zero_acc(acc);
   const int nk = (K + BK - 1) / BK;
@@ -685,19 +771,19 @@ __device__ __forceinline__ void gemm_tile_dma(Acc<C>& acc, const Opnd<bf16>& A,
   e.init(A, B, m0, n0, tid);
   auto issue = [&](char* stage, int kt) {
     const bool live = kt < nk;
-    e.da.load(stage, e.wave, A, kt * BK, live);
-    e.db.load(stage + E::B_OFF, e.wave, B, kt * BK, live);
+    e.da.load(stage, e.wave, A, kt * BK, live, KFULL);
+    e.db.load(stage + E::B_OFF, e.wave, B, kt * BK, live, KFULL);
   };
   issue(st.s[0], 0);
   issue(st.s[1], 1);
   issue(st.s[2], 2);
   barrier_after_vmcnt<E::NL * (S - 2)>();
-  e.read(0, st.s[0], 0);
+  e.read_all(0, st.s[0]);
   for (int kt = 0; kt < nk; kt += S) {
-    e.step(acc, st.s[0], st.s[1], [&] { issue(st.s[3], kt + 3); });
-    e.step(acc, st.s[1], st.s[2], [&] { issue(st.s[0], kt + 4); });
-    e.step(acc, st.s[2], st.s[3], [&] { issue(st.s[1], kt + 5); });
-    e.step(acc, st.s[3], st.s[0], [&] { issue(st.s[2], kt + 6); });
+    e.template step<0>(acc, st.s[1], [&] { issue(st.s[3], kt + 3); });
+    e.template step<1>(acc, st.s[2], [&] { issue(st.s[0], kt + 4); });
+    e.template step<0>(acc, st.s[3], [&] { issue(st.s[1], kt + 5); });
+    e.template step<1>(acc, st.s[0], [&] { issue(st.s[2], kt + 6); });
   }
   // the prefetches past the last tile still write (zeros) into LDS: drain them
   barrier_after_vmcnt<0>();
@@ -715,36 +801,37 @@ template <class C, class Epi>
 __device__ __forceinline__ void gemm_stream_dma(const Opnd<bf16>& A, const Opnd<bf16>& B,
                                                 int mt_begin, int mt_end, int n0, int K,
                                                 const DmaStages& st, int tid, Epi&& epi) {
-  typedef DmaEngine<C, true, true> E;
+  typedef DmaEngine<C, true, true, true> E;
   constexpr int S = E::S, BK = E::BK;
   const int nk = K / BK;
-  const int total = (mt_end - mt_begin) * nk;
   Acc<C> acc;
   zero_acc(acc);
-  if (total <= 0) return;
+  if (mt_end <= mt_begin || nk <= 0) return;
   E e;
   e.init(A, B, mt_begin * C::BM, n0, tid);
-  // stream position g = (M tile index) * nk + (K tile index)
-  auto issue = [&](char* stage, int g) {
-    const bool live = g < total;
-    const int gg = live ? g : 0;
-    const int k0 = (gg % nk) * BK;
-    e.da.load_at(stage, e.wave, A, (mt_begin + gg / nk) * C::BM, k0, live);
-    e.db.load(stage + E::B_OFF, e.wave, B, k0, live);
+  // K tile kt of M tile mt; kt < nk + 3 (past the end it wraps into the next
+  // M tile, past the last M tile the load is dead)
+  auto issue = [&](char* stage, int mt, int kt) {
+    int m = mt, k = kt;
+    if (k >= nk) {
+      k -= nk;
+      ++m;
+    }
+    const bool live = m < mt_end;
+    e.da.load_at(stage, e.wave, A, (live ? m : mt_begin) * C::BM, k * BK, live, true);
+    e.db.load(stage + E::B_OFF, e.wave, B, k * BK, live, true);
   };
-  issue(st.s[0], 0);
-  issue(st.s[1], 1);
-  issue(st.s[2], 2);
+  issue(st.s[0], mt_begin, 0);
+  issue(st.s[1], mt_begin, 1);
+  issue(st.s[2], mt_begin, 2);
   barrier_after_vmcnt<E::NL * (S - 2)>();
-  e.read(0, st.s[0], 0);
+  e.read_all(0, st.s[0]);
   for (int mt = mt_begin; mt < mt_end; ++mt) {
-    const int base = (mt - mt_begin) * nk;
     for (int kt = 0; kt < nk; kt += S) {
-      const int g = base + kt;
-      e.step(acc, st.s[0], st.s[1], [&] { issue(st.s[3], g + 3); });
-      e.step(acc, st.s[1], st.s[2], [&] { issue(st.s[0], g + 4); });
-      e.step(acc, st.s[2], st.s[3], [&] { issue(st.s[1], g + 5); });
-      e.step(acc, st.s[3], st.s[0], [&] { issue(st.s[2], g + 6); });
+      e.template step<0>(acc, st.s[1], [&] { issue(st.s[3], mt, kt + 3); });
+      e.template step<1>(acc, st.s[2], [&] { issue(st.s[0], mt, kt + 4); });
+      e.template step<0>(acc, st.s[3], [&] { issue(st.s[1], mt, kt + 5); });
+      e.template step<1>(acc, st.s[0], [&] { issue(st.s[2], mt, kt + 6); });
     }
     epi(acc, mt * C::BM);
     zero_acc(acc);
@@ -755,12 +842,12 @@ __device__ __forceinline__ void gemm_stream_dma(const Opnd<bf16>& A, const Opnd<
 // bf16 tiles take the DMA pipeline over the four stages, fp32 tiles the
 // register-staged one over stage 0 (which is large enough for both of its
 // LDS buffers).
-template <class C, bool A_KMAJOR, bool B_KMAJOR>
+template <class C, bool A_KMAJOR, bool B_KMAJOR, bool KFULL = false>
 __device__ __forceinline__ void gemm_any(Acc<C>& acc, const Opnd<typename C::Elem>& A,
                                          const Opnd<typename C::Elem>& B, int m0, int n0, int K,
                                          const DmaStages& st, int tid) {
   if constexpr (sizeof(typename C::Elem) == 2) {
-    gemm_tile_dma<C, A_KMAJOR, B_KMAJOR>(acc, A, B, m0, n0, K, st, tid);
+    gemm_tile_dma<C, A_KMAJOR, B_KMAJOR, KFULL>(acc, A, B, m0, n0, K, st, tid);
   } else {
     typedef typename C::Elem T;
     static_assert(C::STAGE * sizeof(T) <= 32768, "an fp32 stage fits one DMA stage");

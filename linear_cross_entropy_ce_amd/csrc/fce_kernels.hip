@@ -116,11 +116,12 @@ __global__ __launch_bounds__(C::NT) void k_fwd_lse(FwdArgs<typename C::Elem> a) 
   const Opnd<T> A{a.W, a.H, a.V, a.H};  // rows: vocabulary
   const Opnd<T> B{a.X, a.H, a.N, a.H};  // rows: tokens
 
+  typedef AccMap<C> Map;
   int yv[C::FN];
   float rm[C::FN], rl[C::FN], rt[C::FN], rz[C::FN];
 #pragma unroll
   for (int fn = 0; fn < C::FN; ++fn) {
-    const int tok = n0 + wn * C::WTN + fn * 32 + (lane & 31);
+    const int tok = n0 + wn * C::WTN + fn * C::NB + Map::col(lane);
     const int y = tok < a.N ? a.labels[tok] : a.ignore;
     yv[fn] = label_ok(y, a.ignore, a.V) ? y : -1;
     rm[fn] = -INFINITY;
@@ -130,7 +131,7 @@ __global__ __launch_bounds__(C::NT) void k_fwd_lse(FwdArgs<typename C::Elem> a) 
   // Running (max, sum-exp, target logit, logit sum) update of one logit tile
   // whose rows are the vocabulary entries m0 .. m0+BM-1.
   auto lse_update = [&](const Acc<C>& acc, int m0) {
-    const int vbase = m0 + wm * C::WTM + 4 * (lane >> 5);
+    const int vbase = m0 + wm * C::WTM;
     const bool full = m0 + C::BM <= a.V;
 #pragma unroll
     for (int fn = 0; fn < C::FN; ++fn) {
@@ -138,8 +139,8 @@ __global__ __launch_bounds__(C::NT) void k_fwd_lse(FwdArgs<typename C::Elem> a) 
 #pragma unroll
       for (int fm = 0; fm < C::FM; ++fm)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int v = vbase + fm * 32 + 8 * (i >> 2) + (i & 3);
+        for (int i = 0; i < C::NV; ++i) {
+          const int v = vbase + fm * C::MB + Map::row(lane, i >> 2) + (i & 3);
           if (full || v < a.V) tmax = fmaxf(tmax, acc.v[fm][fn][i]);
         }
       const float mnew = fmaxf(rm[fn], tmax);
@@ -148,8 +149,8 @@ __global__ __launch_bounds__(C::NT) void k_fwd_lse(FwdArgs<typename C::Elem> a) 
 #pragma unroll
       for (int fm = 0; fm < C::FM; ++fm)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int v = vbase + fm * 32 + 8 * (i >> 2) + (i & 3);
+        for (int i = 0; i < C::NV; ++i) {
+          const int v = vbase + fm * C::MB + Map::row(lane, i >> 2) + (i & 3);
           const float z = acc.v[fm][fn][i];
           const bool ok = full || v < a.V;
           s += ok ? hw_exp2((z - mnew) * kLog2e) : 0.0f;
@@ -160,6 +161,9 @@ __global__ __launch_bounds__(C::NT) void k_fwd_lse(FwdArgs<typename C::Elem> a) 
       rm[fn] = mnew;
       rt[fn] += tg;
       rz[fn] += zs;
+      // one token column at a time: keeps the accumulator copies it needs,
+      // not the whole tile's, in vector registers
+      __builtin_amdgcn_sched_barrier(0);
     }
   };
   if (sizeof(T) == 2 && a.H % 128 == 0) {
@@ -175,30 +179,35 @@ __global__ __launch_bounds__(C::NT) void k_fwd_lse(FwdArgs<typename C::Elem> a) 
     }
   }
 
-  // lanes l and l+32 hold the two halves of every 32-row block: merge them
+  // the 64 / NB lanes that share a column (l, l ^ NB, ...) hold disjoint rows
+  // of it: merge them pairwise (the merge is symmetric, so both lanes of a
+  // pair end with the same bits)
 #pragma unroll
-  for (int fn = 0; fn < C::FN; ++fn) {
-    const float m2 = __shfl_xor(rm[fn], 32);
-    const float l2 = __shfl_xor(rl[fn], 32);
-    const float t2 = __shfl_xor(rt[fn], 32);
-    const float z2 = __shfl_xor(rz[fn], 32);
-    lse_merge(rm[fn], rl[fn], rt[fn], rz[fn], m2, l2, t2, z2);
+  for (int sh = C::NB; sh < 64; sh <<= 1) {
+#pragma unroll
+    for (int fn = 0; fn < C::FN; ++fn) {
+      const float m2 = __shfl_xor(rm[fn], sh);
+      const float l2 = __shfl_xor(rl[fn], sh);
+      const float t2 = __shfl_xor(rt[fn], sh);
+      const float z2 = __shfl_xor(rz[fn], sh);
+      lse_merge(rm[fn], rl[fn], rt[fn], rz[fn], m2, l2, t2, z2);
+    }
   }
   // then the WAVES_M waves that share these token columns, in fixed order
   static_assert(C::WAVES_M * C::BN * sizeof(floatx4) <= 32768, "reduction fits one stage");
   floatx4* red = reinterpret_cast<floatx4*>(lds.s[0]);  // [WAVES_M][BN]; free after gemm_any
-  if (lane < 32) {
+  if (lane < C::NB) {
 #pragma unroll
     for (int fn = 0; fn < C::FN; ++fn) {
       floatx4 st = {rm[fn], rl[fn], rt[fn], rz[fn]};
-      red[wm * C::BN + wn * C::WTN + fn * 32 + lane] = st;
+      red[wm * C::BN + wn * C::WTN + fn * C::NB + lane] = st;
     }
   }
   __syncthreads();
-  if (wm == 0 && lane < 32) {
+  if (wm == 0 && lane < C::NB) {
 #pragma unroll
     for (int fn = 0; fn < C::FN; ++fn) {
-      const int col = wn * C::WTN + fn * 32 + lane;
+      const int col = wn * C::WTN + fn * C::NB + lane;
       floatx4 st = red[col];
       for (int w = 1; w < C::WAVES_M; ++w) {
         const floatx4 o = red[w * C::BN + col];
@@ -288,7 +297,7 @@ __device__ __forceinline__ void store4(bf16* p, float a, float b, float c, float
   *reinterpret_cast<bf16x4*>(p) = v;
 }
 
-template <class C>
+template <class C, bool KFULL>
 __global__ __launch_bounds__(C::NT) void k_bwd_dz(DzArgs<typename C::Elem> a) {
   typedef typename C::Elem T;
   if (*a.flag == 0) return;  // every label of this token block is ignored
@@ -302,13 +311,14 @@ __global__ __launch_bounds__(C::NT) void k_bwd_dz(DzArgs<typename C::Elem> a) {
   const Opnd<T> A{a.W, a.H, a.nvoc, a.H};
   const Opnd<T> B{a.X, a.H, a.ntok, a.H};
   Acc<C> acc;
-  gemm_any<C, true, true>(acc, A, B, m0, n0, a.H, lds, tid);
+  gemm_any<C, true, true, KFULL>(acc, A, B, m0, n0, a.H, lds, tid);
 
+  typedef AccMap<C> Map;
   const float eps_v = a.eps / static_cast<float>(a.V);
   const float one_m_eps = 1.0f - a.eps;
 #pragma unroll
   for (int fn = 0; fn < C::FN; ++fn) {
-    const int tl = n0 + wn * C::WTN + fn * 32 + (lane & 31);
+    const int tl = n0 + wn * C::WTN + fn * C::NB + Map::col(lane);
     const int y = tl < a.ntok ? a.labels[tl] : a.ignore;
     const bool valid = tl < a.ntok && label_ok(y, a.ignore, a.V);
     const float L = valid ? a.lse[tl] : 0.0f;
@@ -317,8 +327,8 @@ __global__ __launch_bounds__(C::NT) void k_bwd_dz(DzArgs<typename C::Elem> a) {
 #pragma unroll
     for (int fm = 0; fm < C::FM; ++fm) {
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int v0 = m0 + wm * C::WTM + fm * 32 + 8 * g + 4 * (lane >> 5);
+      for (int g = 0; g < Map::NGRP; ++g) {
+        const int v0 = m0 + wm * C::WTM + fm * C::MB + Map::row(lane, g);
         float d[4];
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
@@ -363,45 +373,52 @@ __global__ __launch_bounds__(C::NT) void k_bwd_grad(GradArgs<typename C::Elem> a
   if (skip && a.accumulate) return;
   Acc<C> acc;
   if (skip) {
-#pragma unroll
-    for (int fm = 0; fm < C::FM; ++fm)
-#pragma unroll
-      for (int fn = 0; fn < C::FN; ++fn)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) acc.v[fm][fn][i] = 0.0f;
+    zero_acc(acc);
   } else {
-    gemm_any<C, A_KMAJOR, false>(acc, a.A, a.B, m0, n0, a.K, lds, tid);
+    // K is the token count (dW, no K-major operand) or the block's vocabulary
+    // coverage, a whole number of tiles (dX)
+    gemm_any<C, A_KMAJOR, false, true>(acc, a.A, a.B, m0, n0, a.K, lds, tid);
   }
+  typedef AccMap<C> Map;
   const float s = a.ctrl->scale_bwd;
-  // Output element (fm, fn, i) of this lane: row m0 + rbase + 32 fm + 8 (i/4) + (i%4),
-  // column n0 + cbase + 32 fn.  Per 32-row slab fm, all loads of the old values
-  // are issued before any use, so their latencies overlap.
-  const int rbase = wm * C::WTM + 4 * (lane >> 5);
-  const int cbase = wn * C::WTN + (lane & 31);
+  // Output element (fm, fn, i) of this lane: row m0 + wm WTM + fm MB +
+  // row(lane, i/4) + i%4, column n0 + wn WTN + fn NB + col(lane).  Per slab of
+  // SLAB block rows, all loads of the old values are issued before any use,
+  // so their latencies overlap.
+  constexpr int SLAB = (C::MB >= 32) ? 1 : 32 / C::MB;
+  static_assert(C::FM % SLAB == 0, "slabs of block rows");
+  const int rbase = wm * C::WTM;
+  const int cbase = wn * C::WTN + Map::col(lane);
   const bool full = m0 + C::BM <= a.m_valid && n0 + C::BN <= a.n_valid;
   float* tile = a.out + static_cast<int64_t>(m0) * a.ldo + n0;
 #pragma unroll
-  for (int fm = 0; fm < C::FM; ++fm) {
-    float old[C::FN][16];
-    bool ok[C::FN][16];
+  for (int f0 = 0; f0 < C::FM; f0 += SLAB) {
+    float old[SLAB][C::FN][C::NV];
+    bool ok[SLAB][C::FN][C::NV];
 #pragma unroll
-    for (int fn = 0; fn < C::FN; ++fn)
+    for (int j = 0; j < SLAB; ++j)
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int r = rbase + fm * 32 + 8 * (i >> 2) + (i & 3);
-        const int c = cbase + fn * 32;
-        ok[fn][i] = full || (m0 + r < a.m_valid && n0 + c < a.n_valid);
-        old[fn][i] = 0.0f;
-        if (a.accumulate && ok[fn][i]) old[fn][i] = tile[static_cast<int64_t>(r) * a.ldo + c];
-      }
+      for (int fn = 0; fn < C::FN; ++fn)
 #pragma unroll
-    for (int fn = 0; fn < C::FN; ++fn)
+        for (int i = 0; i < C::NV; ++i) {
+          const int r = rbase + (f0 + j) * C::MB + Map::row(lane, i >> 2) + (i & 3);
+          const int c = cbase + fn * C::NB;
+          ok[j][fn][i] = full || (m0 + r < a.m_valid && n0 + c < a.n_valid);
+          old[j][fn][i] = 0.0f;
+          if (a.accumulate && ok[j][fn][i])
+            old[j][fn][i] = tile[static_cast<int64_t>(r) * a.ldo + c];
+        }
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int r = rbase + fm * 32 + 8 * (i >> 2) + (i & 3);
-        const int c = cbase + fn * 32;
-        if (ok[fn][i]) tile[static_cast<int64_t>(r) * a.ldo + c] = old[fn][i] + s * acc.v[fm][fn][i];
-      }
+    for (int j = 0; j < SLAB; ++j)
+#pragma unroll
+      for (int fn = 0; fn < C::FN; ++fn)
+#pragma unroll
+        for (int i = 0; i < C::NV; ++i) {
+          const int r = rbase + (f0 + j) * C::MB + Map::row(lane, i >> 2) + (i & 3);
+          const int c = cbase + fn * C::NB;
+          if (ok[j][fn][i])
+            tile[static_cast<int64_t>(r) * a.ldo + c] = old[j][fn][i] + s * acc.v[f0 + j][fn][i];
+        }
   }
 }
 
@@ -495,7 +512,10 @@ hipError_t run_backward(const Plan& p, const T* X, const T* W, const int32_t* la
                    static_cast<int>(voc0), static_cast<int>(H), static_cast<int>(V), ignore, eps,
                    voc_tiles, tok_tiles, 4, dz, p.ldz, flags + ia};
       timer->begin("bwd_dz", blk_flops, st);
-      k_bwd_dz<C><<<voc_tiles * tok_tiles, C::NT, 0, st>>>(da);
+      if (H % 32 == 0)
+        k_bwd_dz<C, true><<<voc_tiles * tok_tiles, C::NT, 0, st>>>(da);
+      else
+        k_bwd_dz<C, false><<<voc_tiles * tok_tiles, C::NT, 0, st>>>(da);
       FCE_CHECK_LAUNCH();
       timer->end(st);
 

@@ -17,8 +17,8 @@ struct TileShape {
   static constexpr int NT = 64 * WAVES_M_ * WAVES_N_;
 };
 
-// bf16: 256 x 256 output tiles, 8 waves (two per SIMD) of 64 x 128 (8 MFMA 32x32 blocks each).
-using ShapeBf16 = TileShape<256, 256, 64, 4, 2>;
+// bf16: 256 x 256 output tiles, 8 waves (two per SIMD) of 128 x 64 (32 MFMA 16x16 blocks each).
+using ShapeBf16 = TileShape<256, 256, 64, 2, 4>;
 // fp32: 128 x 128 output tiles, 4 waves of 64 x 64.
 using ShapeF32 = TileShape<128, 128, 32, 2, 2>;
 
