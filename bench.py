@@ -125,6 +125,45 @@ def naive_torch(torch, X, W, y, eps, steps):
             "peak_bytes_above_inputs": int(peak)}
 
 
+def run_side(torch, fce, wk, args, side, X, W, y, loss, lse, dX, dW, ws, step, stream, ms):
+    """Measurements outside the headline figure: the forward and backward entry
+    points alone, the step at other chunk sizes and with the token-chunk
+    schedule, and the naive torch step (context)."""
+    N, H = X.shape
+    V = W.shape[0]
+    chunk, sched, eps = args.chunk, args.schedule, wk.WORKLOADS[args.workload].label_smoothing
+    k2 = args.side_steps
+    fwd = lambda: fce.fce_forward(X, W, y, loss, lse, ws, wk.IGNORE_INDEX, eps, "mean", chunk, sched)
+    bwd = lambda: fce.fce_backward(X, W, y, lse, None, dX, dW, ws, wk.IGNORE_INDEX, eps, "mean",
+                                   chunk, sched)
+    fwd()
+    bwd()
+    t_f, _ = time_steps(torch, fwd, k2, stream)
+    t_b, _ = time_steps(torch, bwd, k2, stream)
+    side["fce_forward"] = {"ms": round(t_f / k2, 4), "tflops_2NVH": round(2 * N * V * H / (t_f / k2 / 1e3) / 1e12, 1)}
+    side["fce_backward"] = {"ms": round(t_b / k2, 4), "tflops_6NVH": round(6 * N * V * H / (t_b / k2 / 1e3) / 1e12, 1)}
+    log(f"  forward alone {t_f / k2:.3f} ms, backward alone {t_b / k2:.3f} ms")
+    sweep = {str(chunk) + "/" + sched: round(ms, 4)}
+    variants = [(int(c), sched) for c in args.sweep_chunks.split(",") if c and int(c) != chunk]
+    if sched != "token":
+        variants.append((chunk, "token"))
+    for c, sc in variants:
+        ws_c = fce.workspace_for(N, H, V, X.dtype, c, sc)
+        fn = lambda: step(ws_c, c, sc)
+        fn()
+        t_c, _ = time_steps(torch, fn, k2, stream)
+        sweep[f"{c}/{sc}"] = round(t_c / k2, 4)
+        log(f"  chunk {c} schedule {sc}: {t_c / k2:.3f} ms/step")
+        del ws_c
+    side["ms_per_step_by_chunk_schedule"] = sweep
+    if not args.no_naive:
+        try:
+            side["naive_torch"] = naive_torch(torch, X, W, y, eps, min(k2, 5))
+            log(f"  naive torch: {side['naive_torch']}")
+        except torch.cuda.OutOfMemoryError as e:  # pragma: no cover
+            side["naive_torch"] = {"error": str(e)[:200]}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -138,6 +177,8 @@ def main():
     ap.add_argument("--sweep-chunks", default="256,512")
     ap.add_argument("--side-steps", type=int, default=10)
     ap.add_argument("--no-naive", action="store_true")
+    ap.add_argument("--no-side", action="store_true",
+                    help="only the headline step (no forward/backward alone, sweeps or naive run)")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -216,35 +257,10 @@ def main():
     # ---- outside the headline figure
     side = {}
     k2 = args.side_steps
-    fwd = lambda: fce.fce_forward(X, W, y, loss, lse, ws, wk.IGNORE_INDEX, eps, "mean", chunk, sched)
-    bwd = lambda: fce.fce_backward(X, W, y, lse, None, dX, dW, ws, wk.IGNORE_INDEX, eps, "mean",
-                                   chunk, sched)
-    fwd()
-    bwd()
-    t_f, _ = time_steps(torch, fwd, k2, stream)
-    t_b, _ = time_steps(torch, bwd, k2, stream)
-    side["fce_forward"] = {"ms": round(t_f / k2, 4), "tflops_2NVH": round(2 * N * V * H / (t_f / k2 / 1e3) / 1e12, 1)}
-    side["fce_backward"] = {"ms": round(t_b / k2, 4), "tflops_6NVH": round(6 * N * V * H / (t_b / k2 / 1e3) / 1e12, 1)}
-    log(f"  forward alone {t_f / k2:.3f} ms, backward alone {t_b / k2:.3f} ms")
-    sweep = {str(chunk) + "/" + sched: round(ms, 4)}
-    variants = [(int(c), sched) for c in args.sweep_chunks.split(",") if c and int(c) != chunk]
-    if sched != "token":
-        variants.append((chunk, "token"))
-    for c, sc in variants:
-        ws_c = fce.workspace_for(N, H, V, X.dtype, c, sc)
-        fn = lambda: step(ws_c, c, sc)
-        fn()
-        t_c, _ = time_steps(torch, fn, k2, stream)
-        sweep[f"{c}/{sc}"] = round(t_c / k2, 4)
-        log(f"  chunk {c} schedule {sc}: {t_c / k2:.3f} ms/step")
-        del ws_c
-    side["ms_per_step_by_chunk_schedule"] = sweep
-    if not args.no_naive:
-        try:
-            side["naive_torch"] = naive_torch(torch, X, W, y, eps, min(k2, 5))
-            log(f"  naive torch: {side['naive_torch']}")
-        except torch.cuda.OutOfMemoryError as e:  # pragma: no cover
-            side["naive_torch"] = {"error": str(e)[:200]}
+    if args.no_side or k2 < 1:
+        side = None
+    else:
+        run_side(torch, fce, wk, args, side, X, W, y, loss, lse, dX, dW, ws, step, stream, ms)
 
     mem = {"logit_scratch_bytes": plan["scratch_bytes"],
            "workspace_bytes": plan["workspace_bytes"],
