@@ -209,11 +209,150 @@ def check_row_block_invariance():
         assert np.allclose(r.dW, ref.dW, rtol=1e-13, atol=1e-16)
 
 
+# ------------------------------------------------- z-loss and reduction none
+def check_zloss_zero_weights():
+    # W = 0: LSE = log V in every row, so l_i = log V + alpha log^2 V
+    # ([LLMS] "Numerical Considerations" item 3: L_z = alpha log^2 sum exp z).
+    for V, eps, a in [(7, 0.0, 1e-2), (50, 0.1, 0.3), (1000, 0.3, 1e-4)]:
+        X, _, y = _case(9, 5, V, ignore=3, seed=V + 1)
+        W = np.zeros((V, 5))
+        want = math.log(V) + a * math.log(V) ** 2
+        r = orc.linear_cross_entropy(X, W, y, label_smoothing=eps, z_loss=a)
+        assert abs(r.loss - want) < 1e-12, (V, eps, a, r.loss, want)
+        r = orc.linear_cross_entropy(X, W, y, label_smoothing=eps, z_loss=a, reduction="none")
+        assert np.allclose(r.loss[y != -100], want, atol=1e-12) and np.all(r.loss[y == -100] == 0)
+
+
+def check_zloss_two_class_closed_form():
+    # N = H = 1, V = 2, x = 1, W = (a, b), label 0, no smoothing:
+    # l = softplus(b - a) + alpha s^2 with s = log(e^a + e^b); then
+    # dl/da = sigmoid(a - b) (1 + 2 alpha s) - 1 and dl/db = sigmoid(b - a) (1 + 2 alpha s).
+    def sigmoid(t):
+        return 1.0 / (1.0 + math.exp(-t))
+
+    for a, b, al in [(0.3, -1.2, 0.1), (2.0, 5.0, 0.01), (-1.0, 0.7, 1.0)]:
+        s = max(a, b) + math.log(math.exp(a - max(a, b)) + math.exp(b - max(a, b)))
+        want = s - a + al * s * s
+        r = orc.linear_cross_entropy(np.array([[1.0]]), np.array([[a], [b]]), np.array([0]),
+                                     z_loss=al)
+        assert abs(r.loss - want) < 1e-13, (a, b, al)
+        ga = sigmoid(a - b) * (1 + 2 * al * s) - 1
+        gb = sigmoid(b - a) * (1 + 2 * al * s)
+        assert np.allclose(r.dW[:, 0], [ga, gb], atol=1e-13)
+
+
+def _torch_reference(X, W, y, eps, red, g, al):
+    """torch fp64 autograd of F.cross_entropy(reduction="none") plus
+    alpha logsumexp^2 on the valid rows, reduced as asked."""
+    Xt = torch.tensor(X, requires_grad=True)
+    Wt = torch.tensor(W, requires_grad=True)
+    Z = Xt @ Wt.T
+    yt = torch.tensor(y)
+    ce = torch.nn.functional.cross_entropy(Z, yt, ignore_index=-100, label_smoothing=eps,
+                                           reduction="none")
+    valid = (yt != -100).double()
+    per = ce + al * torch.logsumexp(Z, dim=1) ** 2 * valid
+    if red == "none":
+        L = per
+        (per * torch.tensor(g)).sum().backward()
+    else:
+        L = per.sum() / (max(float(valid.sum()), 1.0) if red == "mean" else 1.0)
+        (L * g).backward()
+    return L.detach().numpy(), Xt.grad.numpy(), Wt.grad.numpy()
+
+
+def check_zloss_and_none_match_torch():
+    cases = [(40, 16, 300, 5, 0.1, "mean", 0.05), (33, 8, 129, 4, 0.0, "sum", 0.2),
+             (29, 12, 200, 6, 0.2, "none", 0.1), (17, 24, 64, 3, 0.0, "none", 0.0)]
+    for n, (N, H, V, ign, eps, red, al) in enumerate(cases):
+        X, W, y = _case(N, H, V, ignore=ign, seed=400 + n)
+        g = np.random.default_rng(n).uniform(-2.0, 2.0, N) if red == "none" else 1.3
+        r = orc.linear_cross_entropy(X, W, y, label_smoothing=eps, reduction=red, grad_loss=g,
+                                     z_loss=al)
+        L, dX, dW = _torch_reference(X, W, y, eps, red, g, al)
+        assert np.allclose(r.loss, L, rtol=1e-12, atol=1e-13), n
+        assert np.allclose(r.dX, dX, rtol=1e-10, atol=1e-13), n
+        assert np.allclose(r.dW, dW, rtol=1e-10, atol=1e-13), n
+
+
+def check_zloss_none_finite_differences():
+    # d/dtheta of sum_i g_i l_i with per-row weights, z-loss and smoothing.
+    h = 1e-6
+    N, H, V = 6, 4, 11
+    X, W, y = _case(N, H, V, ignore=1, seed=500)
+    g = np.random.default_rng(5).uniform(-1.5, 1.5, N)
+    al, eps = 0.2, 0.1
+    r = orc.linear_cross_entropy(X, W, y, label_smoothing=eps, reduction="none", grad_loss=g,
+                                 z_loss=al)
+
+    def L(X_, W_):
+        l = orc.linear_cross_entropy(X_, W_, y, label_smoothing=eps, reduction="none",
+                                     z_loss=al).loss
+        return float((g * l).sum())
+
+    for i in range(N):
+        for k in range(H):
+            Xp = X.copy(); Xp[i, k] += h
+            Xm = X.copy(); Xm[i, k] -= h
+            assert abs((L(Xp, W) - L(Xm, W)) / (2 * h) - r.dX[i, k]) < 1e-7, ("dX", i, k)
+    for v in range(V):
+        for k in range(H):
+            Wp = W.copy(); Wp[v, k] += h
+            Wm = W.copy(); Wm[v, k] -= h
+            assert abs((L(X, Wp) - L(X, Wm)) / (2 * h) - r.dW[v, k]) < 1e-7, ("dW", v, k)
+
+
+def check_reductions_agree():
+    # none summed = sum; mean = sum / N_valid; a constant per-row gradient c
+    # under "none" gives c times the "sum" gradients.
+    X, W, y = _case(31, 7, 90, ignore=4, seed=600)
+    kw = dict(label_smoothing=0.1, z_loss=0.03)
+    none = orc.linear_cross_entropy(X, W, y, reduction="none", grad_loss=np.full(31, 0.7), **kw)
+    s = orc.linear_cross_entropy(X, W, y, reduction="sum", grad_loss=0.7, **kw)
+    m = orc.linear_cross_entropy(X, W, y, reduction="mean", **kw)
+    assert abs(none.loss.sum() - s.loss) < 1e-12 * abs(s.loss)
+    assert abs(m.loss - s.loss / 27) < 1e-13
+    assert np.allclose(none.dX, s.dX, atol=1e-15) and np.allclose(none.dW, s.dW, atol=1e-15)
+
+
+def check_logits_path_matches_torch():
+    # Loss and dZ on given logits ([L27] "Trick 1"): torch autograd on Z.
+    for n, (N, V, ign, eps, red, al) in enumerate([(20, 50, 3, 0.1, "mean", 0.01),
+                                                   (15, 33, 0, 0.0, "none", 0.2),
+                                                   (9, 7, 2, 0.3, "sum", 0.0)]):
+        rng = np.random.default_rng(700 + n)
+        Z = rng.standard_normal((N, V)) * 3.0
+        y = rng.integers(0, V, N)
+        y[rng.choice(N, ign, replace=False)] = -100
+        g = rng.uniform(-1, 1, N) if red == "none" else 0.9
+        loss, lse, dZ = orc.softmax_ce_on_logits(Z, y, label_smoothing=eps, reduction=red,
+                                                 grad_loss=g, z_loss=al)
+        Zt = torch.tensor(Z, requires_grad=True)
+        yt = torch.tensor(y)
+        ce = torch.nn.functional.cross_entropy(Zt, yt, ignore_index=-100, label_smoothing=eps,
+                                               reduction="none")
+        valid = (yt != -100).double()
+        per = ce + al * torch.logsumexp(Zt, dim=1) ** 2 * valid
+        if red == "none":
+            (per * torch.tensor(g)).sum().backward()
+            L = per.detach().numpy()
+        else:
+            Lt = per.sum() / (max(float(valid.sum()), 1.0) if red == "mean" else 1.0)
+            (Lt * g).backward()
+            L = Lt.item()
+        assert np.allclose(loss, L, rtol=1e-12, atol=1e-13), n
+        assert np.allclose(dZ, Zt.grad.numpy(), rtol=1e-10, atol=1e-14), n
+        v = y != -100
+        assert np.allclose(lse[v], torch.logsumexp(torch.tensor(Z), 1).numpy()[v], atol=1e-13)
+
+
 CHECKS = [check_zero_weights_give_log_V, check_two_class_closed_form, check_single_class_is_zero,
           check_uniform_logits_closed_form, check_matches_torch_cross_entropy,
           check_finite_differences, check_gradient_rows_sum_to_zero, check_ignored_rows_are_inert,
           check_shift_invariance, check_large_logits_stay_finite, check_all_ignored_gives_zero,
-          check_row_block_invariance]
+          check_row_block_invariance, check_zloss_zero_weights, check_zloss_two_class_closed_form,
+          check_zloss_and_none_match_torch, check_zloss_none_finite_differences,
+          check_reductions_agree, check_logits_path_matches_torch]
 
 
 @pytest.mark.parametrize("check", CHECKS, ids=[c.__name__[6:] for c in CHECKS])
@@ -244,6 +383,17 @@ def test_sampled_rows_match_full():
     assert np.allclose(dw, r.dW[v], atol=1e-14)
     loss, lse_f, nv = orc.forward(X, W, y, label_smoothing=0.1)
     assert abs(loss - r.loss) < 1e-13 and nv == r.n_valid
+    # the same with z-loss and per-row gradients (reduction "none")
+    g = np.random.default_rng(3).uniform(-1, 1, 50)
+    kw = dict(label_smoothing=0.1, reduction="none", z_loss=0.05)
+    r = orc.linear_cross_entropy(X, W, y, grad_loss=g, **kw)
+    dx, lse, terms = orc.dX_rows(X, W, y, rows, grad_loss=g, **kw)
+    assert np.allclose(dx, r.dX[rows], atol=1e-15)
+    assert np.allclose(terms, r.loss[rows], atol=1e-14)
+    dw = orc.dW_rows(X, W, y, r.lse, v, grad_loss=g, **kw)
+    assert np.allclose(dw, r.dW[v], atol=1e-14)
+    loss, _, _ = orc.forward(X, W, y, **{k: kw[k] for k in kw})
+    assert np.allclose(loss, r.loss, atol=1e-14)
 
 
 # ----------------------------------------------------------- planted mistakes
@@ -252,22 +402,42 @@ def _mutants():
     base_tl, base_dl, base_den = orc.token_losses, orc.dlogits, orc.denominator
     base_lse = orc.log_sum_exp
 
-    def tl_drop_smooth(Z, lse, y, eps):
-        return base_tl(Z, lse, y, 0.0)
+    def tl_drop_smooth(Z, lse, y, eps, z_loss=0.0):
+        return base_tl(Z, lse, y, 0.0, z_loss)
 
-    def tl_sign(Z, lse, y, eps):
-        return -base_tl(Z, lse, y, eps)
+    def tl_sign(Z, lse, y, eps, z_loss=0.0):
+        return -base_tl(Z, lse, y, eps, z_loss)
 
-    def tl_wrong_index(Z, lse, y, eps):
-        return base_tl(Z, lse, (y + 1) % Z.shape[1], eps)
+    def tl_wrong_index(Z, lse, y, eps, z_loss=0.0):
+        return base_tl(Z, lse, (y + 1) % Z.shape[1], eps, z_loss)
 
-    def dl_drop_smooth(Z, lse, y, eps, scale):
-        return base_dl(Z, lse, y, 0.0, scale)
+    def tl_drop_zloss(Z, lse, y, eps, z_loss=0.0):
+        return base_tl(Z, lse, y, eps, 0.0)
 
-    def dl_no_onehot_scale(Z, lse, y, eps, scale):
-        P = np.exp(Z - lse[:, None])
+    def tl_zloss_not_squared(Z, lse, y, eps, z_loss=0.0):
+        return base_tl(Z, lse, y, eps, 0.0) + z_loss * lse
+
+    def dl_drop_smooth(Z, lse, y, eps, scale, z_loss=0.0):
+        return base_dl(Z, lse, y, 0.0, scale, z_loss)
+
+    def dl_no_onehot_scale(Z, lse, y, eps, scale, z_loss=0.0):
+        P = np.exp(Z - lse[:, None]) * (1.0 + 2.0 * z_loss * lse)[:, None]
         P[np.arange(Z.shape[0]), y] -= 1.0
-        return (P - eps / Z.shape[1]) * scale
+        sc = np.asarray(scale)
+        return (P - eps / Z.shape[1]) * (sc[:, None] if sc.ndim else sc)
+
+    def dl_zloss_half(Z, lse, y, eps, scale, z_loss=0.0):
+        return base_dl(Z, lse, y, eps, scale, 0.5 * z_loss)
+
+    def dl_zloss_on_target(Z, lse, y, eps, scale, z_loss=0.0):
+        # z-loss factor applied to (p - q) instead of p
+        d = base_dl(Z, lse, y, eps, 1.0, 0.0) * (1.0 + 2.0 * z_loss * lse)[:, None]
+        sc = np.asarray(scale)
+        return d * (sc[:, None] if sc.ndim else sc)
+
+    def rs_ignore_rows(grad_loss, n_rows, D, reduction):
+        g = np.asarray(grad_loss, dtype=np.float64)
+        return np.full(n_rows, float(g.mean()) / D)
 
     def den_all_rows(n_valid, reduction):
         return base_den(n_valid + 1, reduction)
@@ -282,8 +452,11 @@ def _mutants():
         return X @ W.T * 1.0000001
 
     return [("token_losses", tl_drop_smooth), ("token_losses", tl_sign),
-            ("token_losses", tl_wrong_index), ("dlogits", dl_drop_smooth),
-            ("dlogits", dl_no_onehot_scale), ("denominator", den_all_rows),
+            ("token_losses", tl_wrong_index), ("token_losses", tl_drop_zloss),
+            ("token_losses", tl_zloss_not_squared), ("dlogits", dl_drop_smooth),
+            ("dlogits", dl_no_onehot_scale), ("dlogits", dl_zloss_half),
+            ("dlogits", dl_zloss_on_target), ("row_scales", rs_ignore_rows),
+            ("denominator", den_all_rows),
             ("log_sum_exp", lse_no_max), ("log_sum_exp", lse_drop_max),
             ("logits", logits_transposed_bad)]
 
