@@ -47,6 +47,9 @@
  *     H must be a multiple of 8 (bf16) or 4 (fp32), so that every row starts
  *     on a 16-byte boundary.
  *   - Shapes: N >= 0, H >= 1, V >= 1.  N = 0 gives loss 0 and dW = 0.
+ *   - fce_forward, fce_backward and fce_fused_fwd_bwd take reduction
+ *     FCE_MEAN or FCE_SUM (FCE_NONE is FCE_ERR_ARG there; see the *_ex
+ *     entry points further down for it and for z-loss).
  *
  * `chunk` bounds the logit-space scratch of the backward pass to chunk x V
  * elements (bf16 for FCE_BF16, fp32 for FCE_F32, each dimension rounded up
@@ -73,7 +76,7 @@ typedef enum {
   FCE_OK = 0,
   FCE_ERR_NULL = -1,      /* a required pointer is NULL */
   FCE_ERR_SHAPE = -2,     /* N < 0, H < 1, V < 1, or sizes overflow */
-  FCE_ERR_ARG = -3,       /* bad enum, chunk < 1, label_smoothing outside [0,1) or NaN */
+  FCE_ERR_ARG = -3,       /* bad enum or option, chunk < 1, label_smoothing outside [0,1) */
   FCE_ERR_WORKSPACE = -4, /* workspace smaller than fce_workspace_size() */
   FCE_ERR_ALIGN = -5,     /* pointer not 16-byte aligned or H not a multiple of 8 / 4 */
   FCE_ERR_DEVICE = -6,    /* current device is not gfx950 */
@@ -81,7 +84,8 @@ typedef enum {
 } fce_status;
 
 typedef enum { FCE_F32 = 0, FCE_BF16 = 1 } fce_dtype;
-typedef enum { FCE_MEAN = 0, FCE_SUM = 1 } fce_reduction;
+/* FCE_NONE (per-token losses) is accepted by the *_ex entry points only. */
+typedef enum { FCE_MEAN = 0, FCE_SUM = 1, FCE_NONE = 2 } fce_reduction;
 typedef enum { FCE_SCHED_AUTO = 0, FCE_SCHED_TOKEN = 1, FCE_SCHED_VOCAB = 2 } fce_schedule;
 
 /* The backward schedule chosen for a problem (host-only, no GPU needed). */
@@ -96,6 +100,19 @@ typedef struct {
   int64_t fwd_splits;       /* vocabulary splits of the forward reduction          */
   int64_t grad_rmw_bytes;   /* fp32 dX/dW bytes written + re-read across blocks    */
 } fce_plan_info;
+
+/* Loss options of the *_ex entry points.  Fields are fixed-width so the
+ * layout is the same for every caller (32 bytes). */
+typedef struct {
+  int32_t ignore_index;   /* a label equal to this carries no loss (usually -100)        */
+  float label_smoothing;  /* eps in [0, 1)                                               */
+  float z_loss;           /* alpha >= 0, finite: adds alpha * LSE_i^2 to each valid row's
+                             loss (llms.blog, "Numerical Considerations", item 3)       */
+  int32_t reduction;      /* fce_reduction: FCE_MEAN, FCE_SUM or FCE_NONE               */
+  int64_t chunk;          /* logit-space budget, chunk x V elements (>= 1)              */
+  int32_t schedule;       /* fce_schedule                                               */
+  int32_t variant;        /* reserved: must be 0                                         */
+} fce_options;
 
 /* Size in bytes of the workspace the three compute entry points need for
  * this problem (host-only).  Returns 0 if the arguments are invalid. */
@@ -137,6 +154,47 @@ fce_status fce_fused_fwd_bwd(const void* X, const void* W, const int32_t* labels
 /* Number of labels outside [0, V) that were not ignore_index in the last
  * call that used this workspace.  Synchronises `stream`. */
 fce_status fce_get_label_errors(const void* workspace, int32_t* host_count, hipStream_t stream);
+
+/* ---- Entry points with loss options (fce_options).
+ *
+ * The same operation as fce_forward / fce_backward / fce_fused_fwd_bwd, with
+ * two more loss terms and one more reduction:
+ *   l_i  = LSE_i - (1-eps) z_{i,y_i} - (eps/V) sum_j z_ij + alpha LSE_i^2
+ *   dZ_ij = (softmax_ij (1 + 2 alpha LSE_i) - (1-eps)[j = y_i] - eps/V) * s_i
+ * with s_i = g / D for FCE_MEAN and FCE_SUM (g the scalar upstream
+ * gradient), and s_i = g_i for FCE_NONE (one upstream gradient per token).
+ * For FCE_NONE the loss output is float[N]: l_i for a valid row, 0 for an
+ * ignored row, NaN for a label outside [0, V) that is not ignore_index.
+ * `opt` is a host pointer; NULL is FCE_ERR_NULL.  A z_loss that is negative,
+ * infinite or NaN, an unknown reduction or schedule, chunk < 1 or a
+ * non-zero variant is FCE_ERR_ARG.  With the default-valued options
+ * (z_loss 0, reduction mean or sum) they equal the entry points above
+ * bitwise.  Everything else is as documented above. */
+
+/* Workspace size for these options (host-only; 0 if arguments are invalid). */
+size_t fce_workspace_size_ex(int64_t N, int64_t H, int64_t V, fce_dtype dtype,
+                             const fce_options* opt);
+
+/* Forward: loss (float[1], or float[N] for FCE_NONE) and lse[N]. */
+fce_status fce_forward_ex(const void* X, const void* W, const int32_t* labels, int64_t N,
+                          int64_t H, int64_t V, fce_dtype dtype, const fce_options* opt,
+                          float* loss, float* lse, void* workspace, size_t workspace_bytes,
+                          hipStream_t stream);
+
+/* Backward: grad_loss is float[1] (FCE_MEAN, FCE_SUM) or float[N]
+ * (FCE_NONE), device, or NULL for ones.  lse from fce_forward_ex with the
+ * same X, W, labels and options. */
+fce_status fce_backward_ex(const void* X, const void* W, const int32_t* labels, int64_t N,
+                           int64_t H, int64_t V, fce_dtype dtype, const fce_options* opt,
+                           const float* lse, const float* grad_loss, float* dX, float* dW,
+                           void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* Fused forward and backward with upstream gradient 1 (for FCE_NONE: 1 for
+ * every token). */
+fce_status fce_fused_fwd_bwd_ex(const void* X, const void* W, const int32_t* labels, int64_t N,
+                                int64_t H, int64_t V, fce_dtype dtype, const fce_options* opt,
+                                float* loss, float* dX, float* dW, void* workspace,
+                                size_t workspace_bytes, hipStream_t stream);
 
 /* Static description of a status code. */
 const char* fce_status_string(fce_status status);

@@ -20,9 +20,16 @@ from ._binding import (  # noqa: F401
     FCE_F32,
     FceError,
     SCHEDULES,
+    FCE_NONE,
+    REDUCTIONS,
     fce_backward,
+    fce_backward_ex,
     fce_forward,
+    fce_forward_ex,
     fce_fused_fwd_bwd,
+    fce_fused_fwd_bwd_ex,
+    fce_workspace_size_ex,
+    make_options,
     fce_get_label_errors,
     fce_plan,
     status_string,
@@ -60,8 +67,7 @@ def _make_function():
 
     class _LinearCrossEntropy(torch.autograd.Function):
         @staticmethod
-        def forward(ctx, hidden, weight, labels, ignore_index, label_smoothing, reduction, chunk,
-                    schedule):
+        def forward(ctx, hidden, weight, labels, opts):
             H = hidden.shape[-1]
             X = hidden.reshape(-1, H).contiguous()
             W = weight.contiguous()
@@ -69,28 +75,32 @@ def _make_function():
                 raise TypeError("hidden and weight must share a dtype")
             y = labels.reshape(-1).to(torch.int32).contiguous()
             N, V = X.shape[0], W.shape[0]
-            ws = workspace_for(N, H, V, X.dtype, chunk, schedule, X.device)
-            loss = torch.empty(1, dtype=torch.float32, device=X.device)
+            code = FCE_BF16 if X.dtype == torch.bfloat16 else FCE_F32
+            n = fce_workspace_size_ex(N, H, V, code, **opts)
+            if n == 0:
+                raise ValueError("invalid problem or options for fce_workspace_size_ex")
+            ws = torch.empty(n, dtype=torch.uint8, device=X.device)
+            none = opts["reduction"] == "none"
+            loss = torch.empty(N if none else 1, dtype=torch.float32, device=X.device)
             lse = torch.empty(max(N, 1), dtype=torch.float32, device=X.device)
-            fce_forward(X if N else None, W, y if N else None, loss, lse, ws, ignore_index,
-                        label_smoothing, reduction, chunk, schedule)
+            fce_forward_ex(X if N else None, W, y if N else None, loss if loss.numel() else None,
+                           lse, ws, **opts)
             ctx.save_for_backward(X, W, y, lse)
-            ctx.cfg = (ignore_index, label_smoothing, reduction, chunk, schedule, hidden.shape,
-                       hidden.dtype, weight.dtype)
+            ctx.cfg = (opts, hidden.shape, hidden.dtype, weight.dtype)
             ctx.ws = ws
-            return loss[0]
+            return loss.reshape(labels.shape) if none else loss[0]
 
         @staticmethod
         def backward(ctx, g):
             X, W, y, lse = ctx.saved_tensors
-            ignore_index, eps, reduction, chunk, schedule, hshape, hdt, wdt = ctx.cfg
+            opts, hshape, hdt, wdt = ctx.cfg
             N, H = X.shape
-            g1 = g.reshape(1).to(torch.float32).contiguous()
+            g1 = g.reshape(-1).to(torch.float32).contiguous()
             dX = torch.empty((N, H), dtype=torch.float32, device=X.device)
             dW = torch.empty(W.shape, dtype=torch.float32, device=X.device)
-            fce_backward(X if N else None, W, y if N else None, lse, g1, dX if N else None, dW,
-                         ctx.ws, ignore_index, eps, reduction, chunk, schedule)
-            return (dX.to(hdt).reshape(hshape), dW.to(wdt), None, None, None, None, None, None)
+            fce_backward_ex(X if N else None, W, y if N else None, lse,
+                            g1 if g1.numel() else None, dX if N else None, dW, ctx.ws, **opts)
+            return dX.to(hdt).reshape(hshape), dW.to(wdt), None, None
 
     return _LinearCrossEntropy
 
@@ -100,14 +110,19 @@ _FN = None
 
 def linear_cross_entropy(hidden, weight, labels, ignore_index: int = -100,
                          label_smoothing: float = 0.0, reduction: str = "mean", chunk: int = 1024,
-                         schedule: str = "auto"):
-    """Mean (or summed) cross-entropy of ``hidden @ weight.T`` against ``labels``.
+                         schedule: str = "auto", z_loss: float = 0.0):
+    """Cross-entropy of ``hidden @ weight.T`` against ``labels``: a scalar for
+    reduction "mean" or "sum", per-token losses (labels' shape) for "none".
 
     hidden [..., H] and weight [V, H] share a dtype (bfloat16 or float32);
     labels [...] are class indices, ``ignore_index`` rows carry no loss.
-    Gradients for hidden and weight come from the fused backward."""
+    ``z_loss`` = alpha adds alpha * logsumexp(z)^2 per token.  Gradients for
+    hidden and weight come from the fused backward."""
     global _FN
     if _FN is None:
         _FN = _make_function()
-    return _FN.apply(hidden, weight, labels, ignore_index, label_smoothing, reduction, chunk,
-                     schedule)
+    if reduction not in REDUCTIONS:
+        raise ValueError(f"unknown reduction {reduction!r}")
+    opts = dict(ignore_index=ignore_index, label_smoothing=label_smoothing, z_loss=z_loss,
+                reduction=reduction, chunk=chunk, schedule=schedule)
+    return _FN.apply(hidden, weight, labels, opts)

@@ -26,13 +26,15 @@ FCE_F32 = 0
 FCE_BF16 = 1
 FCE_MEAN = 0
 FCE_SUM = 1
+FCE_NONE = 2
 SCHED_AUTO = 0
 SCHED_TOKEN = 1
 SCHED_VOCAB = 2
 SCHEDULES = {"auto": SCHED_AUTO, "token": SCHED_TOKEN, "vocab": SCHED_VOCAB}
-REDUCTIONS = {"mean": FCE_MEAN, "sum": FCE_SUM}
+REDUCTIONS = {"mean": FCE_MEAN, "sum": FCE_SUM, "none": FCE_NONE}
 
 EXPORTED = ("fce_workspace_size", "fce_plan", "fce_forward", "fce_backward", "fce_fused_fwd_bwd",
+            "fce_workspace_size_ex", "fce_forward_ex", "fce_backward_ex", "fce_fused_fwd_bwd_ex",
             "fce_get_label_errors", "fce_status_string", "fce_last_hip_error",
             "fce_timing_enable", "fce_timing_read")
 
@@ -55,6 +57,21 @@ class PlanInfo(ctypes.Structure):
 
     def as_dict(self):
         return {k: getattr(self, k) for k, _ in self._fields_}
+
+
+class Options(ctypes.Structure):
+    """fce_options (include/fce.h)."""
+    _fields_ = [("ignore_index", ctypes.c_int32), ("label_smoothing", ctypes.c_float),
+                ("z_loss", ctypes.c_float), ("reduction", ctypes.c_int32),
+                ("chunk", ctypes.c_int64), ("schedule", ctypes.c_int32),
+                ("variant", ctypes.c_int32)]
+
+
+def make_options(ignore_index=-100, label_smoothing=0.0, z_loss=0.0, reduction="mean", chunk=1024,
+                 schedule="auto", variant=0) -> Options:
+    return Options(int(ignore_index), float(label_smoothing), float(z_loss),
+                   REDUCTIONS.get(reduction, reduction), int(chunk),
+                   SCHEDULES.get(schedule, schedule), int(variant))
 
 
 class KernelTiming(ctypes.Structure):
@@ -93,6 +110,16 @@ def load_library(path: str = LIB_PATH):
     lib.fce_backward.argtypes = common + [vp, vp, vp, vp, vp, u64, vp]
     lib.fce_fused_fwd_bwd.restype = i32
     lib.fce_fused_fwd_bwd.argtypes = common + [vp, vp, vp, vp, u64, vp]
+    op = ctypes.POINTER(Options)
+    lib.fce_workspace_size_ex.restype = u64
+    lib.fce_workspace_size_ex.argtypes = [i64, i64, i64, i32, op]
+    common_ex = [vp, vp, vp, i64, i64, i64, i32, op]
+    lib.fce_forward_ex.restype = i32
+    lib.fce_forward_ex.argtypes = common_ex + [vp, vp, vp, u64, vp]
+    lib.fce_backward_ex.restype = i32
+    lib.fce_backward_ex.argtypes = common_ex + [vp, vp, vp, vp, vp, u64, vp]
+    lib.fce_fused_fwd_bwd_ex.restype = i32
+    lib.fce_fused_fwd_bwd_ex.argtypes = common_ex + [vp, vp, vp, vp, u64, vp]
     lib.fce_get_label_errors.restype = i32
     lib.fce_get_label_errors.argtypes = [vp, ctypes.POINTER(i32), vp]
     lib.fce_status_string.restype = ctypes.c_char_p
@@ -181,6 +208,43 @@ def fce_fused_fwd_bwd(X, W, labels, loss, dX, dW, workspace, ignore_index=-100,
                                           workspace.numel() * workspace.element_size(),
                                           _stream(stream))
     _check(st, "fce_fused_fwd_bwd")
+
+
+def fce_workspace_size_ex(N, H, V, dtype, **options) -> int:
+    o = make_options(**options)
+    return int(load_library().fce_workspace_size_ex(N, H, V, dtype, ctypes.byref(o)))
+
+
+def _common_ex(X, W, labels):
+    N, H = (X.shape[0], X.shape[1]) if X is not None else (0, W.shape[1])
+    return [_ptr(X), _ptr(W), _ptr(labels), N, H, W.shape[0], _dtype_code(W)]
+
+
+def _ws(workspace):
+    return [_ptr(workspace), workspace.numel() * workspace.element_size()]
+
+
+def fce_forward_ex(X, W, labels, loss, lse, workspace, stream=None, **options):
+    o = make_options(**options)
+    st = load_library().fce_forward_ex(*_common_ex(X, W, labels), ctypes.byref(o), _ptr(loss),
+                                       _ptr(lse), *_ws(workspace), _stream(stream))
+    _check(st, "fce_forward_ex")
+
+
+def fce_backward_ex(X, W, labels, lse, grad_loss, dX, dW, workspace, stream=None, **options):
+    o = make_options(**options)
+    st = load_library().fce_backward_ex(*_common_ex(X, W, labels), ctypes.byref(o), _ptr(lse),
+                                        _ptr(grad_loss), _ptr(dX), _ptr(dW), *_ws(workspace),
+                                        _stream(stream))
+    _check(st, "fce_backward_ex")
+
+
+def fce_fused_fwd_bwd_ex(X, W, labels, loss, dX, dW, workspace, stream=None, **options):
+    o = make_options(**options)
+    st = load_library().fce_fused_fwd_bwd_ex(*_common_ex(X, W, labels), ctypes.byref(o),
+                                             _ptr(loss), _ptr(dX), _ptr(dW), *_ws(workspace),
+                                             _stream(stream))
+    _check(st, "fce_fused_fwd_bwd_ex")
 
 
 def fce_get_label_errors(workspace, stream=None) -> int:

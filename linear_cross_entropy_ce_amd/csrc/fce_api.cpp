@@ -101,28 +101,122 @@ fce_status check_device() {
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
+// Options of one call, checked.  allow_none: the *_ex entry points.
+fce_status check_options(const fce_options* opt, bool allow_none, fce::LossOpts* lo) {
+  if (opt == nullptr) return FCE_ERR_NULL;
+  const int r = opt->reduction;
+  if (r != FCE_MEAN && r != FCE_SUM && !(allow_none && r == FCE_NONE)) return FCE_ERR_ARG;
+  if (opt->schedule != FCE_SCHED_AUTO && opt->schedule != FCE_SCHED_TOKEN &&
+      opt->schedule != FCE_SCHED_VOCAB)
+    return FCE_ERR_ARG;
+  if (opt->chunk < 1 || opt->variant != 0) return FCE_ERR_ARG;
+  const float eps = opt->label_smoothing;
+  if (!(eps >= 0.0f && eps < 1.0f)) return FCE_ERR_ARG;  // also rejects NaN
+  const float z = opt->z_loss;
+  if (!(z >= 0.0f && z <= 3.4e38f)) return FCE_ERR_ARG;  // rejects NaN and +inf
+  lo->ignore = opt->ignore_index;
+  lo->eps = eps;
+  lo->zloss = z;
+  lo->reduction = static_cast<fce::Reduction>(r);
+  return FCE_OK;
+}
+
 fce_status validate(const void* X, const void* W, const int32_t* labels, int64_t N, int64_t H,
-                    int64_t V, fce_dtype dtype, float eps, fce_reduction red, int64_t chunk,
-                    fce_schedule sched, size_t ws_bytes, const void* ws, Plan* plan) {
+                    int64_t V, fce_dtype dtype, const fce_options* opt, bool allow_none,
+                    size_t ws_bytes, const void* ws, Plan* plan, fce::LossOpts* lo) {
   if (N < 0 || H < 1 || V < 1) return FCE_ERR_SHAPE;
   if (W == nullptr || ws == nullptr) return FCE_ERR_NULL;
   if (N > 0 && (X == nullptr || labels == nullptr)) return FCE_ERR_NULL;
   if (dtype != FCE_F32 && dtype != FCE_BF16) return FCE_ERR_ARG;
-  if (red != FCE_MEAN && red != FCE_SUM) return FCE_ERR_ARG;
-  if (sched != FCE_SCHED_AUTO && sched != FCE_SCHED_TOKEN && sched != FCE_SCHED_VOCAB)
-    return FCE_ERR_ARG;
-  if (chunk < 1) return FCE_ERR_ARG;
-  if (!(eps >= 0.0f && eps < 1.0f)) return FCE_ERR_ARG;  // also rejects NaN
+  if (fce_status s = check_options(opt, allow_none, lo); s != FCE_OK) return s;
   const int64_t vec = (dtype == FCE_BF16) ? 8 : 4;
   if (H % vec != 0) return FCE_ERR_ALIGN;
   if (!aligned16(W) || !aligned16(ws) || (N > 0 && !aligned16(X))) return FCE_ERR_ALIGN;
-  if (!fce::make_plan(N, H, V, static_cast<Dtype>(dtype), chunk, static_cast<Schedule>(sched),
-                      plan))
+  if (!fce::make_plan(N, H, V, static_cast<Dtype>(dtype), opt->chunk,
+                      static_cast<Schedule>(opt->schedule), plan))
     return FCE_ERR_SHAPE;
   if (ws_bytes < plan->total) return FCE_ERR_WORKSPACE;
   return FCE_OK;
 }
 
+fce_options make_options(int32_t ignore_index, float eps, fce_reduction reduction, int64_t chunk,
+                         fce_schedule schedule) {
+  fce_options o;
+  std::memset(&o, 0, sizeof(o));
+  o.ignore_index = ignore_index;
+  o.label_smoothing = eps;
+  o.z_loss = 0.0f;
+  o.reduction = reduction;
+  o.chunk = chunk;
+  o.schedule = schedule;
+  o.variant = 0;
+  return o;
+}
+
+fce_status forward_impl(const void* X, const void* W, const int32_t* labels, int64_t N, int64_t H,
+                        int64_t V, fce_dtype dtype, const fce_options* opt, bool allow_none,
+                        float* loss, float* lse, void* workspace, size_t workspace_bytes,
+                        hipStream_t stream) {
+  Plan p;
+  fce::LossOpts lo;
+  fce_status s = validate(X, W, labels, N, H, V, dtype, opt, allow_none, workspace_bytes,
+                          workspace, &p, &lo);
+  if (s != FCE_OK) return s;
+  const bool none = lo.reduction == fce::Reduction::None;
+  if ((loss == nullptr && !(none && N == 0)) || (N > 0 && lse == nullptr)) return FCE_ERR_NULL;
+  if ((s = check_device()) != FCE_OK) return s;
+  char* ws = static_cast<char*>(workspace);
+  hipError_t e = fce::launch_label_scan(p, labels, lo, nullptr, ws, stream, timer());
+  if (e == hipSuccess) e = fce::launch_forward(p, X, W, labels, lo, loss, lse, ws, stream, timer());
+  return from_hip(e);
+}
+
+fce_status backward_impl(const void* X, const void* W, const int32_t* labels, int64_t N, int64_t H,
+                         int64_t V, fce_dtype dtype, const fce_options* opt, bool allow_none,
+                         const float* lse, const float* grad_loss, float* dX, float* dW,
+                         void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  Plan p;
+  fce::LossOpts lo;
+  fce_status s = validate(X, W, labels, N, H, V, dtype, opt, allow_none, workspace_bytes,
+                          workspace, &p, &lo);
+  if (s != FCE_OK) return s;
+  if (dW == nullptr || (N > 0 && (lse == nullptr || dX == nullptr))) return FCE_ERR_NULL;
+  if (!aligned16(dW) || (N > 0 && !aligned16(dX))) return FCE_ERR_ALIGN;
+  if ((s = check_device()) != FCE_OK) return s;
+  const bool none = lo.reduction == fce::Reduction::None;
+  char* ws = static_cast<char*>(workspace);
+  hipError_t e = fce::launch_label_scan(p, labels, lo, none ? nullptr : grad_loss, ws, stream,
+                                        timer());
+  if (e == hipSuccess)
+    e = fce::launch_backward(p, X, W, labels, lo, lse, none ? grad_loss : nullptr, dX, dW, ws,
+                             stream, timer());
+  return from_hip(e);
+}
+
+fce_status fused_impl(const void* X, const void* W, const int32_t* labels, int64_t N, int64_t H,
+                      int64_t V, fce_dtype dtype, const fce_options* opt, bool allow_none,
+                      float* loss, float* dX, float* dW, void* workspace, size_t workspace_bytes,
+                      hipStream_t stream) {
+  Plan p;
+  fce::LossOpts lo;
+  fce_status s = validate(X, W, labels, N, H, V, dtype, opt, allow_none, workspace_bytes,
+                          workspace, &p, &lo);
+  if (s != FCE_OK) return s;
+  const bool none = lo.reduction == fce::Reduction::None;
+  if ((loss == nullptr && !(none && N == 0)) || dW == nullptr || (N > 0 && dX == nullptr))
+    return FCE_ERR_NULL;
+  if (!aligned16(dW) || (N > 0 && !aligned16(dX))) return FCE_ERR_ALIGN;
+  if ((s = check_device()) != FCE_OK) return s;
+  char* ws = static_cast<char*>(workspace);
+  float* lse = reinterpret_cast<float*>(ws + p.off_lse);
+  // One label scan serves both passes: with g = 1 its backward scale equals
+  // the one fce_backward would compute.
+  hipError_t e = fce::launch_label_scan(p, labels, lo, nullptr, ws, stream, timer());
+  if (e == hipSuccess) e = fce::launch_forward(p, X, W, labels, lo, loss, lse, ws, stream, timer());
+  if (e == hipSuccess)
+    e = fce::launch_backward(p, X, W, labels, lo, lse, nullptr, dX, dW, ws, stream, timer());
+  return from_hip(e);
+}
 
 }  // namespace
 
@@ -130,12 +224,18 @@ extern "C" {
 
 size_t fce_workspace_size(int64_t N, int64_t H, int64_t V, fce_dtype dtype, int64_t chunk,
                           fce_schedule schedule) {
+  const fce_options o = make_options(-100, 0.0f, FCE_MEAN, chunk, schedule);
+  return fce_workspace_size_ex(N, H, V, dtype, &o);
+}
+
+size_t fce_workspace_size_ex(int64_t N, int64_t H, int64_t V, fce_dtype dtype,
+                             const fce_options* opt) {
   if (dtype != FCE_F32 && dtype != FCE_BF16) return 0;
-  if (schedule != FCE_SCHED_AUTO && schedule != FCE_SCHED_TOKEN && schedule != FCE_SCHED_VOCAB)
-    return 0;
+  fce::LossOpts lo;
+  if (check_options(opt, true, &lo) != FCE_OK) return 0;
   Plan p;
-  if (!fce::make_plan(N, H, V, static_cast<Dtype>(dtype), chunk, static_cast<Schedule>(schedule),
-                      &p))
+  if (!fce::make_plan(N, H, V, static_cast<Dtype>(dtype), opt->chunk,
+                      static_cast<Schedule>(opt->schedule), &p))
     return 0;
   return p.total;
 }
@@ -168,19 +268,9 @@ fce_status fce_forward(const void* X, const void* W, const int32_t* labels, int6
                        int64_t V, fce_dtype dtype, int32_t ignore_index, float label_smoothing,
                        fce_reduction reduction, int64_t chunk, fce_schedule schedule, float* loss,
                        float* lse, void* workspace, size_t workspace_bytes, hipStream_t stream) {
-  Plan p;
-  fce_status s = validate(X, W, labels, N, H, V, dtype, label_smoothing, reduction, chunk,
-                          schedule, workspace_bytes, workspace, &p);
-  if (s != FCE_OK) return s;
-  if (loss == nullptr || (N > 0 && lse == nullptr)) return FCE_ERR_NULL;
-  if ((s = check_device()) != FCE_OK) return s;
-  char* ws = static_cast<char*>(workspace);
-  hipError_t e = fce::launch_label_scan(p, labels, ignore_index, reduction == FCE_SUM, nullptr, ws,
-                                        stream, timer());
-  if (e == hipSuccess)
-    e = fce::launch_forward(p, X, W, labels, ignore_index, label_smoothing, loss, lse, ws, stream,
-                            timer());
-  return from_hip(e);
+  const fce_options o = make_options(ignore_index, label_smoothing, reduction, chunk, schedule);
+  return forward_impl(X, W, labels, N, H, V, dtype, &o, false, loss, lse, workspace,
+                      workspace_bytes, stream);
 }
 
 fce_status fce_backward(const void* X, const void* W, const int32_t* labels, int64_t N, int64_t H,
@@ -188,20 +278,9 @@ fce_status fce_backward(const void* X, const void* W, const int32_t* labels, int
                         fce_reduction reduction, int64_t chunk, fce_schedule schedule,
                         const float* lse, const float* grad_loss, float* dX, float* dW,
                         void* workspace, size_t workspace_bytes, hipStream_t stream) {
-  Plan p;
-  fce_status s = validate(X, W, labels, N, H, V, dtype, label_smoothing, reduction, chunk,
-                          schedule, workspace_bytes, workspace, &p);
-  if (s != FCE_OK) return s;
-  if (dW == nullptr || (N > 0 && (lse == nullptr || dX == nullptr))) return FCE_ERR_NULL;
-  if (!aligned16(dW) || (N > 0 && !aligned16(dX))) return FCE_ERR_ALIGN;
-  if ((s = check_device()) != FCE_OK) return s;
-  char* ws = static_cast<char*>(workspace);
-  hipError_t e = fce::launch_label_scan(p, labels, ignore_index, reduction == FCE_SUM, grad_loss,
-                                        ws, stream, timer());
-  if (e == hipSuccess)
-    e = fce::launch_backward(p, X, W, labels, ignore_index, label_smoothing, lse, dX, dW, ws,
-                             stream, timer());
-  return from_hip(e);
+  const fce_options o = make_options(ignore_index, label_smoothing, reduction, chunk, schedule);
+  return backward_impl(X, W, labels, N, H, V, dtype, &o, false, lse, grad_loss, dX, dW, workspace,
+                       workspace_bytes, stream);
 }
 
 fce_status fce_fused_fwd_bwd(const void* X, const void* W, const int32_t* labels, int64_t N,
@@ -209,26 +288,33 @@ fce_status fce_fused_fwd_bwd(const void* X, const void* W, const int32_t* labels
                              float label_smoothing, fce_reduction reduction, int64_t chunk,
                              fce_schedule schedule, float* loss, float* dX, float* dW,
                              void* workspace, size_t workspace_bytes, hipStream_t stream) {
-  Plan p;
-  fce_status s = validate(X, W, labels, N, H, V, dtype, label_smoothing, reduction, chunk,
-                          schedule, workspace_bytes, workspace, &p);
-  if (s != FCE_OK) return s;
-  if (loss == nullptr || dW == nullptr || (N > 0 && dX == nullptr)) return FCE_ERR_NULL;
-  if (!aligned16(dW) || (N > 0 && !aligned16(dX))) return FCE_ERR_ALIGN;
-  if ((s = check_device()) != FCE_OK) return s;
-  char* ws = static_cast<char*>(workspace);
-  float* lse = reinterpret_cast<float*>(ws + p.off_lse);
-  // One label scan serves both passes: with g = 1 its backward scale equals
-  // the one fce_backward would compute.
-  hipError_t e = fce::launch_label_scan(p, labels, ignore_index, reduction == FCE_SUM, nullptr, ws,
-                                        stream, timer());
-  if (e == hipSuccess)
-    e = fce::launch_forward(p, X, W, labels, ignore_index, label_smoothing, loss, lse, ws, stream,
-                            timer());
-  if (e == hipSuccess)
-    e = fce::launch_backward(p, X, W, labels, ignore_index, label_smoothing, lse, dX, dW, ws,
-                             stream, timer());
-  return from_hip(e);
+  const fce_options o = make_options(ignore_index, label_smoothing, reduction, chunk, schedule);
+  return fused_impl(X, W, labels, N, H, V, dtype, &o, false, loss, dX, dW, workspace,
+                    workspace_bytes, stream);
+}
+
+fce_status fce_forward_ex(const void* X, const void* W, const int32_t* labels, int64_t N,
+                          int64_t H, int64_t V, fce_dtype dtype, const fce_options* opt,
+                          float* loss, float* lse, void* workspace, size_t workspace_bytes,
+                          hipStream_t stream) {
+  return forward_impl(X, W, labels, N, H, V, dtype, opt, true, loss, lse, workspace,
+                      workspace_bytes, stream);
+}
+
+fce_status fce_backward_ex(const void* X, const void* W, const int32_t* labels, int64_t N,
+                           int64_t H, int64_t V, fce_dtype dtype, const fce_options* opt,
+                           const float* lse, const float* grad_loss, float* dX, float* dW,
+                           void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  return backward_impl(X, W, labels, N, H, V, dtype, opt, true, lse, grad_loss, dX, dW, workspace,
+                       workspace_bytes, stream);
+}
+
+fce_status fce_fused_fwd_bwd_ex(const void* X, const void* W, const int32_t* labels, int64_t N,
+                                int64_t H, int64_t V, fce_dtype dtype, const fce_options* opt,
+                                float* loss, float* dX, float* dW, void* workspace,
+                                size_t workspace_bytes, hipStream_t stream) {
+  return fused_impl(X, W, labels, N, H, V, dtype, opt, true, loss, dX, dW, workspace,
+                    workspace_bytes, stream);
 }
 
 fce_status fce_get_label_errors(const void* workspace, int32_t* host_count, hipStream_t stream) {

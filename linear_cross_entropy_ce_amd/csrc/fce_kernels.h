@@ -18,15 +18,27 @@ class KernelTimer {
   virtual void end(hipStream_t st) = 0;
 };
 
-hipError_t launch_label_scan(const Plan& p, const int32_t* labels, int ignore, int reduction_sum,
+// Loss options shared by every launch of one call.
+enum class Reduction { Mean = 0, Sum = 1, None = 2 };
+struct LossOpts {
+  int ignore = -100;
+  float eps = 0.0f;     // label smoothing
+  float zloss = 0.0f;   // alpha of the z-loss term alpha * LSE^2
+  Reduction reduction = Reduction::Mean;
+};
+
+// `grad`: the upstream gradient, a device scalar (mean / sum) or NULL (1).
+hipError_t launch_label_scan(const Plan& p, const int32_t* labels, const LossOpts& o,
                              const float* grad, char* ws, hipStream_t st, KernelTimer* timer);
 
+// `loss`: one float (mean / sum) or N floats (none).
 hipError_t launch_forward(const Plan& p, const void* X, const void* W, const int32_t* labels,
-                          int ignore, float eps, float* loss, float* lse, char* ws, hipStream_t st,
+                          const LossOpts& o, float* loss, float* lse, char* ws, hipStream_t st,
                           KernelTimer* timer);
 
+// `grad_tok`: per-token upstream gradient [N] for reduction none, or NULL (1).
 hipError_t launch_backward(const Plan& p, const void* X, const void* W, const int32_t* labels,
-                           int ignore, float eps, const float* lse, float* dX, float* dW, char* ws,
-                           hipStream_t st, KernelTimer* timer);
+                           const LossOpts& o, const float* lse, const float* grad_tok, float* dX,
+                           float* dW, char* ws, hipStream_t st, KernelTimer* timer);
 
 }  // namespace fce

@@ -50,8 +50,10 @@ __device__ __forceinline__ void lse_merge(floatx4& a, const floatx4& b) {
 }
 
 // ---------------------------------------------------------------- label scan
+// reduction: 0 mean (D = max(N_valid, 1)), 1 sum (D = 1), 2 none (D = 1, and
+// the upstream gradient is applied per token by the dZ kernel).
 __global__ __launch_bounds__(1024) void k_label_scan(const int32_t* __restrict__ labels, int N,
-                                                     int V, int ignore, int reduction_sum,
+                                                     int V, int ignore, int reduction,
                                                      const float* __restrict__ grad, Ctrl* ctrl,
                                                      int32_t* flags, int CN, int nblocks) {
   __shared__ int s_valid[1024], s_bad[1024];
@@ -80,8 +82,8 @@ __global__ __launch_bounds__(1024) void k_label_scan(const int32_t* __restrict__
   }
   if (tid == 0) {
     const int n_valid = s_valid[0];
-    const float D = reduction_sum ? 1.0f : static_cast<float>(n_valid > 0 ? n_valid : 1);
-    const float g = grad ? grad[0] : 1.0f;
+    const float D = (reduction != 0) ? 1.0f : static_cast<float>(n_valid > 0 ? n_valid : 1);
+    const float g = (grad && reduction != 2) ? grad[0] : 1.0f;
     ctrl->n_valid = n_valid;
     ctrl->n_invalid = s_bad[0];
     ctrl->scale_fwd = D;  // the loss is divided by D
@@ -219,9 +221,14 @@ __global__ __launch_bounds__(C::NT) void k_fwd_lse(FwdArgs<typename C::Elem> a) 
   }
 }
 
+// Per token: LSE from the split partials, the loss term
+// l = LSE - (1-eps) z_y - (eps/V) sum z + alpha LSE^2, and a fixed-order sum
+// per block of kLossBlock tokens.  tok_loss (reduction none) receives l, 0
+// for an ignored row and NaN for a label outside [0, V).
 __global__ __launch_bounds__(kLossBlock) void k_lse_merge(
     const floatx4* __restrict__ part, int splits, int64_t n_pad, const int32_t* __restrict__ labels,
-    int N, int V, int ignore, float eps, float* __restrict__ lse, float* __restrict__ blockloss) {
+    int N, int V, int ignore, float eps, float zloss, float* __restrict__ lse,
+    float* __restrict__ blockloss, float* __restrict__ tok_loss) {
   __shared__ float s_red[kLossBlock];
   const int tok = blockIdx.x * kLossBlock + threadIdx.x;
   float term = 0.0f;
@@ -237,8 +244,11 @@ __global__ __launch_bounds__(kLossBlock) void k_lse_merge(
       lse[tok] = L;
       term = L - (1.0f - eps) * st[2];
       if (eps != 0.0f) term -= (eps / static_cast<float>(V)) * st[3];
+      if (zloss != 0.0f) term += zloss * L * L;
+      if (tok_loss) tok_loss[tok] = term;
     } else {
       lse[tok] = NAN;
+      if (tok_loss) tok_loss[tok] = (y == ignore) ? 0.0f : NAN;
     }
   }
   s_red[threadIdx.x] = term;
@@ -279,7 +289,8 @@ struct DzArgs {
   const int32_t* labels;  // labels + tok0
   const float* lse;       // lse + tok0
   int ntok, nvoc, voc0, H, V, ignore;
-  float eps;
+  float eps, zloss;
+  const float* gtok;  // per-token upstream gradient (reduction none) + tok0, or NULL
   int voc_tiles, tok_tiles, group_m;
   T* dz;
   int64_t ldz;
@@ -323,6 +334,9 @@ __global__ __launch_bounds__(C::NT) void k_bwd_dz(DzArgs<typename C::Elem> a) {
     const bool valid = tl < a.ntok && label_ok(y, a.ignore, a.V);
     const float L = valid ? a.lse[tl] : 0.0f;
     const int yl = valid ? y - a.voc0 : -1;  // label as a block-local column
+    // d(alpha LSE^2)/dz = 2 alpha LSE p; reduction none scales the row by g_i
+    const float zf = 1.0f + 2.0f * a.zloss * L;
+    const float gi = (valid && a.gtok) ? a.gtok[tl] : 1.0f;
     T* row = a.dz + static_cast<int64_t>(tl) * a.ldz;
 #pragma unroll
     for (int fm = 0; fm < C::FM; ++fm) {
@@ -334,9 +348,9 @@ __global__ __launch_bounds__(C::NT) void k_bwd_dz(DzArgs<typename C::Elem> a) {
         for (int q = 0; q < 4; ++q) {
           const int v = v0 + q;
           const float z = acc.v[fm][fn][4 * g + q];
-          float p = hw_exp2((z - L) * kLog2e) - eps_v;
+          float p = hw_exp2((z - L) * kLog2e) * zf - eps_v;
           if (v == yl) p -= one_m_eps;
-          d[q] = (valid && v < a.nvoc) ? p : 0.0f;
+          d[q] = (valid && v < a.nvoc) ? p * gi : 0.0f;
         }
         store4(row + v0, d[0], d[1], d[2], d[3]);
       }
@@ -443,9 +457,12 @@ int cdiv_i(int64_t a, int64_t b) { return static_cast<int>((a + b - 1) / b); }
   } while (0)
 
 template <typename T>
-hipError_t run_forward(const Plan& p, const T* X, const T* W, const int32_t* labels, int ignore,
-                       float eps, float* loss, float* lse, char* ws, hipStream_t st,
+hipError_t run_forward(const Plan& p, const T* X, const T* W, const int32_t* labels,
+                       const LossOpts& o, float* loss, float* lse, char* ws, hipStream_t st,
                        KernelTimer* timer) {
+  const int ignore = o.ignore;
+  const float eps = o.eps;
+  const bool none = o.reduction == Reduction::None;
   typedef typename ShapeOf<T>::C C;
   Ctrl* ctrl = reinterpret_cast<Ctrl*>(ws + p.off_ctrl);
   float* blockloss = reinterpret_cast<float*>(ws + p.off_blockloss);
@@ -467,11 +484,13 @@ hipError_t run_forward(const Plan& p, const T* X, const T* W, const int32_t* lab
     FCE_CHECK_LAUNCH();
     timer->end(st);
     timer->begin("lse_merge", 0.0, st);
-    k_lse_merge<<<cdiv_i(N, kLossBlock), kLossBlock, 0, st>>>(part, fa.splits, p.n_pad, labels, N,
-                                                              V, ignore, eps, lse, blockloss);
+    k_lse_merge<<<cdiv_i(N, kLossBlock), kLossBlock, 0, st>>>(
+        part, fa.splits, p.n_pad, labels, N, V, ignore, eps, o.zloss, lse, blockloss,
+        none ? loss : nullptr);
     FCE_CHECK_LAUNCH();
     timer->end(st);
   }
+  if (none) return hipSuccess;  // the per-token losses are the output
   timer->begin("loss_final", 0.0, st);
   k_loss_final<<<1, 256, 0, st>>>(blockloss, N > 0 ? static_cast<int>(p.n_loss_blocks) : 0, ctrl,
                                   loss);
@@ -481,9 +500,11 @@ hipError_t run_forward(const Plan& p, const T* X, const T* W, const int32_t* lab
 }
 
 template <typename T>
-hipError_t run_backward(const Plan& p, const T* X, const T* W, const int32_t* labels, int ignore,
-                        float eps, const float* lse, float* dX, float* dW, char* ws,
-                        hipStream_t st, KernelTimer* timer) {
+hipError_t run_backward(const Plan& p, const T* X, const T* W, const int32_t* labels,
+                        const LossOpts& o, const float* lse, const float* grad_tok, float* dX,
+                        float* dW, char* ws, hipStream_t st, KernelTimer* timer) {
+  const int ignore = o.ignore;
+  const float eps = o.eps;
   typedef typename ShapeOf<T>::C C;
   const Ctrl* ctrl = reinterpret_cast<const Ctrl*>(ws + p.off_ctrl);
   const int32_t* flags = reinterpret_cast<const int32_t*>(ws + p.off_flags);
@@ -510,7 +531,8 @@ hipError_t run_backward(const Plan& p, const T* X, const T* W, const int32_t* la
 
       DzArgs<T> da{X + tok0 * H, W + voc0 * H, labels + tok0, lse + tok0, ntok, nvoc,
                    static_cast<int>(voc0), static_cast<int>(H), static_cast<int>(V), ignore, eps,
-                   voc_tiles, tok_tiles, 4, dz, p.ldz, flags + ia};
+                   o.zloss, grad_tok ? grad_tok + tok0 : nullptr, voc_tiles, tok_tiles, 4, dz,
+                   p.ldz, flags + ia};
       timer->begin("bwd_dz", blk_flops, st);
       if (H % 32 == 0)
         k_bwd_dz<C, true><<<voc_tiles * tok_tiles, C::NT, 0, st>>>(da);
@@ -565,13 +587,14 @@ hipError_t run_backward(const Plan& p, const T* X, const T* W, const int32_t* la
 
 }  // namespace
 
-hipError_t launch_label_scan(const Plan& p, const int32_t* labels, int ignore, int reduction_sum,
+hipError_t launch_label_scan(const Plan& p, const int32_t* labels, const LossOpts& o,
                              const float* grad, char* ws, hipStream_t st, KernelTimer* timer) {
   Ctrl* ctrl = reinterpret_cast<Ctrl*>(ws + p.off_ctrl);
   int32_t* flags = reinterpret_cast<int32_t*>(ws + p.off_flags);
   timer->begin("label_scan", 0.0, st);
-  k_label_scan<<<1, 1024, 0, st>>>(labels, static_cast<int>(p.N), static_cast<int>(p.V), ignore,
-                                   reduction_sum, grad, ctrl, flags, static_cast<int>(p.CN),
+  k_label_scan<<<1, 1024, 0, st>>>(labels, static_cast<int>(p.N), static_cast<int>(p.V), o.ignore,
+                                   static_cast<int>(o.reduction), grad, ctrl, flags,
+                                   static_cast<int>(p.CN),
                                    static_cast<int>(std::max<int64_t>(p.a, 1)));
   FCE_CHECK_LAUNCH();
   timer->end(st);
@@ -579,23 +602,23 @@ hipError_t launch_label_scan(const Plan& p, const int32_t* labels, int ignore, i
 }
 
 hipError_t launch_forward(const Plan& p, const void* X, const void* W, const int32_t* labels,
-                          int ignore, float eps, float* loss, float* lse, char* ws, hipStream_t st,
+                          const LossOpts& o, float* loss, float* lse, char* ws, hipStream_t st,
                           KernelTimer* timer) {
   if (p.dtype == Dtype::BF16)
     return run_forward<bf16>(p, static_cast<const bf16*>(X), static_cast<const bf16*>(W), labels,
-                             ignore, eps, loss, lse, ws, st, timer);
+                             o, loss, lse, ws, st, timer);
   return run_forward<float>(p, static_cast<const float*>(X), static_cast<const float*>(W), labels,
-                            ignore, eps, loss, lse, ws, st, timer);
+                            o, loss, lse, ws, st, timer);
 }
 
 hipError_t launch_backward(const Plan& p, const void* X, const void* W, const int32_t* labels,
-                           int ignore, float eps, const float* lse, float* dX, float* dW, char* ws,
-                           hipStream_t st, KernelTimer* timer) {
+                           const LossOpts& o, const float* lse, const float* grad_tok, float* dX,
+                           float* dW, char* ws, hipStream_t st, KernelTimer* timer) {
   if (p.dtype == Dtype::BF16)
     return run_backward<bf16>(p, static_cast<const bf16*>(X), static_cast<const bf16*>(W), labels,
-                              ignore, eps, lse, dX, dW, ws, st, timer);
+                              o, lse, grad_tok, dX, dW, ws, st, timer);
   return run_backward<float>(p, static_cast<const float*>(X), static_cast<const float*>(W), labels,
-                             ignore, eps, lse, dX, dW, ws, st, timer);
+                             o, lse, grad_tok, dX, dW, ws, st, timer);
 }
 
 }  // namespace fce

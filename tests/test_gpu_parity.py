@@ -199,6 +199,115 @@ def test_autograd_wrapper():
     assert rel_l2(Wr.grad.cpu().numpy(), ref.dW) <= 1e-5
 
 
+# ------------------------------------------- z-loss and reduction "none"
+def run_ex(inp, grad=None, split=True, **opts):
+    """The *_ex entry points; grad: per-token array for "none", scalar else."""
+    wl = inp.workload
+    X, W, y = wk.to_torch(inp, "cuda")
+    N, H, V = wl.N, wl.H, wl.V
+    opts.setdefault("label_smoothing", wl.label_smoothing)
+    code = fce.FCE_BF16 if X.dtype == torch.bfloat16 else fce.FCE_F32
+    ws = torch.empty(fce.fce_workspace_size_ex(N, H, V, code, **opts), dtype=torch.uint8,
+                     device="cuda")
+    none = opts.get("reduction", "mean") == "none"
+    loss = torch.full((N if none else 1,), float("nan"), device="cuda")
+    lse = torch.full((max(N, 1),), float("nan"), device="cuda")
+    dX = torch.full((max(N, 1), H), float("nan"), device="cuda")
+    dW = torch.full((V, H), float("nan"), device="cuda")
+    if split:
+        g = None if grad is None else torch.tensor(np.atleast_1d(grad), dtype=torch.float32,
+                                                   device="cuda")
+        fce.fce_forward_ex(X, W, y, loss, lse, ws, **opts)
+        fce.fce_backward_ex(X, W, y, lse, g, dX, dW, ws, **opts)
+    else:
+        fce.fce_fused_fwd_bwd_ex(X, W, y, loss, dX, dW, ws, **opts)
+    torch.cuda.synchronize()
+    return dict(loss=loss.cpu().numpy(), lse=lse[:N].cpu().numpy(), dX=dX[:N].cpu().numpy(),
+                dW=dW.cpu().numpy())
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+@pytest.mark.parametrize("reduction", ["mean", "sum", "none"])
+def test_zloss_and_reductions(dtype, reduction):
+    wl = wk.custom(700, 264 if dtype == "bf16" else 36, 5003, dtype, 0.05, "zipf", 1.1, 0.05, 0.1,
+                   seed=71)
+    inp = wk.draw(wl)
+    al = 1e-3
+    g = (np.random.default_rng(5).uniform(-2.0, 2.0, wl.N).astype(np.float32)
+         if reduction == "none" else 1.5)
+    got = run_ex(inp, grad=g, z_loss=al, reduction=reduction, chunk=200)
+    ref = orc.linear_cross_entropy(inp.X, inp.W, inp.labels, -100, wl.label_smoothing, reduction,
+                                   np.asarray(g, dtype=np.float64), z_loss=al)
+    tl, tg = TOL[dtype]
+    valid = inp.labels != -100
+    if reduction == "none":
+        err = np.abs(got["loss"] - ref.loss).max() / np.abs(ref.loss[valid]).mean()
+        assert np.all(got["loss"][~valid] == 0.0)
+    else:
+        err = abs(got["loss"][0] - ref.loss) / abs(ref.loss)
+    ex, ew = rel_l2(got["dX"], ref.dX), rel_l2(got["dW"], ref.dW)
+    print(f"[z-loss {al} {reduction} {dtype}] loss err {err:.2e}; dX {ex:.2e}; dW {ew:.2e}",
+          flush=True)
+    assert err <= tl and ex <= tg and ew <= tg
+    assert rel_l2(got["lse"][valid], ref.lse[valid]) <= tl
+    assert np.all(got["dX"][~valid] == 0.0)
+
+
+def test_fused_none_is_unit_gradient():
+    wl = wk.custom(520, 128, 3001, "bf16", 0.05, "uniform", ignore_frac=0.1, label_smoothing=0.05,
+                   seed=73)
+    inp = wk.draw(wl)
+    got = run_ex(inp, split=False, reduction="none", z_loss=1e-4, chunk=128)
+    ref = orc.linear_cross_entropy(inp.X, inp.W, inp.labels, -100, 0.05, "none", 1.0, z_loss=1e-4)
+    valid = inp.labels != -100
+    assert np.abs(got["loss"] - ref.loss).max() <= 2e-3 * np.abs(ref.loss[valid]).mean()
+    assert rel_l2(got["dX"], ref.dX) <= 2e-2 and rel_l2(got["dW"], ref.dW) <= 2e-2
+
+
+def test_ex_with_default_options_equals_plain_entry_points_bitwise():
+    wl = wk.custom(900, 256, 4000, "bf16", 0.03, "zipf", 1.1, 0.03, 0.1, seed=75)
+    inp = wk.draw(wl)
+    for red in ("mean", "sum"):
+        a = run(inp, chunk=300, reduction=red, split=True, grad=0.7)
+        b = run_ex(inp, grad=0.7, reduction=red, chunk=300)
+        assert a["loss"] == b["loss"][0]
+        assert np.array_equal(a["dX"], b["dX"]) and np.array_equal(a["dW"], b["dW"])
+        assert np.array_equal(a["lse"], b["lse"], equal_nan=True)
+
+
+def test_none_flags_invalid_labels_with_nan():
+    wl = wk.custom(200, 64, 500, "bf16", seed=77)
+    inp = wk.draw(wl)
+    inp.labels[[3, 50]] = [500, -7]  # outside [0, V), not ignore_index
+    got = run_ex(inp, reduction="none", chunk=64)
+    assert np.isnan(got["loss"][3]) and np.isnan(got["loss"][50])
+    ok = np.ones(wl.N, bool)
+    ok[[3, 50]] = False
+    assert np.isfinite(got["loss"][ok]).all()
+
+
+def test_full_size_zloss_none_sampled():
+    # 4096 x 2048 x 32000 with z-loss and per-token gradients, against the
+    # oracle on sampled rows of dX and dW and on every token's loss.
+    wl = wk.WORKLOADS[2]
+    inp = wk.draw(wl)
+    al = 1e-4
+    g = np.random.default_rng(9).uniform(-1.0, 1.0, wl.N).astype(np.float32)
+    got = run_ex(inp, grad=g, z_loss=al, reduction="none", chunk=1024)
+    loss, lse, _ = orc.forward(inp.X, inp.W, inp.labels, -100, wl.label_smoothing, "none",
+                               z_loss=al)
+    valid = inp.labels != -100
+    assert np.abs(got["loss"] - loss).max() <= 2e-3 * np.abs(loss[valid]).mean()
+    rows = np.random.default_rng(1).choice(wl.N, 64, replace=False)
+    dx, _, _ = orc.dX_rows(inp.X, inp.W, inp.labels, rows, -100, wl.label_smoothing, "none",
+                           g.astype(np.float64), z_loss=al)
+    assert rel_l2(got["dX"][rows], dx) <= 2e-2
+    vocab = np.random.default_rng(2).choice(wl.V, 64, replace=False)
+    dw = orc.dW_rows(inp.X, inp.W, inp.labels, lse, vocab, -100, wl.label_smoothing, "none",
+                     g.astype(np.float64), z_loss=al)
+    assert rel_l2(got["dW"][vocab], dw) <= 2e-2
+
+
 # ----------------------------------------------------- full-size workloads
 def _golden(k):
     path = os.path.join(GOLDEN, f"oracle_config{k}.npz")

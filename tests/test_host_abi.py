@@ -156,3 +156,53 @@ def test_token_schedule_scratch_is_one_chunk():
     assert p["scratch_bytes"] <= c["bytes"]
     rep = memory.report(c["N"], c["V"], 2, p["scratch_bytes"])
     assert math.isclose(rep["naive_3x_bytes"] / 1e9, 6.3, abs_tol=0.05)
+
+
+# ------------------------------------------------------------ options (*_ex)
+def _opts(**kw):
+    return B.make_options(**kw)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(z_loss=-1e-3), B.FCE_ERR_ARG), (dict(z_loss=float("nan")), B.FCE_ERR_ARG),
+    (dict(z_loss=float("inf")), B.FCE_ERR_ARG), (dict(reduction=3), B.FCE_ERR_ARG),
+    (dict(variant=1), B.FCE_ERR_ARG), (dict(chunk=0), B.FCE_ERR_ARG), (dict(schedule=5), B.FCE_ERR_ARG),
+    (dict(label_smoothing=1.0), B.FCE_ERR_ARG)])
+def test_ex_rejects_bad_options(kw, status):
+    lib = B.load_library()
+    o = _opts(**kw)
+    ws = lib.fce_workspace_size(64, 64, 100, 1, 16, 0)
+    assert lib.fce_forward_ex(FAKE, FAKE, FAKE, 64, 64, 100, 1, ctypes.byref(o), FAKE, FAKE, FAKE,
+                              ws, None) == status
+    assert lib.fce_fused_fwd_bwd_ex(FAKE, FAKE, FAKE, 64, 64, 100, 1, ctypes.byref(o), FAKE, FAKE,
+                                    FAKE, FAKE, ws, None) == status
+    assert lib.fce_workspace_size_ex(64, 64, 100, 1, ctypes.byref(o)) == 0
+
+
+def test_ex_null_options_and_none_on_old_entry_points():
+    lib = B.load_library()
+    ws = lib.fce_workspace_size(64, 64, 100, 1, 16, 0)
+    assert lib.fce_forward_ex(FAKE, FAKE, FAKE, 64, 64, 100, 1, None, FAKE, FAKE, FAKE, ws,
+                              None) == B.FCE_ERR_NULL
+    assert lib.fce_backward_ex(FAKE, FAKE, FAKE, 64, 64, 100, 1, None, FAKE, None, FAKE, FAKE, FAKE,
+                               ws, None) == B.FCE_ERR_NULL
+    assert lib.fce_workspace_size_ex(64, 64, 100, 1, None) == 0
+    # reduction none is for the *_ex entry points only
+    assert _fwd(red=B.FCE_NONE) == B.FCE_ERR_ARG
+
+
+@pytest.mark.parametrize("N,H,V,dtype,chunk,sched", [(8192, 4096, 128256, 1, 1024, 0),
+                                                     (777, 264, 5003, 1, 100, 1),
+                                                     (5000, 64, 300, 0, 7, 2)])
+def test_ex_workspace_matches_plain(N, H, V, dtype, chunk, sched):
+    lib = B.load_library()
+    for red in ("mean", "sum", "none"):
+        o = _opts(z_loss=1e-4, reduction=red, chunk=chunk, schedule=sched, label_smoothing=0.1)
+        assert lib.fce_workspace_size_ex(N, H, V, dtype, ctypes.byref(o)) == \
+            lib.fce_workspace_size(N, H, V, dtype, chunk, sched)
+
+
+def test_options_struct_layout():
+    # 32 bytes, chunk at offset 16 (include/fce.h)
+    assert ctypes.sizeof(B.Options) == 32
+    assert B.Options.chunk.offset == 16 and B.Options.variant.offset == 28
