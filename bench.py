@@ -156,12 +156,50 @@ def run_side(torch, fce, wk, args, side, X, W, y, loss, lse, dX, dW, ws, step, s
         log(f"  chunk {c} schedule {sc}: {t_c / k2:.3f} ms/step")
         del ws_c
     side["ms_per_step_by_chunk_schedule"] = sweep
+    side["ce_logits"] = ce_logits_side(torch, fce, wk, args, X, W, y, eps, stream)
     if not args.no_naive:
         try:
             side["naive_torch"] = naive_torch(torch, X, W, y, eps, min(k2, 5))
             log(f"  naive torch: {side['naive_torch']}")
         except torch.cuda.OutOfMemoryError as e:  # pragma: no cover
             side["naive_torch"] = {"error": str(e)[:200]}
+
+
+def ce_logits_side(torch, fce, wk, args, X, W, y, eps, stream):
+    """The loss on logits the caller holds (fce_ce_logits) on this workload's
+    own logits Z = X W^T (made by a torch GEMM outside the timed region):
+    dZ into another buffer, dZ over Z, and the loss alone.  HBM-bound; the
+    algorithmic bytes are one read of Z plus, with a gradient, one write."""
+    N, V = X.shape[0], W.shape[0]
+    Z = X @ W.t()
+    esz = Z.element_size()
+    dZ = torch.empty_like(Z)
+    loss = torch.empty(1, device="cuda")
+    lse = torch.empty(N, device="cuda")
+    ws = torch.empty(fce.fce_ce_logits_workspace_size(N), dtype=torch.uint8, device="cuda")
+    k2 = args.side_steps
+    res = {"what": f"loss on given {N}x{V} logits ({str(Z.dtype).split('.')[-1]}), "
+                   "one workgroup per row, two streaming passes", "peak_GBps": HBM_PEAK_GBS}
+    Zc = Z.clone()
+    modes = {"separate_dZ": (dZ, 2), "loss_only": (None, 1), "in_place_dZ": (Zc, 2)}
+    for name, (out, passes) in modes.items():
+        src = Zc if name == "in_place_dZ" else Z
+        fn = lambda: fce.fce_ce_logits(src, y, loss, lse, ws, dZ=out, ignore_index=wk.IGNORE_INDEX,
+                                       label_smoothing=eps)
+        fn()
+        fce.fce_timing_enable(True)
+        t, _ = time_steps(torch, fn, k2, stream)
+        kt = fce.fce_timing_read().get("ce_logits")
+        fce.fce_timing_enable(False)
+        kms = kt["total_ms"] / kt["launches"] if kt else t / k2
+        nbytes = passes * N * V * esz
+        gbps = nbytes / (kms / 1e3) / 1e9
+        res[name] = {"ms": round(kms, 4), "algorithmic_bytes": nbytes, "GBps": round(gbps, 1),
+                     "frac": round(gbps / HBM_PEAK_GBS, 4)}
+        log(f"  ce_logits {name}: {kms:.3f} ms, {gbps:.0f} GB/s ({100 * gbps / HBM_PEAK_GBS:.1f}%)")
+    del Z, Zc, dZ
+    torch.cuda.empty_cache()
+    return res
 
 
 def main():

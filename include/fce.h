@@ -196,6 +196,30 @@ fce_status fce_fused_fwd_bwd_ex(const void* X, const void* W, const int32_t* lab
                                 float* loss, float* dX, float* dW, void* workspace,
                                 size_t workspace_bytes, hipStream_t stream);
 
+/* ---- Loss on logits the caller holds ("Fused cross-entropy -- the memory
+ * kernel", lesson 27: "Trick 1" alone, the logit-space memory table's fused
+ * softmax+CE row, where probs and dlogits reuse the logits buffer).
+ *
+ * Z is DEVICE, row-major [N][ldz] with ldz >= V (elements), dtype FCE_BF16
+ * or FCE_F32, 16-byte aligned with ldz * element size a multiple of 16.
+ * Writes lse[N] and the loss (float[1], or float[N] for FCE_NONE) as in
+ * fce_forward_ex.  If dZ is not NULL it also writes
+ *   dZ_ij = (softmax_ij (1 + 2 alpha LSE_i) - (1-eps)[j = y_i] - eps/V) * s_i
+ * (s_i as in fce_backward_ex, from grad_loss: float[1] or float[N], or NULL
+ * for ones) in Z's dtype, row-major [N][lddz]; dZ may be Z itself (the
+ * gradient then overwrites the logits; lddz must equal ldz).  Columns
+ * V .. of a row's last 16-byte vector are written as 0 in dZ; columns
+ * past that are not touched.  Ignored rows get dZ = 0.  opt->chunk,
+ * opt->schedule and opt->variant are checked as elsewhere but unused.
+ * The workspace (fce_ce_logits_workspace_size) holds the label scan and
+ * per-row loss terms. */
+size_t fce_ce_logits_workspace_size(int64_t N);
+
+fce_status fce_ce_logits(const void* Z, int64_t ldz, const int32_t* labels, int64_t N, int64_t V,
+                         fce_dtype dtype, const fce_options* opt, float* loss, float* lse,
+                         void* dZ, int64_t lddz, const float* grad_loss, void* workspace,
+                         size_t workspace_bytes, hipStream_t stream);
+
 /* Static description of a status code. */
 const char* fce_status_string(fce_status status);
 

@@ -24,6 +24,8 @@ from ._binding import (  # noqa: F401
     REDUCTIONS,
     fce_backward,
     fce_backward_ex,
+    fce_ce_logits,
+    fce_ce_logits_workspace_size,
     fce_forward,
     fce_forward_ex,
     fce_fused_fwd_bwd,

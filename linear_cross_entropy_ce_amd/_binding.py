@@ -35,6 +35,7 @@ REDUCTIONS = {"mean": FCE_MEAN, "sum": FCE_SUM, "none": FCE_NONE}
 
 EXPORTED = ("fce_workspace_size", "fce_plan", "fce_forward", "fce_backward", "fce_fused_fwd_bwd",
             "fce_workspace_size_ex", "fce_forward_ex", "fce_backward_ex", "fce_fused_fwd_bwd_ex",
+            "fce_ce_logits_workspace_size", "fce_ce_logits",
             "fce_get_label_errors", "fce_status_string", "fce_last_hip_error",
             "fce_timing_enable", "fce_timing_read")
 
@@ -120,6 +121,10 @@ def load_library(path: str = LIB_PATH):
     lib.fce_backward_ex.argtypes = common_ex + [vp, vp, vp, vp, vp, u64, vp]
     lib.fce_fused_fwd_bwd_ex.restype = i32
     lib.fce_fused_fwd_bwd_ex.argtypes = common_ex + [vp, vp, vp, vp, u64, vp]
+    lib.fce_ce_logits_workspace_size.restype = u64
+    lib.fce_ce_logits_workspace_size.argtypes = [i64]
+    lib.fce_ce_logits.restype = i32
+    lib.fce_ce_logits.argtypes = [vp, i64, vp, i64, i64, i32, op, vp, vp, vp, i64, vp, vp, u64, vp]
     lib.fce_get_label_errors.restype = i32
     lib.fce_get_label_errors.argtypes = [vp, ctypes.POINTER(i32), vp]
     lib.fce_status_string.restype = ctypes.c_char_p
@@ -245,6 +250,24 @@ def fce_fused_fwd_bwd_ex(X, W, labels, loss, dX, dW, workspace, stream=None, **o
                                              _ptr(loss), _ptr(dX), _ptr(dW), *_ws(workspace),
                                              _stream(stream))
     _check(st, "fce_fused_fwd_bwd_ex")
+
+
+def fce_ce_logits_workspace_size(N) -> int:
+    return int(load_library().fce_ce_logits_workspace_size(N))
+
+
+def fce_ce_logits(Z, labels, loss, lse, workspace, dZ=None, grad_loss=None, V=None, stream=None,
+                  **options):
+    """Loss (and dZ, which may be Z) on given logits Z [N, ldz]; V defaults
+    to Z's row length."""
+    o = make_options(**options)
+    N, ldz = Z.shape
+    V = ldz if V is None else V
+    lddz = dZ.shape[1] if dZ is not None else 0
+    st = load_library().fce_ce_logits(_ptr(Z), ldz, _ptr(labels), N, V, _dtype_code(Z),
+                                      ctypes.byref(o), _ptr(loss), _ptr(lse), _ptr(dZ), lddz,
+                                      _ptr(grad_loss), *_ws(workspace), _stream(stream))
+    _check(st, "fce_ce_logits")
 
 
 def fce_get_label_errors(workspace, stream=None) -> int:

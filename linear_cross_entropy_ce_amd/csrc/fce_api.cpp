@@ -317,6 +317,48 @@ fce_status fce_fused_fwd_bwd_ex(const void* X, const void* W, const int32_t* lab
                     workspace_bytes, stream);
 }
 
+size_t fce_ce_logits_workspace_size(int64_t N) {
+  if (N < 0) return 0;
+  return fce::ce_workspace_bytes(N);
+}
+
+fce_status fce_ce_logits(const void* Z, int64_t ldz, const int32_t* labels, int64_t N, int64_t V,
+                         fce_dtype dtype, const fce_options* opt, float* loss, float* lse,
+                         void* dZ, int64_t lddz, const float* grad_loss, void* workspace,
+                         size_t workspace_bytes, hipStream_t stream) {
+  if (N < 0 || V < 1 || N >= (int64_t{1} << 31) || V >= (int64_t{1} << 30)) return FCE_ERR_SHAPE;
+  if (workspace == nullptr) return FCE_ERR_NULL;
+  if (N > 0 && (Z == nullptr || labels == nullptr || lse == nullptr)) return FCE_ERR_NULL;
+  if (dtype != FCE_F32 && dtype != FCE_BF16) return FCE_ERR_ARG;
+  fce::LossOpts lo;
+  if (fce_status s = check_options(opt, true, &lo); s != FCE_OK) return s;
+  const bool none = lo.reduction == fce::Reduction::None;
+  if (loss == nullptr && !(none && N == 0)) return FCE_ERR_NULL;
+  const int64_t es = (dtype == FCE_BF16) ? 2 : 4;
+  if (ldz < V || (dZ != nullptr && lddz < V)) return FCE_ERR_SHAPE;
+  if (dZ == Z && lddz != ldz) return FCE_ERR_ARG;
+  if ((ldz * es) % 16 != 0 || (dZ != nullptr && (lddz * es) % 16 != 0)) return FCE_ERR_ALIGN;
+  if ((N > 0 && !aligned16(Z)) || (dZ != nullptr && !aligned16(dZ)) || !aligned16(workspace))
+    return FCE_ERR_ALIGN;
+  if (workspace_bytes < fce::ce_workspace_bytes(N)) return FCE_ERR_WORKSPACE;
+  if (fce_status s = check_device(); s != FCE_OK) return s;
+  fce::CeLogitsCall c;
+  c.Z = Z;
+  c.ldz = ldz;
+  c.dZ = dZ;
+  c.lddz = dZ ? lddz : 0;
+  c.labels = labels;
+  c.N = N;
+  c.V = V;
+  c.bf16 = dtype == FCE_BF16;
+  c.o = lo;
+  c.grad = grad_loss;
+  c.loss = loss;
+  c.lse = lse;
+  c.ws = static_cast<char*>(workspace);
+  return from_hip(fce::launch_ce_logits(c, stream, timer()));
+}
+
 fce_status fce_get_label_errors(const void* workspace, int32_t* host_count, hipStream_t stream) {
   if (workspace == nullptr || host_count == nullptr) return FCE_ERR_NULL;
   const fce::Ctrl* ctrl = static_cast<const fce::Ctrl*>(workspace);

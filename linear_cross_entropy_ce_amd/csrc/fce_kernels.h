@@ -41,4 +41,28 @@ hipError_t launch_backward(const Plan& p, const void* X, const void* W, const in
                            const LossOpts& o, const float* lse, const float* grad_tok, float* dX,
                            float* dW, char* ws, hipStream_t st, KernelTimer* timer);
 
+// Loss (and optionally dZ) on logits the caller holds.  Workspace layout:
+// Ctrl, one flag word, then N per-row loss terms (each 256-byte aligned).
+constexpr size_t ce_off_ctrl() { return 0; }
+constexpr size_t ce_off_flags() { return 256; }
+constexpr size_t ce_off_rowloss() { return 512; }
+inline size_t ce_workspace_bytes(int64_t N) {
+  return ce_off_rowloss() + ((static_cast<size_t>(std::max<int64_t>(N, 1)) * 4 + 255) / 256) * 256;
+}
+struct CeLogitsCall {
+  const void* Z;
+  int64_t ldz;
+  void* dZ;  // may equal Z, or NULL
+  int64_t lddz;
+  const int32_t* labels;
+  int64_t N, V;
+  bool bf16;
+  LossOpts o;
+  const float* grad;  // scalar (mean / sum) or per-token (none), or NULL
+  float* loss;        // [1] or [N] (none)
+  float* lse;         // [N]
+  char* ws;
+};
+hipError_t launch_ce_logits(const CeLogitsCall& c, hipStream_t st, KernelTimer* timer);
+
 }  // namespace fce

@@ -436,6 +436,189 @@ __global__ __launch_bounds__(C::NT) void k_bwd_grad(GradArgs<typename C::Elem> a
   }
 }
 
+// ------------------------------------------- loss on given logits
+// The pages' "Trick 1" path ("Fused cross-entropy -- the memory kernel",
+// logit-space memory table: probs and dlogits reuse the logits buffer): for
+// logits Z the caller holds, one workgroup per row computes
+// LSE = m + log sum exp(z - m), the loss term and, if asked, dZ, written
+// over Z or into another buffer.  HBM-bound: the row is streamed twice, the
+// first time for (max, sum-exp, sum z), the second time for dZ; with one row
+// per CU in flight the second read is served from L2 or the MALL.
+constexpr int kCeThreads = 1024;
+constexpr int kCeUnroll = 4;  // 16-byte loads in flight per thread
+
+template <typename T>
+struct CeVec;
+template <>
+struct CeVec<bf16> {
+  static constexpr int E = 8;  // elements per 16-byte vector
+  __device__ __forceinline__ static void unpack(const u32x4& r, float (&f)[E]) {
+    const bf16x8 v = __builtin_bit_cast(bf16x8, r);
+#pragma unroll
+    for (int e = 0; e < E; ++e) f[e] = static_cast<float>(v[e]);
+  }
+  __device__ __forceinline__ static u32x4 pack(const float (&f)[E]) {  // round to nearest even
+    typedef bf16 bf16x2 __attribute__((ext_vector_type(2)));
+    u32x4 r;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const bf16x2 h = {static_cast<bf16>(f[2 * i]), static_cast<bf16>(f[2 * i + 1])};
+      r[i] = __builtin_bit_cast(uint32_t, h);
+    }
+    return r;
+  }
+};
+template <>
+struct CeVec<float> {
+  static constexpr int E = 4;
+  __device__ __forceinline__ static void unpack(const u32x4& r, float (&f)[E]) {
+    const floatx4 v = __builtin_bit_cast(floatx4, r);  // (whole-vector cast)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) f[i] = v[i];
+  }
+  __device__ __forceinline__ static u32x4 pack(const float (&f)[E]) {
+    const floatx4 v = {f[0], f[1], f[2], f[3]};
+    return __builtin_bit_cast(u32x4, v);
+  }
+};
+
+struct CeArgs {
+  const void* Z;
+  int64_t ldz;  // elements
+  void* dZ;     // may equal Z; NULL: no gradient
+  int64_t lddz;
+  const int32_t* labels;
+  int N, V, ignore, reduction;  // reduction: 0 mean, 1 sum, 2 none
+  float eps, zloss;
+  const float* grad;  // per-token upstream gradient (none), or NULL
+  const Ctrl* ctrl;   // scale_bwd = g / D (mean, sum)
+  float* lse;
+  float* rowloss;  // per-row loss terms
+};
+
+template <typename T>
+__global__ __launch_bounds__(kCeThreads) void k_ce_logits(CeArgs a) {
+  typedef CeVec<T> CV;
+  constexpr int E = CV::E;
+  __shared__ floatx4 s_part[kCeThreads / 64];
+  __shared__ float s_bcast[1];
+  const int row = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int y = a.labels[row];
+  const bool valid = label_ok(y, a.ignore, a.V);
+  const int nv = (a.V + E - 1) / E;  // 16-byte vectors per row
+  const T* zrow = static_cast<const T*>(a.Z) + row * a.ldz;
+  T* drow = a.dZ ? static_cast<T*>(a.dZ) + row * a.lddz : nullptr;
+  // Loads past the row's vectors return zeros and stores there are dropped:
+  // the descriptors cover exactly the row's nv vectors.
+  const __amdgpu_buffer_rsrc_t rz = make_rsrc(zrow, static_cast<int64_t>(nv) * 16);
+  const __amdgpu_buffer_rsrc_t rd = make_rsrc(drow, drow ? static_cast<int64_t>(nv) * 16 : 0);
+  // Elements past V (only in vector nv-1, or in whole vectors past the row)
+  // become -inf for the max and the exponentials, are left out of the logit
+  // sum, and get a dZ of 0.
+  auto pad = [](float (&f)[E], int lim, float v) {
+#pragma unroll
+    for (int e = 0; e < E; ++e) f[e] = (e < lim) ? f[e] : v;
+  };
+  if (!valid) {  // ignored (or invalid) label: no loss, zero gradient row
+    if (tid == 0) {
+      a.lse[row] = NAN;
+      a.rowloss[row] = (y == a.ignore || a.reduction != 2) ? 0.0f : NAN;
+    }
+    if (drow)
+      for (int j = tid; j < nv; j += kCeThreads)
+        __builtin_amdgcn_raw_buffer_store_b128(u32x4{0u, 0u, 0u, 0u}, rd, j * 16, 0, 0);
+    return;
+  }
+
+  // pass 1: running (max, sum-exp, sum z) of this thread's vectors
+  float m = -INFINITY, l = 0.0f, zs = 0.0f;
+  const bool smooth = a.eps != 0.0f;
+  for (int j0 = tid; j0 < nv; j0 += kCeUnroll * kCeThreads) {
+    u32x4 r[kCeUnroll];
+#pragma unroll
+    for (int u = 0; u < kCeUnroll; ++u) r[u] = buf_load16(rz, (j0 + u * kCeThreads) * 16);
+#pragma unroll
+    for (int u = 0; u < kCeUnroll; ++u) {
+      float f[E];
+      CV::unpack(r[u], f);
+      const int lim = a.V - (j0 + u * kCeThreads) * E;
+      if (lim < E) {
+        if (smooth) {
+#pragma unroll
+          for (int e = 0; e < E; ++e) zs += (e < lim) ? f[e] : 0.0f;
+        }
+        pad(f, lim, -INFINITY);
+      } else if (smooth) {
+#pragma unroll
+        for (int e = 0; e < E; ++e) zs += f[e];
+      }
+      float vm = f[0];
+#pragma unroll
+      for (int e = 1; e < E; ++e) vm = fmaxf(vm, f[e]);
+      if (vm == -INFINITY) continue;
+      const float mn = fmaxf(m, vm);
+      const float mnl = mn * kLog2e;
+      float acc = 0.0f;
+#pragma unroll
+      for (int e = 0; e < E; ++e) acc += hw_exp2(fmaf(f[e], kLog2e, -mnl));
+      l = ((m == -INFINITY) ? 0.0f : l * hw_exp2((m - mn) * kLog2e)) + acc;
+      m = mn;
+    }
+  }
+  // wave, then fixed-order workgroup merge of (m, l, sum z)
+#pragma unroll
+  for (int sh = 32; sh > 0; sh >>= 1) {
+    float t0 = 0.0f;
+    const float m2 = __shfl_xor(m, sh), l2 = __shfl_xor(l, sh), z2 = __shfl_xor(zs, sh);
+    lse_merge(m, l, t0, zs, m2, l2, 0.0f, z2);
+  }
+  if (lane == 0) s_part[wave] = floatx4{m, l, 0.0f, zs};
+  __syncthreads();
+  if (tid == 0) {
+    floatx4 st = s_part[0];
+    for (int w = 1; w < kCeThreads / 64; ++w) lse_merge(st, s_part[w]);
+    const float L = st[0] + hw_log2(st[1]) * kLn2;
+    const float zy = static_cast<float>(zrow[y]);  // the target logit
+    float term = L - (1.0f - a.eps) * zy;
+    if (smooth) term -= (a.eps / static_cast<float>(a.V)) * st[3];
+    if (a.zloss != 0.0f) term += a.zloss * L * L;
+    a.lse[row] = L;
+    a.rowloss[row] = term;
+    s_bcast[0] = L;
+  }
+  if (!drow) return;
+  __syncthreads();
+
+  // pass 2: dZ = (p (1 + 2 alpha L) - eps/V - (1-eps)[i = y]) * scale, p = exp(z - L)
+  const float L = s_bcast[0];
+  const float scale = (a.reduction == 2) ? (a.grad ? a.grad[row] : 1.0f) : a.ctrl->scale_bwd;
+  const float ga = (1.0f + 2.0f * a.zloss * L) * scale;
+  const float gb = (a.eps / static_cast<float>(a.V)) * scale;
+  const float gy = (1.0f - a.eps) * scale;
+  const float Ll = L * kLog2e;
+  const int jy = y / E, ey = y % E;
+  for (int j0 = tid; j0 < nv; j0 += kCeUnroll * kCeThreads) {
+    u32x4 r[kCeUnroll];
+#pragma unroll
+    for (int u = 0; u < kCeUnroll; ++u) r[u] = buf_load16(rz, (j0 + u * kCeThreads) * 16);
+#pragma unroll
+    for (int u = 0; u < kCeUnroll; ++u) {
+      const int j = j0 + u * kCeThreads;
+      float f[E];
+      CV::unpack(r[u], f);
+#pragma unroll
+      for (int e = 0; e < E; ++e) f[e] = fmaf(hw_exp2(fmaf(f[e], kLog2e, -Ll)), ga, -gb);
+      if (j == jy) {  // the one lane holding the label
+#pragma unroll
+        for (int e = 0; e < E; ++e) f[e] -= (e == ey) ? gy : 0.0f;
+      }
+      const int lim = a.V - j * E;
+      if (lim < E) pad(f, lim, 0.0f);
+      __builtin_amdgcn_raw_buffer_store_b128(CV::pack(f), rd, j * 16, 0, 0);
+    }
+  }
+}
+
 // ------------------------------------------------------------- launching
 template <typename T>
 struct ShapeOf;
@@ -619,6 +802,37 @@ hipError_t launch_backward(const Plan& p, const void* X, const void* W, const in
                               o, lse, grad_tok, dX, dW, ws, st, timer);
   return run_backward<float>(p, static_cast<const float*>(X), static_cast<const float*>(W), labels,
                              o, lse, grad_tok, dX, dW, ws, st, timer);
+}
+
+hipError_t launch_ce_logits(const CeLogitsCall& c, hipStream_t st, KernelTimer* timer) {
+  Ctrl* ctrl = reinterpret_cast<Ctrl*>(c.ws + ce_off_ctrl());
+  int32_t* flags = reinterpret_cast<int32_t*>(c.ws + ce_off_flags());
+  float* rowloss = reinterpret_cast<float*>(c.ws + ce_off_rowloss());
+  const int N = static_cast<int>(c.N), V = static_cast<int>(c.V);
+  const bool none = c.o.reduction == Reduction::None;
+  timer->begin("label_scan", 0.0, st);
+  k_label_scan<<<1, 1024, 0, st>>>(c.labels, N, V, c.o.ignore, static_cast<int>(c.o.reduction),
+                                   none ? nullptr : c.grad, ctrl, flags, std::max(N, 1), 1);
+  FCE_CHECK_LAUNCH();
+  timer->end(st);
+  if (N > 0) {
+    CeArgs a{c.Z, c.ldz, c.dZ, c.lddz, c.labels, N, V, c.o.ignore,
+             static_cast<int>(c.o.reduction), c.o.eps, c.o.zloss, none ? c.grad : nullptr,
+             ctrl, c.lse, none ? c.loss : rowloss};
+    timer->begin("ce_logits", 0.0, st);
+    if (c.bf16)
+      k_ce_logits<bf16><<<N, kCeThreads, 0, st>>>(a);
+    else
+      k_ce_logits<float><<<N, kCeThreads, 0, st>>>(a);
+    FCE_CHECK_LAUNCH();
+    timer->end(st);
+  }
+  if (none) return hipSuccess;
+  timer->begin("loss_final", 0.0, st);
+  k_loss_final<<<1, 256, 0, st>>>(rowloss, N, ctrl, c.loss);
+  FCE_CHECK_LAUNCH();
+  timer->end(st);
+  return hipSuccess;
 }
 
 }  // namespace fce

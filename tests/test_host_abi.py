@@ -206,3 +206,24 @@ def test_options_struct_layout():
     # 32 bytes, chunk at offset 16 (include/fce.h)
     assert ctypes.sizeof(B.Options) == 32
     assert B.Options.chunk.offset == 16 and B.Options.variant.offset == 28
+
+
+def test_ce_logits_rejects_bad_arguments():
+    lib = B.load_library()
+    o = _opts()
+    ws = lib.fce_ce_logits_workspace_size(64)
+    f = lambda **k: lib.fce_ce_logits(
+        k.get("Z", FAKE), k.get("ldz", 104), k.get("labels", FAKE), k.get("N", 64),
+        k.get("V", 100), k.get("dtype", 1), ctypes.byref(k.get("o", o)), k.get("loss", FAKE),
+        k.get("lse", FAKE), k.get("dZ", None), k.get("lddz", 0), None, k.get("ws", FAKE),
+        k.get("ws_bytes", ws), None)
+    assert f(ldz=99) == B.FCE_ERR_SHAPE          # ldz < V
+    assert f(ldz=100) == B.FCE_ERR_ALIGN         # 200-byte rows are not 16-byte multiples
+    assert f(Z=FAKE + 2) == B.FCE_ERR_ALIGN
+    assert f(Z=None) == B.FCE_ERR_NULL and f(lse=None) == B.FCE_ERR_NULL
+    assert f(ws_bytes=ws - 1) == B.FCE_ERR_WORKSPACE
+    assert f(dZ=FAKE, lddz=96) == B.FCE_ERR_SHAPE
+    assert f(dZ=FAKE, lddz=112, Z=FAKE) == B.FCE_ERR_ARG  # in place needs lddz == ldz
+    assert f(o=_opts(z_loss=-1.0)) == B.FCE_ERR_ARG
+    assert f(dtype=3) == B.FCE_ERR_ARG
+    assert lib.fce_ce_logits_workspace_size(-1) == 0

@@ -49,3 +49,17 @@ def test_zipf_head_mass():
     r = wk._zipf_ranks(g, 200_000, 128256, 1.1)
     frac = (r == 0).mean()
     assert abs(frac - 0.13334) < 4 * np.sqrt(0.1333 * 0.8667 / 200_000)
+
+
+def test_draw_logits_deterministic_labels_and_scale():
+    # the logits of the loss-on-logits path: seeded, the same labels as draw(),
+    # N(0, (w_sigma sqrt H)^2) -- the spread of x.w for unit x and W of sd w_sigma
+    wl = wk.custom(600, 256, 3001, "bf16", 0.02, "zipf", 1.1, 0.05, 0.0, seed=21)
+    a, b = wk.draw_logits(wl), wk.draw_logits(wl)
+    assert a.digest() == b.digest()
+    assert np.array_equal(a.labels, wk.draw(wl).labels)
+    assert np.array_equal(wk.bf16_bits_to_f32(a.Z_bits), a.Z)
+    sd = 0.02 * np.sqrt(256)
+    assert abs(a.Z.std() / sd - 1.0) < 0.01 and abs(a.Z.mean()) < 0.01 * sd
+    f = wk.draw_logits(wk.custom(600, 256, 3001, "fp32", 0.02, seed=21))
+    assert f.Z_bits is None and f.Z.dtype == np.float32

@@ -23,6 +23,10 @@ Recipe (every array is a pure function of the workload's seed):
     permutation of the vocabulary.
   * Exactly round(p * N) positions, drawn without replacement, are set to
     ``ignore_index`` (-100).
+  * ``draw_logits`` (inputs of the loss on given logits): the same labels,
+    and logits Z[N,V] ~ N(0, (sigma sqrt(H))^2) -- the scale X W^T has for
+    this workload -- from a sixth spawned stream, in slabs of 256 rows,
+    rounded to bfloat16 like X and W.
 """
 from __future__ import annotations
 
@@ -153,12 +157,7 @@ def _zipf_ranks(g: np.random.Generator, n: int, V: int, s: float) -> np.ndarray:
     return np.minimum(r, V - 1)
 
 
-def draw(wl: Workload) -> Inputs:
-    """Draw the inputs of a workload (deterministic in ``wl.seed``)."""
-    s_x, s_w, s_lab, s_perm, s_ign = np.random.SeedSequence(wl.seed).spawn(5)
-    X = _normal_matrix(s_x, wl.N, wl.H, 1.0)
-    W = _normal_matrix(s_w, wl.V, wl.H, wl.w_sigma)
-
+def _labels(wl: Workload, s_lab, s_perm, s_ign) -> np.ndarray:
     g_lab = np.random.Generator(np.random.PCG64(s_lab))
     if wl.label_dist == "uniform":
         labels = g_lab.integers(0, wl.V, size=wl.N, dtype=np.int64)
@@ -174,6 +173,15 @@ def draw(wl: Workload) -> Inputs:
     if k > 0:
         pos = np.random.Generator(np.random.PCG64(s_ign)).choice(wl.N, size=k, replace=False)
         labels[pos] = IGNORE_INDEX
+    return labels
+
+
+def draw(wl: Workload) -> Inputs:
+    """Draw the inputs of a workload (deterministic in ``wl.seed``)."""
+    s_x, s_w, s_lab, s_perm, s_ign = np.random.SeedSequence(wl.seed).spawn(5)
+    X = _normal_matrix(s_x, wl.N, wl.H, 1.0)
+    W = _normal_matrix(s_w, wl.V, wl.H, wl.w_sigma)
+    labels = _labels(wl, s_lab, s_perm, s_ign)
 
     X_bits = W_bits = None
     if wl.dtype == "bf16":
@@ -184,6 +192,67 @@ def draw(wl: Workload) -> Inputs:
     elif wl.dtype != "fp32":
         raise ValueError(f"unknown dtype {wl.dtype!r}")
     return Inputs(wl, X, W, labels, X_bits, W_bits)
+
+
+@dataclasses.dataclass
+class LogitInputs:
+    """Inputs of the loss on given logits: Z holds the stored values as
+    float32; Z_bits the bfloat16 bit patterns for bf16 workloads."""
+
+    workload: Workload
+    Z: np.ndarray
+    labels: np.ndarray
+    Z_bits: np.ndarray | None
+
+    def digest(self) -> str:
+        h = hashlib.sha256()
+        for a in (self.Z, self.labels):
+            h.update(np.ascontiguousarray(a).tobytes())
+        return h.hexdigest()
+
+
+def draw_logits(wl: Workload) -> LogitInputs:
+    """Logits and labels for the loss on given logits (deterministic in
+    ``wl.seed``; the labels equal those of :func:`draw`)."""
+    s_x, s_w, s_lab, s_perm, s_ign, s_z = np.random.SeedSequence(wl.seed).spawn(6)
+    labels = _labels(wl, s_lab, s_perm, s_ign)
+    sigma = float(wl.w_sigma) * float(np.sqrt(wl.H))
+    Z = np.empty((wl.N, wl.V), dtype=np.float32)
+    rows = 256
+    children = s_z.spawn(max(1, -(-wl.N // rows)))
+
+    def fill(i):
+        r0, r1 = i * rows, min(wl.N, (i + 1) * rows)
+        g = np.random.Generator(np.random.PCG64(children[i]))
+        view = Z[r0:r1]
+        g.standard_normal(out=view, dtype=np.float32)
+        np.multiply(view, np.float32(sigma), out=view)
+
+    with ThreadPoolExecutor(_threads()) as ex:
+        list(ex.map(fill, range(len(children))))
+    Z_bits = None
+    if wl.dtype == "bf16":
+        Z_bits = np.empty(Z.shape, dtype=np.uint16)
+
+        def conv(i):
+            r0, r1 = i * rows, min(wl.N, (i + 1) * rows)
+            Z_bits[r0:r1] = round_to_bf16_bits(Z[r0:r1])
+            Z[r0:r1] = bf16_bits_to_f32(Z_bits[r0:r1])
+
+        with ThreadPoolExecutor(_threads()) as ex:
+            list(ex.map(conv, range(len(children))))
+    return LogitInputs(wl, Z, labels, Z_bits)
+
+
+def logits_to_torch(inp: LogitInputs, device="cuda"):
+    """Z as a torch tensor of the workload dtype and int32 labels, on ``device``."""
+    import torch
+
+    if inp.workload.dtype == "bf16":
+        Z = torch.from_numpy(inp.Z_bits.view(np.int16)).view(torch.bfloat16)
+    else:
+        Z = torch.from_numpy(inp.Z)
+    return Z.to(device), torch.from_numpy(inp.labels).to(device)
 
 
 def to_torch(inp: Inputs, device="cuda"):
