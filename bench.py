@@ -156,6 +156,8 @@ def run_side(torch, fce, wk, args, side, X, W, y, loss, lse, dX, dW, ws, step, s
         log(f"  chunk {c} schedule {sc}: {t_c / k2:.3f} ms/step")
         del ws_c
     side["ms_per_step_by_chunk_schedule"] = sweep
+    side["store_logits"] = store_logits_side(torch, fce, wk, args, X, W, y, loss, dX, dW, eps,
+                                             stream)
     side["ce_logits"] = ce_logits_side(torch, fce, wk, args, X, W, y, eps, stream)
     if not args.no_naive:
         try:
@@ -163,6 +165,38 @@ def run_side(torch, fce, wk, args, side, X, W, y, loss, lse, dX, dW, ws, step, s
             log(f"  naive torch: {side['naive_torch']}")
         except torch.cuda.OutOfMemoryError as e:  # pragma: no cover
             side["naive_torch"] = {"error": str(e)[:200]}
+
+
+def store_logits_side(torch, fce, wk, args, X, W, y, loss, dX, dW, eps, stream):
+    """The store-logits variant of the fused step (each chunk's logits kept
+    in the workspace and overwritten by dZ; 6NVH executed FLOPs) at two chunk
+    sizes: the whole batch in one chunk, and the default chunk."""
+    N, H = X.shape
+    V = W.shape[0]
+    k2 = args.side_steps
+    res = {"what": "store-logits fused step: executed FLOPs 6NVH (no recompute); tokens/s "
+                   "comparable with the headline, TFLOP/s counted on 6NVH"}
+    for chunk in sorted({N, args.chunk}, reverse=True):
+        opts = dict(ignore_index=wk.IGNORE_INDEX, label_smoothing=eps, chunk=chunk,
+                    variant="store_logits")
+        ws = fce.workspace_for(N, H, V, X.dtype, **opts)
+        fn = lambda: fce.fce_fused_fwd_bwd_ex(X, W, y, loss, dX, dW, ws, **opts)
+        fn()
+        fce.fce_timing_enable(True)
+        t, per = time_steps(torch, fn, k2, stream)
+        kern = fce.fce_timing_read()
+        fce.fce_timing_enable(False)
+        ms = t / k2
+        res[f"chunk_{chunk}"] = {
+            "ms_per_step": round(ms, 4), "tokens_per_s": round(N / (ms / 1e3), 1),
+            "tflops_6NVH": round(6.0 * N * V * H / (ms / 1e3) / 1e12, 1),
+            "workspace_bytes": int(ws.numel()),
+            "kernels_ms_per_step": {k: round(r["total_ms"] / k2, 4) for k, r in kern.items()}}
+        log(f"  store-logits chunk {chunk}: {ms:.3f} ms/step, workspace {ws.numel() / 1e9:.2f} GB, "
+            f"{res[f'chunk_{chunk}']['kernels_ms_per_step']}")
+        del ws
+        torch.cuda.empty_cache()
+    return res
 
 
 def ce_logits_side(torch, fce, wk, args, X, W, y, eps, stream):

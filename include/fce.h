@@ -87,6 +87,16 @@ typedef enum { FCE_F32 = 0, FCE_BF16 = 1 } fce_dtype;
 /* FCE_NONE (per-token losses) is accepted by the *_ex entry points only. */
 typedef enum { FCE_MEAN = 0, FCE_SUM = 1, FCE_NONE = 2 } fce_reduction;
 typedef enum { FCE_SCHED_AUTO = 0, FCE_SCHED_TOKEN = 1, FCE_SCHED_VOCAB = 2 } fce_schedule;
+/* How the backward gets its logits (fce_options.variant).
+ * FCE_VARIANT_RECOMPUTE: rebuild each logit block from X and W (8NVH FLOPs
+ *   per forward + backward; lesson 27, "Trick 2").
+ * FCE_VARIANT_STORE_LOGITS: fce_fused_fwd_bwd_ex only.  The forward keeps each
+ *   chunk's logits, [C][V rounded up to the tile] in the dtype of X, in the
+ *   workspace, and the backward overwrites them in place with dZ (6NVH FLOPs;
+ *   llms.blog, "LinkedIn Liger Kernel").  C is `chunk` rounded up to 256
+ *   tokens; the logit buffer is C x V elements, and dW is re-read once per
+ *   chunk after the first. */
+typedef enum { FCE_VARIANT_RECOMPUTE = 0, FCE_VARIANT_STORE_LOGITS = 1 } fce_variant;
 
 /* The backward schedule chosen for a problem (host-only, no GPU needed). */
 typedef struct {
@@ -111,7 +121,7 @@ typedef struct {
   int32_t reduction;      /* fce_reduction: FCE_MEAN, FCE_SUM or FCE_NONE               */
   int64_t chunk;          /* logit-space budget, chunk x V elements (>= 1)              */
   int32_t schedule;       /* fce_schedule                                               */
-  int32_t variant;        /* reserved: must be 0                                         */
+  int32_t variant;        /* fce_variant; FCE_VARIANT_STORE_LOGITS only where stated    */
 } fce_options;
 
 /* Size in bytes of the workspace the three compute entry points need for
@@ -166,8 +176,9 @@ fce_status fce_get_label_errors(const void* workspace, int32_t* host_count, hipS
  * For FCE_NONE the loss output is float[N]: l_i for a valid row, 0 for an
  * ignored row, NaN for a label outside [0, V) that is not ignore_index.
  * `opt` is a host pointer; NULL is FCE_ERR_NULL.  A z_loss that is negative,
- * infinite or NaN, an unknown reduction or schedule, chunk < 1 or a
- * non-zero variant is FCE_ERR_ARG.  With the default-valued options
+ * infinite or NaN, an unknown reduction, schedule or variant, chunk < 1, or
+ * FCE_VARIANT_STORE_LOGITS anywhere but fce_fused_fwd_bwd_ex and
+ * fce_workspace_size_ex is FCE_ERR_ARG.  With the default-valued options
  * (z_loss 0, reduction mean or sum) they equal the entry points above
  * bitwise.  Everything else is as documented above. */
 
@@ -190,7 +201,9 @@ fce_status fce_backward_ex(const void* X, const void* W, const int32_t* labels, 
                            void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /* Fused forward and backward with upstream gradient 1 (for FCE_NONE: 1 for
- * every token). */
+ * every token).  With opt->variant = FCE_VARIANT_STORE_LOGITS the logits are
+ * kept per chunk instead of recomputed (schedule is then unused); the
+ * workspace must be sized by fce_workspace_size_ex with the same options. */
 fce_status fce_fused_fwd_bwd_ex(const void* X, const void* W, const int32_t* labels, int64_t N,
                                 int64_t H, int64_t V, fce_dtype dtype, const fce_options* opt,
                                 float* loss, float* dX, float* dW, void* workspace,
@@ -209,8 +222,9 @@ fce_status fce_fused_fwd_bwd_ex(const void* X, const void* W, const int32_t* lab
  * for ones) in Z's dtype, row-major [N][lddz]; dZ may be Z itself (the
  * gradient then overwrites the logits; lddz must equal ldz).  Columns
  * V .. of a row's last 16-byte vector are written as 0 in dZ; columns
- * past that are not touched.  Ignored rows get dZ = 0.  opt->chunk,
- * opt->schedule and opt->variant are checked as elsewhere but unused.
+ * past that are not touched.  Ignored rows get dZ = 0.  opt->chunk and
+ * opt->schedule are checked as elsewhere but unused; opt->variant must be
+ * FCE_VARIANT_RECOMPUTE.
  * The workspace (fce_ce_logits_workspace_size) holds the label scan and
  * per-row loss terms. */
 size_t fce_ce_logits_workspace_size(int64_t N);

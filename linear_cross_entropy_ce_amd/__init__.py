@@ -21,7 +21,10 @@ from ._binding import (  # noqa: F401
     FceError,
     SCHEDULES,
     FCE_NONE,
+    FCE_VARIANT_RECOMPUTE,
+    FCE_VARIANT_STORE_LOGITS,
     REDUCTIONS,
+    VARIANTS,
     fce_backward,
     fce_backward_ex,
     fce_ce_logits,
@@ -53,12 +56,16 @@ def _dtype_code(t):
     raise TypeError(f"unsupported dtype {t.dtype}")
 
 
-def workspace_for(N, H, V, dtype, chunk=1024, schedule="auto", device="cuda"):
-    """A uint8 workspace tensor of the size the library asks for."""
+def workspace_for(N, H, V, dtype, chunk=1024, schedule="auto", device="cuda", **options):
+    """A uint8 workspace tensor of the size the library asks for (``options``:
+    those of the *_ex entry points, e.g. ``variant="store_logits"``)."""
     import torch
 
     code = dtype if isinstance(dtype, int) else (FCE_BF16 if dtype == torch.bfloat16 else FCE_F32)
-    n = fce_workspace_size(N, H, V, code, chunk, SCHEDULES.get(schedule, schedule))
+    if options:
+        n = fce_workspace_size_ex(N, H, V, code, chunk=chunk, schedule=schedule, **options)
+    else:
+        n = fce_workspace_size(N, H, V, code, chunk, SCHEDULES.get(schedule, schedule))
     if n == 0:
         raise ValueError("invalid problem for fce_workspace_size")
     return torch.empty(n, dtype=torch.uint8, device=device)

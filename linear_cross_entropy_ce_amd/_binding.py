@@ -32,6 +32,8 @@ SCHED_TOKEN = 1
 SCHED_VOCAB = 2
 SCHEDULES = {"auto": SCHED_AUTO, "token": SCHED_TOKEN, "vocab": SCHED_VOCAB}
 REDUCTIONS = {"mean": FCE_MEAN, "sum": FCE_SUM, "none": FCE_NONE}
+FCE_VARIANT_RECOMPUTE, FCE_VARIANT_STORE_LOGITS = 0, 1
+VARIANTS = {"recompute": FCE_VARIANT_RECOMPUTE, "store_logits": FCE_VARIANT_STORE_LOGITS}
 
 EXPORTED = ("fce_workspace_size", "fce_plan", "fce_forward", "fce_backward", "fce_fused_fwd_bwd",
             "fce_workspace_size_ex", "fce_forward_ex", "fce_backward_ex", "fce_fused_fwd_bwd_ex",
@@ -72,7 +74,7 @@ def make_options(ignore_index=-100, label_smoothing=0.0, z_loss=0.0, reduction="
                  schedule="auto", variant=0) -> Options:
     return Options(int(ignore_index), float(label_smoothing), float(z_loss),
                    REDUCTIONS.get(reduction, reduction), int(chunk),
-                   SCHEDULES.get(schedule, schedule), int(variant))
+                   SCHEDULES.get(schedule, schedule), int(VARIANTS.get(variant, variant)))
 
 
 class KernelTiming(ctypes.Structure):

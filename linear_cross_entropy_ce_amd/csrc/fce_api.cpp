@@ -101,15 +101,20 @@ fce_status check_device() {
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
-// Options of one call, checked.  allow_none: the *_ex entry points.
-fce_status check_options(const fce_options* opt, bool allow_none, fce::LossOpts* lo) {
+// Options of one call, checked.  allow_none: the *_ex entry points;
+// allow_store: those that can run the store-logits variant.
+fce_status check_options(const fce_options* opt, bool allow_none, bool allow_store,
+                         fce::LossOpts* lo) {
   if (opt == nullptr) return FCE_ERR_NULL;
   const int r = opt->reduction;
   if (r != FCE_MEAN && r != FCE_SUM && !(allow_none && r == FCE_NONE)) return FCE_ERR_ARG;
   if (opt->schedule != FCE_SCHED_AUTO && opt->schedule != FCE_SCHED_TOKEN &&
       opt->schedule != FCE_SCHED_VOCAB)
     return FCE_ERR_ARG;
-  if (opt->chunk < 1 || opt->variant != 0) return FCE_ERR_ARG;
+  if (opt->chunk < 1) return FCE_ERR_ARG;
+  if (opt->variant != FCE_VARIANT_RECOMPUTE &&
+      !(allow_store && opt->variant == FCE_VARIANT_STORE_LOGITS))
+    return FCE_ERR_ARG;
   const float eps = opt->label_smoothing;
   if (!(eps >= 0.0f && eps < 1.0f)) return FCE_ERR_ARG;  // also rejects NaN
   const float z = opt->z_loss;
@@ -123,17 +128,19 @@ fce_status check_options(const fce_options* opt, bool allow_none, fce::LossOpts*
 
 fce_status validate(const void* X, const void* W, const int32_t* labels, int64_t N, int64_t H,
                     int64_t V, fce_dtype dtype, const fce_options* opt, bool allow_none,
-                    size_t ws_bytes, const void* ws, Plan* plan, fce::LossOpts* lo) {
+                    bool allow_store, size_t ws_bytes, const void* ws, Plan* plan,
+                    fce::LossOpts* lo) {
   if (N < 0 || H < 1 || V < 1) return FCE_ERR_SHAPE;
   if (W == nullptr || ws == nullptr) return FCE_ERR_NULL;
   if (N > 0 && (X == nullptr || labels == nullptr)) return FCE_ERR_NULL;
   if (dtype != FCE_F32 && dtype != FCE_BF16) return FCE_ERR_ARG;
-  if (fce_status s = check_options(opt, allow_none, lo); s != FCE_OK) return s;
+  if (fce_status s = check_options(opt, allow_none, allow_store, lo); s != FCE_OK) return s;
   const int64_t vec = (dtype == FCE_BF16) ? 8 : 4;
   if (H % vec != 0) return FCE_ERR_ALIGN;
   if (!aligned16(W) || !aligned16(ws) || (N > 0 && !aligned16(X))) return FCE_ERR_ALIGN;
   if (!fce::make_plan(N, H, V, static_cast<Dtype>(dtype), opt->chunk,
-                      static_cast<Schedule>(opt->schedule), plan))
+                      static_cast<Schedule>(opt->schedule), plan,
+                      static_cast<fce::Variant>(opt->variant)))
     return FCE_ERR_SHAPE;
   if (ws_bytes < plan->total) return FCE_ERR_WORKSPACE;
   return FCE_OK;
@@ -159,7 +166,7 @@ fce_status forward_impl(const void* X, const void* W, const int32_t* labels, int
                         hipStream_t stream) {
   Plan p;
   fce::LossOpts lo;
-  fce_status s = validate(X, W, labels, N, H, V, dtype, opt, allow_none, workspace_bytes,
+  fce_status s = validate(X, W, labels, N, H, V, dtype, opt, allow_none, false, workspace_bytes,
                           workspace, &p, &lo);
   if (s != FCE_OK) return s;
   const bool none = lo.reduction == fce::Reduction::None;
@@ -177,7 +184,7 @@ fce_status backward_impl(const void* X, const void* W, const int32_t* labels, in
                          void* workspace, size_t workspace_bytes, hipStream_t stream) {
   Plan p;
   fce::LossOpts lo;
-  fce_status s = validate(X, W, labels, N, H, V, dtype, opt, allow_none, workspace_bytes,
+  fce_status s = validate(X, W, labels, N, H, V, dtype, opt, allow_none, false, workspace_bytes,
                           workspace, &p, &lo);
   if (s != FCE_OK) return s;
   if (dW == nullptr || (N > 0 && (lse == nullptr || dX == nullptr))) return FCE_ERR_NULL;
@@ -199,8 +206,8 @@ fce_status fused_impl(const void* X, const void* W, const int32_t* labels, int64
                       hipStream_t stream) {
   Plan p;
   fce::LossOpts lo;
-  fce_status s = validate(X, W, labels, N, H, V, dtype, opt, allow_none, workspace_bytes,
-                          workspace, &p, &lo);
+  fce_status s = validate(X, W, labels, N, H, V, dtype, opt, allow_none, allow_none,
+                          workspace_bytes, workspace, &p, &lo);
   if (s != FCE_OK) return s;
   const bool none = lo.reduction == fce::Reduction::None;
   if ((loss == nullptr && !(none && N == 0)) || dW == nullptr || (N > 0 && dX == nullptr))
@@ -212,6 +219,11 @@ fce_status fused_impl(const void* X, const void* W, const int32_t* labels, int64
   // One label scan serves both passes: with g = 1 its backward scale equals
   // the one fce_backward would compute.
   hipError_t e = fce::launch_label_scan(p, labels, lo, nullptr, ws, stream, timer());
+  if (p.variant == fce::Variant::StoreLogits) {
+    if (e == hipSuccess)
+      e = fce::launch_fused_store(p, X, W, labels, lo, loss, lse, dX, dW, ws, stream, timer());
+    return from_hip(e);
+  }
   if (e == hipSuccess) e = fce::launch_forward(p, X, W, labels, lo, loss, lse, ws, stream, timer());
   if (e == hipSuccess)
     e = fce::launch_backward(p, X, W, labels, lo, lse, nullptr, dX, dW, ws, stream, timer());
@@ -232,10 +244,11 @@ size_t fce_workspace_size_ex(int64_t N, int64_t H, int64_t V, fce_dtype dtype,
                              const fce_options* opt) {
   if (dtype != FCE_F32 && dtype != FCE_BF16) return 0;
   fce::LossOpts lo;
-  if (check_options(opt, true, &lo) != FCE_OK) return 0;
+  if (check_options(opt, true, true, &lo) != FCE_OK) return 0;
   Plan p;
   if (!fce::make_plan(N, H, V, static_cast<Dtype>(dtype), opt->chunk,
-                      static_cast<Schedule>(opt->schedule), &p))
+                      static_cast<Schedule>(opt->schedule), &p,
+                      static_cast<fce::Variant>(opt->variant)))
     return 0;
   return p.total;
 }
@@ -331,7 +344,7 @@ fce_status fce_ce_logits(const void* Z, int64_t ldz, const int32_t* labels, int6
   if (N > 0 && (Z == nullptr || labels == nullptr || lse == nullptr)) return FCE_ERR_NULL;
   if (dtype != FCE_F32 && dtype != FCE_BF16) return FCE_ERR_ARG;
   fce::LossOpts lo;
-  if (fce_status s = check_options(opt, true, &lo); s != FCE_OK) return s;
+  if (fce_status s = check_options(opt, true, false, &lo); s != FCE_OK) return s;
   const bool none = lo.reduction == fce::Reduction::None;
   if (loss == nullptr && !(none && N == 0)) return FCE_ERR_NULL;
   const int64_t es = (dtype == FCE_BF16) ? 2 : 4;

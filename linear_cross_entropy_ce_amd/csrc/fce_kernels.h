@@ -41,6 +41,12 @@ hipError_t launch_backward(const Plan& p, const void* X, const void* W, const in
                            const LossOpts& o, const float* lse, const float* grad_tok, float* dX,
                            float* dW, char* ws, hipStream_t st, KernelTimer* timer);
 
+// Store-logits variant of forward + backward (upstream gradient 1): the plan
+// must be made with Variant::StoreLogits; the label scan runs first.
+hipError_t launch_fused_store(const Plan& p, const void* X, const void* W, const int32_t* labels,
+                              const LossOpts& o, float* loss, float* lse, float* dX, float* dW,
+                              char* ws, hipStream_t st, KernelTimer* timer);
+
 // Loss (and optionally dZ) on logits the caller holds.  Workspace layout:
 // Ctrl, one flag word, then N per-row loss terms (each 256-byte aligned).
 constexpr size_t ce_off_ctrl() { return 0; }

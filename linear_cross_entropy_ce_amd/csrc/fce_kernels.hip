@@ -92,6 +92,18 @@ __global__ __launch_bounds__(1024) void k_label_scan(const int32_t* __restrict__
 }
 
 // ------------------------------------------------------------------ forward
+// Four consecutive elements of a row, rounded to T (bf16: nearest even).
+__device__ __forceinline__ void store4(float* p, float a, float b, float c, float d) {
+  floatx4 v = {a, b, c, d};
+  *reinterpret_cast<floatx4*>(p) = v;
+}
+__device__ __forceinline__ void store4(bf16* p, float a, float b, float c, float d) {
+  typedef bf16 bf16x4 __attribute__((ext_vector_type(4)));
+  bf16x4 v = {static_cast<bf16>(a), static_cast<bf16>(b), static_cast<bf16>(c),
+              static_cast<bf16>(d)};
+  *reinterpret_cast<bf16x4*>(p) = v;
+}
+
 template <typename T>
 struct FwdArgs {
   const T* X;
@@ -101,9 +113,14 @@ struct FwdArgs {
   int tok_tiles, voc_tiles, splits, group_m;
   int64_t n_pad;
   floatx4* part;  // [splits][n_pad]: (m, l, z_y, sum z)
+  T* zout;        // STORE: logits [N][ldz] in T, columns up to the tile coverage
+  int64_t ldz;
 };
 
-template <class C, bool SMOOTH>
+// STORE: also write every logit tile, rounded to T, to zout (the logits of
+// the store-logits variant).  Columns past V hold 0 (W rows past V load as
+// zeros), so a row is written up to the vocabulary tile coverage.
+template <class C, bool SMOOTH, bool STORE>
 __global__ __launch_bounds__(C::NT) void k_fwd_lse(FwdArgs<typename C::Elem> a) {
   typedef typename C::Elem T;
   FCE_DMA_STAGES(lds);
@@ -137,6 +154,18 @@ __global__ __launch_bounds__(C::NT) void k_fwd_lse(FwdArgs<typename C::Elem> a) 
     const bool full = m0 + C::BM <= a.V;
 #pragma unroll
     for (int fn = 0; fn < C::FN; ++fn) {
+      if constexpr (STORE) {
+        const int tok = n0 + wn * C::WTN + fn * C::NB + Map::col(lane);
+        if (tok < a.N) {
+          T* zr = a.zout + static_cast<int64_t>(tok) * a.ldz + vbase;
+#pragma unroll
+          for (int fm = 0; fm < C::FM; ++fm)
+#pragma unroll
+            for (int g = 0; g < Map::NGRP; ++g)
+              store4(zr + fm * C::MB + Map::row(lane, g), acc.v[fm][fn][4 * g],
+                     acc.v[fm][fn][4 * g + 1], acc.v[fm][fn][4 * g + 2], acc.v[fm][fn][4 * g + 3]);
+        }
+      }
       float tmax = -INFINITY;
 #pragma unroll
       for (int fm = 0; fm < C::FM; ++fm)
@@ -296,17 +325,6 @@ struct DzArgs {
   int64_t ldz;
   const int32_t* flag;  // this token block's "has a valid label" flag
 };
-
-__device__ __forceinline__ void store4(float* p, float a, float b, float c, float d) {
-  floatx4 v = {a, b, c, d};
-  *reinterpret_cast<floatx4*>(p) = v;
-}
-__device__ __forceinline__ void store4(bf16* p, float a, float b, float c, float d) {
-  typedef bf16 bf16x4 __attribute__((ext_vector_type(4)));
-  bf16x4 v = {static_cast<bf16>(a), static_cast<bf16>(b), static_cast<bf16>(c),
-              static_cast<bf16>(d)};
-  *reinterpret_cast<bf16x4*>(p) = v;
-}
 
 template <class C, bool KFULL>
 __global__ __launch_bounds__(C::NT) void k_bwd_dz(DzArgs<typename C::Elem> a) {
@@ -496,7 +514,12 @@ struct CeArgs {
   float* rowloss;  // per-row loss terms
 };
 
-template <typename T>
+// GIVEN: lse holds each valid row's LSE already (the store-logits variant,
+// whose forward computed it from the fp32 accumulators); only pass 2 runs,
+// neither lse nor the loss terms are written, and dZ leaves out the scale
+// g / D, which the gradient products apply in fp32 (the per-token g_i of
+// reduction none is kept).
+template <typename T, bool GIVEN>
 __global__ __launch_bounds__(kCeThreads) void k_ce_logits(CeArgs a) {
   typedef CeVec<T> CV;
   constexpr int E = CV::E;
@@ -520,7 +543,7 @@ __global__ __launch_bounds__(kCeThreads) void k_ce_logits(CeArgs a) {
     for (int e = 0; e < E; ++e) f[e] = (e < lim) ? f[e] : v;
   };
   if (!valid) {  // ignored (or invalid) label: no loss, zero gradient row
-    if (tid == 0) {
+    if (!GIVEN && tid == 0) {
       a.lse[row] = NAN;
       a.rowloss[row] = (y == a.ignore || a.reduction != 2) ? 0.0f : NAN;
     }
@@ -530,68 +553,74 @@ __global__ __launch_bounds__(kCeThreads) void k_ce_logits(CeArgs a) {
     return;
   }
 
-  // pass 1: running (max, sum-exp, sum z) of this thread's vectors
-  float m = -INFINITY, l = 0.0f, zs = 0.0f;
-  const bool smooth = a.eps != 0.0f;
-  for (int j0 = tid; j0 < nv; j0 += kCeUnroll * kCeThreads) {
-    u32x4 r[kCeUnroll];
+  float L;
+  if constexpr (GIVEN) {
+    L = a.lse[row];
+  } else {
+    // pass 1: running (max, sum-exp, sum z) of this thread's vectors
+    float m = -INFINITY, l = 0.0f, zs = 0.0f;
+    const bool smooth = a.eps != 0.0f;
+    for (int j0 = tid; j0 < nv; j0 += kCeUnroll * kCeThreads) {
+      u32x4 r[kCeUnroll];
 #pragma unroll
-    for (int u = 0; u < kCeUnroll; ++u) r[u] = buf_load16(rz, (j0 + u * kCeThreads) * 16);
+      for (int u = 0; u < kCeUnroll; ++u) r[u] = buf_load16(rz, (j0 + u * kCeThreads) * 16);
 #pragma unroll
-    for (int u = 0; u < kCeUnroll; ++u) {
-      float f[E];
-      CV::unpack(r[u], f);
-      const int lim = a.V - (j0 + u * kCeThreads) * E;
-      if (lim < E) {
-        if (smooth) {
+      for (int u = 0; u < kCeUnroll; ++u) {
+        float f[E];
+        CV::unpack(r[u], f);
+        const int lim = a.V - (j0 + u * kCeThreads) * E;
+        if (lim < E) {
+          if (smooth) {
 #pragma unroll
-          for (int e = 0; e < E; ++e) zs += (e < lim) ? f[e] : 0.0f;
+            for (int e = 0; e < E; ++e) zs += (e < lim) ? f[e] : 0.0f;
+          }
+          pad(f, lim, -INFINITY);
+        } else if (smooth) {
+#pragma unroll
+          for (int e = 0; e < E; ++e) zs += f[e];
         }
-        pad(f, lim, -INFINITY);
-      } else if (smooth) {
+        float vm = f[0];
 #pragma unroll
-        for (int e = 0; e < E; ++e) zs += f[e];
+        for (int e = 1; e < E; ++e) vm = fmaxf(vm, f[e]);
+        if (vm == -INFINITY) continue;
+        const float mn = fmaxf(m, vm);
+        const float mnl = mn * kLog2e;
+        float acc = 0.0f;
+#pragma unroll
+        for (int e = 0; e < E; ++e) acc += hw_exp2(fmaf(f[e], kLog2e, -mnl));
+        l = ((m == -INFINITY) ? 0.0f : l * hw_exp2((m - mn) * kLog2e)) + acc;
+        m = mn;
       }
-      float vm = f[0];
-#pragma unroll
-      for (int e = 1; e < E; ++e) vm = fmaxf(vm, f[e]);
-      if (vm == -INFINITY) continue;
-      const float mn = fmaxf(m, vm);
-      const float mnl = mn * kLog2e;
-      float acc = 0.0f;
-#pragma unroll
-      for (int e = 0; e < E; ++e) acc += hw_exp2(fmaf(f[e], kLog2e, -mnl));
-      l = ((m == -INFINITY) ? 0.0f : l * hw_exp2((m - mn) * kLog2e)) + acc;
-      m = mn;
     }
-  }
-  // wave, then fixed-order workgroup merge of (m, l, sum z)
+    // wave, then fixed-order workgroup merge of (m, l, sum z)
 #pragma unroll
-  for (int sh = 32; sh > 0; sh >>= 1) {
-    float t0 = 0.0f;
-    const float m2 = __shfl_xor(m, sh), l2 = __shfl_xor(l, sh), z2 = __shfl_xor(zs, sh);
-    lse_merge(m, l, t0, zs, m2, l2, 0.0f, z2);
+    for (int sh = 32; sh > 0; sh >>= 1) {
+      float t0 = 0.0f;
+      const float m2 = __shfl_xor(m, sh), l2 = __shfl_xor(l, sh), z2 = __shfl_xor(zs, sh);
+      lse_merge(m, l, t0, zs, m2, l2, 0.0f, z2);
+    }
+    if (lane == 0) s_part[wave] = floatx4{m, l, 0.0f, zs};
+    __syncthreads();
+    if (tid == 0) {
+      floatx4 st = s_part[0];
+      for (int w = 1; w < kCeThreads / 64; ++w) lse_merge(st, s_part[w]);
+      const float Lr = st[0] + hw_log2(st[1]) * kLn2;
+      const float zy = static_cast<float>(zrow[y]);  // the target logit
+      float term = Lr - (1.0f - a.eps) * zy;
+      if (smooth) term -= (a.eps / static_cast<float>(a.V)) * st[3];
+      if (a.zloss != 0.0f) term += a.zloss * Lr * Lr;
+      a.lse[row] = Lr;
+      a.rowloss[row] = term;
+      s_bcast[0] = Lr;
+    }
+    if (!drow) return;
+    __syncthreads();
+    L = s_bcast[0];
   }
-  if (lane == 0) s_part[wave] = floatx4{m, l, 0.0f, zs};
-  __syncthreads();
-  if (tid == 0) {
-    floatx4 st = s_part[0];
-    for (int w = 1; w < kCeThreads / 64; ++w) lse_merge(st, s_part[w]);
-    const float L = st[0] + hw_log2(st[1]) * kLn2;
-    const float zy = static_cast<float>(zrow[y]);  // the target logit
-    float term = L - (1.0f - a.eps) * zy;
-    if (smooth) term -= (a.eps / static_cast<float>(a.V)) * st[3];
-    if (a.zloss != 0.0f) term += a.zloss * L * L;
-    a.lse[row] = L;
-    a.rowloss[row] = term;
-    s_bcast[0] = L;
-  }
-  if (!drow) return;
-  __syncthreads();
 
   // pass 2: dZ = (p (1 + 2 alpha L) - eps/V - (1-eps)[i = y]) * scale, p = exp(z - L)
-  const float L = s_bcast[0];
-  const float scale = (a.reduction == 2) ? (a.grad ? a.grad[row] : 1.0f) : a.ctrl->scale_bwd;
+  const float scale = (a.reduction == 2) ? (a.grad ? a.grad[row] : 1.0f)
+                                         : (GIVEN ? 1.0f : a.ctrl->scale_bwd);
   const float ga = (1.0f + 2.0f * a.zloss * L) * scale;
   const float gb = (a.eps / static_cast<float>(a.V)) * scale;
   const float gy = (1.0f - a.eps) * scale;
@@ -661,9 +690,9 @@ hipError_t run_forward(const Plan& p, const T* X, const T* W, const int32_t* lab
     const double flops = 2.0 * static_cast<double>(p.N) * p.V * p.H;
     timer->begin("fwd_lse", flops, st);
     if (eps != 0.0f)
-      k_fwd_lse<C, true><<<grid, C::NT, 0, st>>>(fa);
+      k_fwd_lse<C, true, false><<<grid, C::NT, 0, st>>>(fa);
     else
-      k_fwd_lse<C, false><<<grid, C::NT, 0, st>>>(fa);
+      k_fwd_lse<C, false, false><<<grid, C::NT, 0, st>>>(fa);
     FCE_CHECK_LAUNCH();
     timer->end(st);
     timer->begin("lse_merge", 0.0, st);
@@ -677,6 +706,66 @@ hipError_t run_forward(const Plan& p, const T* X, const T* W, const int32_t* lab
   timer->begin("loss_final", 0.0, st);
   k_loss_final<<<1, 256, 0, st>>>(blockloss, N > 0 ? static_cast<int>(p.n_loss_blocks) : 0, ctrl,
                                   loss);
+  FCE_CHECK_LAUNCH();
+  timer->end(st);
+  return hipSuccess;
+}
+
+// The two gradient products of one logit block: dZ is [ntok][>= nvoc
+// rounded up to the tile] at dz with row pitch ldz, for tokens tok0.. and
+// vocabulary columns voc0...  acc_dw / acc_dx: add to the previous block's
+// values instead of storing.
+template <typename T>
+hipError_t grad_products(const Plan& p, const T* X, const T* W, const T* dz, int64_t ldz,
+                         int64_t tok0, int ntok, int64_t voc0, int nvoc, bool acc_dw, bool acc_dx,
+                         const Ctrl* ctrl, const int32_t* flag, float* dX, float* dW,
+                         hipStream_t st, KernelTimer* timer, const char* name_dw,
+                         const char* name_dx) {
+  typedef typename ShapeOf<T>::C C;
+  const int64_t H = p.H;
+  const int h_tiles = cdiv_i(H, C::BN);
+  const int tok_tiles = cdiv_i(ntok, C::BN);
+  const int voc_tiles = cdiv_i(nvoc, C::BM);
+  const int nvoc_cov = voc_tiles * C::BM;
+  const double blk_flops = 2.0 * static_cast<double>(ntok) * nvoc * H;
+
+  // dW[voc0 : voc0+nvoc] (=|+=) s * dZ^T X[tok0 : tok0+ntok]
+  GradArgs<T> gw;
+  gw.A = Opnd<T>{dz, ldz, nvoc, ntok};                            // (v, t) at dz[t*ldz + v]
+  gw.B = Opnd<T>{X + tok0 * H, H, static_cast<int>(H), ntok};    // (h, t) at X[t*H + h]
+  gw.K = ntok;
+  gw.m_valid = nvoc;
+  gw.n_valid = static_cast<int>(H);
+  gw.tm_tiles = voc_tiles;
+  gw.tn_tiles = h_tiles;
+  gw.group_m = 2;
+  gw.out = dW + voc0 * H;
+  gw.ldo = H;
+  gw.ctrl = ctrl;
+  gw.accumulate = acc_dw;
+  gw.flag = flag;
+  timer->begin(name_dw, blk_flops, st);
+  k_bwd_grad<C, false><<<voc_tiles * h_tiles, C::NT, 0, st>>>(gw);
+  FCE_CHECK_LAUNCH();
+  timer->end(st);
+
+  // dX[tok0 : tok0+ntok] (=|+=) s * dZ W[voc0 : voc0+nvoc]
+  GradArgs<T> gx;
+  gx.A = Opnd<T>{dz, ldz, ntok, nvoc_cov};                         // (t, v) at dz[t*ldz + v]
+  gx.B = Opnd<T>{W + voc0 * H, H, static_cast<int>(H), nvoc};     // (h, v) at W[v*H + h]
+  gx.K = nvoc_cov;
+  gx.m_valid = ntok;
+  gx.n_valid = static_cast<int>(H);
+  gx.tm_tiles = tok_tiles;
+  gx.tn_tiles = h_tiles;
+  gx.group_m = 2;
+  gx.out = dX + tok0 * H;
+  gx.ldo = H;
+  gx.ctrl = ctrl;
+  gx.accumulate = acc_dx;
+  gx.flag = flag;
+  timer->begin(name_dx, blk_flops, st);
+  k_bwd_grad<C, true><<<tok_tiles * h_tiles, C::NT, 0, st>>>(gx);
   FCE_CHECK_LAUNCH();
   timer->end(st);
   return hipSuccess;
@@ -700,7 +789,6 @@ hipError_t run_backward(const Plan& p, const T* X, const T* W, const int32_t* la
     timer->end(st);
     return hipSuccess;
   }
-  const int h_tiles = cdiv_i(H, C::BN);
   for (int64_t ia = 0; ia < p.a; ++ia) {
     const int64_t tok0 = ia * p.CN;
     const int ntok = static_cast<int>(std::min(p.CN, N - tok0));
@@ -709,7 +797,6 @@ hipError_t run_backward(const Plan& p, const T* X, const T* W, const int32_t* la
       const int64_t voc0 = ib * p.CV;
       const int nvoc = static_cast<int>(std::min(p.CV, V - voc0));
       const int voc_tiles = cdiv_i(nvoc, C::BM);
-      const int nvoc_cov = voc_tiles * C::BM;  // columns of the block written by k_bwd_dz
       const double blk_flops = 2.0 * static_cast<double>(ntok) * nvoc * H;
 
       DzArgs<T> da{X + tok0 * H, W + voc0 * H, labels + tok0, lse + tok0, ntok, nvoc,
@@ -724,51 +811,93 @@ hipError_t run_backward(const Plan& p, const T* X, const T* W, const int32_t* la
       FCE_CHECK_LAUNCH();
       timer->end(st);
 
-      // dW[voc0 : voc0+nvoc] (=|+=) s * dZ^T X[tok0 : tok0+ntok]
-      GradArgs<T> gw;
-      gw.A = Opnd<T>{dz, p.ldz, nvoc, ntok};                         // (v, t) at dz[t*ldz + v]
-      gw.B = Opnd<T>{X + tok0 * H, H, static_cast<int>(H), ntok};    // (h, t) at X[t*H + h]
-      gw.K = ntok;
-      gw.m_valid = nvoc;
-      gw.n_valid = static_cast<int>(H);
-      gw.tm_tiles = voc_tiles;
-      gw.tn_tiles = h_tiles;
-      gw.group_m = 2;
-      gw.out = dW + voc0 * H;
-      gw.ldo = H;
-      gw.ctrl = ctrl;
-      gw.accumulate = ia > 0;
-      gw.flag = flags + ia;
-      timer->begin("bwd_dw", blk_flops, st);
-      k_bwd_grad<C, false><<<voc_tiles * h_tiles, C::NT, 0, st>>>(gw);
-      FCE_CHECK_LAUNCH();
-      timer->end(st);
-
-      // dX[tok0 : tok0+ntok] (=|+=) s * dZ W[voc0 : voc0+nvoc]
-      GradArgs<T> gx;
-      gx.A = Opnd<T>{dz, p.ldz, ntok, nvoc_cov};                      // (t, v) at dz[t*ldz + v]
-      gx.B = Opnd<T>{W + voc0 * H, H, static_cast<int>(H), nvoc};     // (h, v) at W[v*H + h]
-      gx.K = nvoc_cov;
-      gx.m_valid = ntok;
-      gx.n_valid = static_cast<int>(H);
-      gx.tm_tiles = tok_tiles;
-      gx.tn_tiles = h_tiles;
-      gx.group_m = 2;
-      gx.out = dX + tok0 * H;
-      gx.ldo = H;
-      gx.ctrl = ctrl;
-      gx.accumulate = ib > 0;
-      gx.flag = flags + ia;
-      timer->begin("bwd_dx", blk_flops, st);
-      k_bwd_grad<C, true><<<tok_tiles * h_tiles, C::NT, 0, st>>>(gx);
-      FCE_CHECK_LAUNCH();
-      timer->end(st);
+      const hipError_t e = grad_products<T>(p, X, W, dz, p.ldz, tok0, ntok, voc0, nvoc, ia > 0,
+                                            ib > 0, ctrl, flags + ia, dX, dW, st, timer,
+                                            "bwd_dw", "bwd_dx");
+      if (e != hipSuccess) return e;
     }
   }
   return hipSuccess;
 }
 
+// Store-logits fused forward and backward (the Liger-style design of
+// "Chunked and Fused Cross-Entropy", llms.blog, "LinkedIn Liger Kernel": a
+// token chunk's logits are kept and overwritten in place by their gradient).
+// Per block of C_N tokens: the forward keeps the block's logits [C_N][V] in
+// the workspace while it reduces them to LSE partials; the merge gives LSE and
+// the loss terms; a streaming pass turns the logits into dZ in place; then
+// the two gradient products.  Executed work is 6NVH (no recompute).
+template <typename T>
+hipError_t run_fused_store(const Plan& p, const T* X, const T* W, const int32_t* labels,
+                           const LossOpts& o, float* loss, float* lse, float* dX, float* dW,
+                           char* ws, hipStream_t st, KernelTimer* timer) {
+  typedef typename ShapeOf<T>::C C;
+  const bool none = o.reduction == Reduction::None;
+  Ctrl* ctrl = reinterpret_cast<Ctrl*>(ws + p.off_ctrl);
+  const int32_t* flags = reinterpret_cast<const int32_t*>(ws + p.off_flags);
+  float* blockloss = reinterpret_cast<float*>(ws + p.off_blockloss);
+  floatx4* part = reinterpret_cast<floatx4*>(ws + p.off_part);
+  T* zs = reinterpret_cast<T*>(ws + p.off_scratch);
+  const int64_t N = p.N, H = p.H, V = p.V;
+  if (N == 0) {
+    timer->begin("fill_zero", 0.0, st);
+    k_fill_zero<<<1024, 256, 0, st>>>(dW, V * H);
+    FCE_CHECK_LAUNCH();
+    timer->end(st);
+  }
+  for (int64_t ia = 0; ia < p.a; ++ia) {
+    const int64_t tok0 = ia * p.CN;  // a multiple of kLossBlock
+    const int ntok = static_cast<int>(std::min(p.CN, N - tok0));
+    FwdArgs<T> fa{X + tok0 * H, W, labels + tok0, ntok, static_cast<int>(H), static_cast<int>(V),
+                  o.ignore, cdiv_i(ntok, C::BN), static_cast<int>(p.fwd_voc_tiles),
+                  static_cast<int>(p.fwd_splits), 1, p.n_pad, part, zs, p.ldz};
+    fa.group_m = static_cast<int>(std::max<int64_t>(1, 32 / std::max<int64_t>(p.fwd_splits, 1)));
+    const double blk_flops = 2.0 * static_cast<double>(ntok) * V * H;
+    timer->begin("sl_fwd", blk_flops, st);
+    if (o.eps != 0.0f)
+      k_fwd_lse<C, true, true><<<fa.tok_tiles * fa.splits, C::NT, 0, st>>>(fa);
+    else
+      k_fwd_lse<C, false, true><<<fa.tok_tiles * fa.splits, C::NT, 0, st>>>(fa);
+    FCE_CHECK_LAUNCH();
+    timer->end(st);
+    timer->begin("lse_merge", 0.0, st);
+    k_lse_merge<<<cdiv_i(ntok, kLossBlock), kLossBlock, 0, st>>>(
+        part, fa.splits, p.n_pad, labels + tok0, ntok, static_cast<int>(V), o.ignore, o.eps,
+        o.zloss, lse + tok0, blockloss + tok0 / kLossBlock, none ? loss + tok0 : nullptr);
+    FCE_CHECK_LAUNCH();
+    timer->end(st);
+    // logits -> dZ in place (upstream gradient 1 per token for reduction none)
+    CeArgs ca{zs, p.ldz, zs, p.ldz, labels + tok0, ntok, static_cast<int>(V), o.ignore,
+              static_cast<int>(o.reduction), o.eps, o.zloss, nullptr, ctrl, lse + tok0, nullptr};
+    timer->begin("sl_dz", 0.0, st);
+    k_ce_logits<T, true><<<ntok, kCeThreads, 0, st>>>(ca);
+    FCE_CHECK_LAUNCH();
+    timer->end(st);
+    const hipError_t e = grad_products<T>(p, X, W, zs, p.ldz, tok0, ntok, 0, static_cast<int>(V),
+                                          ia > 0, false, ctrl, flags + ia, dX, dW, st, timer,
+                                          "sl_dw", "sl_dx");
+    if (e != hipSuccess) return e;
+  }
+  if (none) return hipSuccess;
+  timer->begin("loss_final", 0.0, st);
+  k_loss_final<<<1, 256, 0, st>>>(blockloss, N > 0 ? static_cast<int>(p.n_loss_blocks) : 0, ctrl,
+                                  loss);
+  FCE_CHECK_LAUNCH();
+  timer->end(st);
+  return hipSuccess;
+}
+
 }  // namespace
+
+hipError_t launch_fused_store(const Plan& p, const void* X, const void* W, const int32_t* labels,
+                              const LossOpts& o, float* loss, float* lse, float* dX, float* dW,
+                              char* ws, hipStream_t st, KernelTimer* timer) {
+  if (p.dtype == Dtype::BF16)
+    return run_fused_store<bf16>(p, static_cast<const bf16*>(X), static_cast<const bf16*>(W),
+                                 labels, o, loss, lse, dX, dW, ws, st, timer);
+  return run_fused_store<float>(p, static_cast<const float*>(X), static_cast<const float*>(W),
+                                labels, o, loss, lse, dX, dW, ws, st, timer);
+}
 
 hipError_t launch_label_scan(const Plan& p, const int32_t* labels, const LossOpts& o,
                              const float* grad, char* ws, hipStream_t st, KernelTimer* timer) {
@@ -821,9 +950,9 @@ hipError_t launch_ce_logits(const CeLogitsCall& c, hipStream_t st, KernelTimer* 
              ctrl, c.lse, none ? c.loss : rowloss};
     timer->begin("ce_logits", 0.0, st);
     if (c.bf16)
-      k_ce_logits<bf16><<<N, kCeThreads, 0, st>>>(a);
+      k_ce_logits<bf16, false><<<N, kCeThreads, 0, st>>>(a);
     else
-      k_ce_logits<float><<<N, kCeThreads, 0, st>>>(a);
+      k_ce_logits<float, false><<<N, kCeThreads, 0, st>>>(a);
     FCE_CHECK_LAUNCH();
     timer->end(st);
   }

@@ -57,8 +57,10 @@ double model_time(const Plan& p, int64_t CN, int64_t CV, int64_t a, int64_t b) {
 }  // namespace
 
 bool make_plan(int64_t N, int64_t H, int64_t V, Dtype dtype, int64_t chunk, Schedule sched,
-               Plan* out) {
+               Plan* out, Variant variant) {
   if (!out || N < 0 || H < 1 || V < 1 || chunk < 1) return false;
+  if (variant != Variant::Recompute && variant != Variant::StoreLogits) return false;
+  if (sched != Schedule::Auto && sched != Schedule::Token && sched != Schedule::Vocab) return false;
   // Index arithmetic inside the kernels uses 64-bit row offsets, but tile
   // coordinates are 32-bit: keep every extent comfortably inside int32.
   const int64_t lim = static_cast<int64_t>(1) << 30;
@@ -68,13 +70,22 @@ bool make_plan(int64_t N, int64_t H, int64_t V, Dtype dtype, int64_t chunk, Sche
   p.H = H;
   p.V = V;
   p.dtype = dtype;
+  p.variant = variant;
   p.elem_bytes = (dtype == Dtype::BF16) ? 2 : 4;
   const int64_t BM = (dtype == Dtype::BF16) ? ShapeBf16::BM : ShapeF32::BM;
   const int64_t BN = (dtype == Dtype::BF16) ? ShapeBf16::BN : ShapeF32::BN;
   p.tile = std::max(BM, BN);
+  const bool store = variant == Variant::StoreLogits;
+  // StoreLogits: token blocks of `chunk` tokens (a whole number of loss
+  // blocks, so each block's loss sums land in their own slots) by all of V;
+  // the forward runs once per block.
+  const int64_t store_cn =
+      round_up(std::max<int64_t>(std::min(chunk, std::max<int64_t>(N, 1)), 1),
+               std::max<int64_t>(p.tile, kLossBlock));
+  const int64_t Nf = store ? std::min(N, store_cn) : N;
 
   // ---- forward grid: minimise ceil(tiles/CUs) * vocab tiles per split
-  p.fwd_tok_tiles = cdiv(N, BN);
+  p.fwd_tok_tiles = cdiv(Nf, BN);
   p.fwd_voc_tiles = cdiv(V, BM);
   p.n_pad = std::max<int64_t>(p.fwd_tok_tiles, 1) * BN;
   if (N > 0) {
@@ -98,7 +109,12 @@ bool make_plan(int64_t N, int64_t H, int64_t V, Dtype dtype, int64_t chunk, Sche
   const int64_t G = p.tile;
   const double budget = static_cast<double>(chunk) * static_cast<double>(V);
   const int64_t Vp = round_up(V, G);
-  if (N == 0) {
+  if (store) {
+    p.CN = store_cn;
+    p.CV = Vp;
+    p.a = cdiv(N, p.CN);
+    p.b = 1;
+  } else if (N == 0) {
     p.CN = G;
     p.CV = Vp;
     p.a = 0;
@@ -163,6 +179,7 @@ bool make_plan(int64_t N, int64_t H, int64_t V, Dtype dtype, int64_t chunk, Sche
   if ((p.ldz * p.elem_bytes) % 1024 == 0) p.ldz += 128 / p.elem_bytes;
   p.grad_rmw_bytes = (N == 0) ? 4 * V * H
                               : 4 * V * H * (2 * p.a - 1) + 4 * N * H * (2 * p.b - 1);
+  if (store && N > 0) p.grad_rmw_bytes = 4 * V * H * (2 * p.a - 1) + 4 * N * H;
 
   // ---- workspace layout
   size_t off = 0;

@@ -10,13 +10,19 @@ namespace fce {
 
 enum class Dtype : int { F32 = 0, BF16 = 1 };
 enum class Schedule : int { Auto = 0, Token = 1, Vocab = 2 };
+// Recompute: the backward rebuilds each logit block from X and W.
+// StoreLogits: the forward keeps a chunk's logits (chunk tokens x all V) in
+// the workspace and the backward turns them into dZ in place.
+enum class Variant : int { Recompute = 0, StoreLogits = 1 };
 
 struct Plan {
   int64_t N = 0, H = 0, V = 0;
   Dtype dtype = Dtype::BF16;
+  Variant variant = Variant::Recompute;
   int64_t elem_bytes = 2;
 
   // forward: token tiles x vocabulary splits, each split walks a range of vocab tiles
+  // (StoreLogits: of one token block, the forward runs block by block)
   int64_t fwd_tok_tiles = 0;
   int64_t fwd_voc_tiles = 0;
   int64_t fwd_splits = 0;
@@ -48,6 +54,6 @@ constexpr int kLossBlock = 256;  // tokens per block of the loss reduction
 
 // Returns false if the arguments are invalid (shapes, chunk, overflow).
 bool make_plan(int64_t N, int64_t H, int64_t V, Dtype dtype, int64_t chunk, Schedule sched,
-               Plan* out);
+               Plan* out, Variant variant = Variant::Recompute);
 
 }  // namespace fce

@@ -339,6 +339,13 @@ def test_full_size_workload(k, chunk, schedule):
     assert str(g["digest"]) == inp.digest(), "input generator drifted from the stored goldens"
     print(f"[{wl.name}] chunk {chunk} schedule {schedule}", flush=True)
     got = run(inp, chunk=chunk, schedule=schedule)
+    check_golden(inp, g, got)
+
+
+def check_golden(inp, g, got):
+    """Full-size results against the stored oracle values: the loss, every
+    row's LSE, sampled dX and dW rows, and the dW column-sum invariant."""
+    wl = inp.workload
     tl, tg = TOL[wl.dtype]
     le = abs(got["loss"] - float(g["loss"])) / abs(float(g["loss"]))
     valid = inp.labels != -100
@@ -355,3 +362,103 @@ def test_full_size_workload(k, chunk, schedule):
     assert np.all(got["dX"][~valid] == 0.0)
     assert col <= 1e-2 * fro  # rows of dZ sum to zero up to the bf16 rounding of dZ
     assert np.isfinite(got["dX"]).all() and np.isfinite(got["dW"]).all()
+
+
+# ------------------------------------------- store-logits variant (6NVH)
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+@pytest.mark.parametrize("reduction", ["mean", "sum", "none"])
+def test_store_logits_against_oracle(dtype, reduction):
+    # 700 tokens in chunks of 256 (the last one partial), ragged H and V,
+    # smoothing, ignored rows and z-loss
+    wl = wk.custom(700, 264 if dtype == "bf16" else 36, 5003, dtype, 0.05, "zipf", 1.1, 0.05, 0.1,
+                   seed=91)
+    inp = wk.draw(wl)
+    al = 1e-3
+    got = run_ex(inp, split=False, z_loss=al, reduction=reduction, chunk=200,
+                 variant="store_logits")
+    ref = orc.linear_cross_entropy(inp.X, inp.W, inp.labels, -100, wl.label_smoothing, reduction,
+                                   1.0, z_loss=al)
+    tl, tg = TOL[dtype]
+    valid = inp.labels != -100
+    if reduction == "none":
+        err = np.abs(got["loss"] - ref.loss).max() / np.abs(ref.loss[valid]).mean()
+        assert np.all(got["loss"][~valid] == 0.0)
+    else:
+        err = abs(got["loss"][0] - ref.loss) / abs(ref.loss)
+    ex, ew = rel_l2(got["dX"], ref.dX), rel_l2(got["dW"], ref.dW)
+    print(f"[store-logits {reduction} {dtype}] loss err {err:.2e}; dX {ex:.2e}; dW {ew:.2e}",
+          flush=True)
+    assert err <= tl and ex <= tg and ew <= tg
+    assert np.all(got["dX"][~valid] == 0.0)
+    # the loss comes from the same fp32 accumulators as the recompute path's
+    rec = run_ex(inp, split=False, z_loss=al, reduction=reduction, chunk=200)
+    assert np.allclose(got["loss"], rec["loss"], rtol=1e-6, atol=0.0, equal_nan=True)
+
+
+def test_store_logits_chunk_of_ignored_rows_and_invalid_label():
+    wl = wk.custom(600, 128, 3001, "bf16", 0.05, "uniform", ignore_frac=0.0, seed=93)
+    inp = wk.draw(wl)
+    inp.labels[256:512] = -100  # the whole second chunk
+    got = run_ex(inp, split=False, chunk=256, variant="store_logits")
+    ref = orc.linear_cross_entropy(inp.X, inp.W, inp.labels, -100, 0.0, "mean", 1.0)
+    assert abs(got["loss"][0] - ref.loss) <= 2e-3 * abs(ref.loss)
+    assert rel_l2(got["dX"], ref.dX) <= 2e-2 and rel_l2(got["dW"], ref.dW) <= 2e-2
+    assert np.all(got["dX"][256:512] == 0.0)
+    inp.labels[7] = 3001  # outside [0, V): NaN loss, the row's gradient is zero
+    got = run_ex(inp, split=False, chunk=256, variant="store_logits")
+    assert np.isnan(got["loss"][0]) and np.all(got["dX"][7] == 0.0)
+
+
+@pytest.mark.parametrize("N,H,V", [(1, 8, 1), (5, 8, 2), (33, 8, 257), (257, 520, 300), (0, 8, 10)])
+def test_store_logits_degenerate_shapes(N, H, V):
+    inp = wk.draw(wk.custom(N, H, V, "bf16", 0.5, seed=95 + N))
+    if N == 0:
+        X = torch.empty((0, H), dtype=torch.bfloat16, device="cuda")
+        _, W, _ = wk.to_torch(inp, "cuda")
+        ws = fce.workspace_for(0, H, V, torch.bfloat16, variant="store_logits")
+        loss = torch.full((1,), float("nan"), device="cuda")
+        dW = torch.full((V, H), float("nan"), device="cuda")
+        fce.fce_fused_fwd_bwd_ex(None, W, None, loss, None, dW, ws, variant="store_logits")
+        torch.cuda.synchronize()
+        assert loss.item() == 0.0 and torch.all(dW == 0).item()
+        return
+    got = run_ex(inp, split=False, chunk=64, variant="store_logits")
+    ref = orc.linear_cross_entropy(inp.X, inp.W, inp.labels, -100, 0.0, "mean", 1.0)
+    assert abs(got["loss"][0] - ref.loss) <= 2e-3 * max(abs(ref.loss), 1.0)
+    # The kept logits are rounded to bf16 (relative error 2^-9) before
+    # exp(z - LSE), so |error of dZ_ij| <= p_ij |z_ij| 2^-8 with the LSE from
+    # fp32: an absolute floor that matters where dZ is ~0 (V = 1: p = 1).
+    X64, W64 = inp.X.astype(np.float64), inp.W.astype(np.float64)
+    zmax = np.abs(X64 @ W64.T).max()
+    D = max(int((inp.labels != -100).sum()), 1)
+    fx = 2.0 ** -8 * zmax * np.linalg.norm(W64, axis=1).max() * np.sqrt(N) / D
+    fw = 2.0 ** -8 * zmax * np.linalg.norm(X64, axis=1).sum() / D
+    assert np.linalg.norm(got["dX"] - ref.dX) <= 2e-2 * np.linalg.norm(ref.dX) + fx
+    assert np.linalg.norm(got["dW"] - ref.dW) <= 2e-2 * np.linalg.norm(ref.dW) + fw
+
+
+# The headline shape in one chunk (the whole 8192 x 128256 logits kept) and
+# in chunks of 1024, and the 4096 x 2048 x 32000 workload.
+@pytest.mark.parametrize("k,chunk", [(2, 1024), (3, 1024), (3, 8192)])
+def test_store_logits_full_size(k, chunk):
+    wl = wk.WORKLOADS[k]
+    g = _golden(k)
+    inp = _draw_cached(k)
+    assert str(g["digest"]) == inp.digest(), "input generator drifted from the stored goldens"
+    print(f"[{wl.name}] store-logits chunk {chunk}", flush=True)
+    got = run_ex(inp, split=False, chunk=chunk, variant="store_logits")
+    got["loss"] = float(got["loss"][0])
+    # the LSE stays in the workspace; take it from the forward entry point
+    got["lse"] = run_ex_lse(inp)
+    check_golden(inp, g, got)
+
+
+def run_ex_lse(inp):
+    X, W, y = wk.to_torch(inp, "cuda")
+    wl = inp.workload
+    ws = fce.workspace_for(wl.N, wl.H, wl.V, X.dtype)
+    loss = torch.empty(1, device="cuda")
+    lse = torch.empty(wl.N, device="cuda")
+    fce.fce_forward(X, W, y, loss, lse, ws, -100, wl.label_smoothing, "mean", 1024, "auto")
+    torch.cuda.synchronize()
+    return lse.cpu().numpy()

@@ -166,7 +166,7 @@ def _opts(**kw):
 @pytest.mark.parametrize("kw,status", [
     (dict(z_loss=-1e-3), B.FCE_ERR_ARG), (dict(z_loss=float("nan")), B.FCE_ERR_ARG),
     (dict(z_loss=float("inf")), B.FCE_ERR_ARG), (dict(reduction=3), B.FCE_ERR_ARG),
-    (dict(variant=1), B.FCE_ERR_ARG), (dict(chunk=0), B.FCE_ERR_ARG), (dict(schedule=5), B.FCE_ERR_ARG),
+    (dict(variant=2), B.FCE_ERR_ARG), (dict(chunk=0), B.FCE_ERR_ARG), (dict(schedule=5), B.FCE_ERR_ARG),
     (dict(label_smoothing=1.0), B.FCE_ERR_ARG)])
 def test_ex_rejects_bad_options(kw, status):
     lib = B.load_library()
@@ -177,6 +177,26 @@ def test_ex_rejects_bad_options(kw, status):
     assert lib.fce_fused_fwd_bwd_ex(FAKE, FAKE, FAKE, 64, 64, 100, 1, ctypes.byref(o), FAKE, FAKE,
                                     FAKE, FAKE, ws, None) == status
     assert lib.fce_workspace_size_ex(64, 64, 100, 1, ctypes.byref(o)) == 0
+
+
+def test_store_logits_variant_where_accepted_and_its_workspace():
+    lib = B.load_library()
+    N, H, V = 1000, 64, 5000
+    rec = lib.fce_workspace_size_ex(N, H, V, 1, ctypes.byref(_opts(chunk=300)))
+    sto = lib.fce_workspace_size_ex(N, H, V, 1, ctypes.byref(_opts(chunk=300, variant=1)))
+    # chunk 300 rounds up to 512 tokens by V rounded up to the 256 tile (bf16)
+    assert sto >= 512 * 5120 * 2 and sto != rec
+    o = _opts(chunk=300, variant=1)
+    # accepted by the fused call (a recompute-sized workspace is too small for it) ...
+    assert lib.fce_fused_fwd_bwd_ex(FAKE, FAKE, FAKE, N, H, V, 1, ctypes.byref(o), FAKE, FAKE,
+                                    FAKE, FAKE, min(rec, sto - 1), None) == B.FCE_ERR_WORKSPACE
+    # ... and by nothing else
+    assert lib.fce_forward_ex(FAKE, FAKE, FAKE, N, H, V, 1, ctypes.byref(o), FAKE, FAKE, FAKE,
+                              sto, None) == B.FCE_ERR_ARG
+    assert lib.fce_backward_ex(FAKE, FAKE, FAKE, N, H, V, 1, ctypes.byref(o), FAKE, None, FAKE,
+                               FAKE, FAKE, sto, None) == B.FCE_ERR_ARG
+    assert lib.fce_ce_logits(FAKE, V, FAKE, N, V, 1, ctypes.byref(o), FAKE, FAKE, None, 0, None,
+                             FAKE, 1 << 20, None) == B.FCE_ERR_ARG
 
 
 def test_ex_null_options_and_none_on_old_entry_points():
