@@ -109,6 +109,7 @@ typedef struct {
   int64_t workspace_bytes;  /* == fce_workspace_size()                             */
   int64_t fwd_splits;       /* vocabulary splits of the forward reduction          */
   int64_t grad_rmw_bytes;   /* fp32 dX/dW bytes written + re-read across blocks    */
+  int64_t dx_splits;        /* splits of the dX product over V (fp32 partials)     */
 } fce_plan_info;
 
 /* Loss options of the *_ex entry points.  Fields are fixed-width so the

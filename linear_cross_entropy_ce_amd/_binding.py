@@ -56,7 +56,7 @@ class PlanInfo(ctypes.Structure):
                 ("n_token_blocks", ctypes.c_int64), ("n_vocab_blocks", ctypes.c_int64),
                 ("scratch_bytes", ctypes.c_int64), ("partial_bytes", ctypes.c_int64),
                 ("workspace_bytes", ctypes.c_int64), ("fwd_splits", ctypes.c_int64),
-                ("grad_rmw_bytes", ctypes.c_int64)]
+                ("grad_rmw_bytes", ctypes.c_int64), ("dx_splits", ctypes.c_int64)]
 
     def as_dict(self):
         return {k: getattr(self, k) for k, _ in self._fields_}

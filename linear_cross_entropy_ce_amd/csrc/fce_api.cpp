@@ -271,6 +271,7 @@ fce_status fce_plan(int64_t N, int64_t H, int64_t V, fce_dtype dtype, int64_t ch
   out->n_vocab_blocks = p.b;
   out->scratch_bytes = static_cast<int64_t>(p.scratch_bytes);
   out->partial_bytes = static_cast<int64_t>(p.partial_bytes);
+  out->dx_splits = p.dx_splits;
   out->workspace_bytes = static_cast<int64_t>(p.total);
   out->fwd_splits = p.fwd_splits;
   out->grad_rmw_bytes = p.grad_rmw_bytes;

@@ -389,7 +389,18 @@ struct GradArgs {
   const Ctrl* ctrl;
   int accumulate;
   const int32_t* flag;
+  // split over K (gridDim.y > 1): split z covers k in [z ksplit, (z+1) ksplit)
+  // and writes its own output at out + z * split_stride
+  int ksplit;
+  int64_t split_stride;
 };
+
+// The part of an operand from contraction index k0 on.
+template <bool KMAJOR, typename T>
+__device__ __forceinline__ Opnd<T> opnd_from_k(const Opnd<T>& o, int k0) {
+  return Opnd<T>{o.p + (KMAJOR ? static_cast<int64_t>(k0) : static_cast<int64_t>(k0) * o.ld), o.ld,
+                 o.mn_ext, o.k_ext - k0};
+}
 
 template <class C, bool A_KMAJOR>
 __global__ __launch_bounds__(C::NT) void k_bwd_grad(GradArgs<typename C::Elem> a) {
@@ -403,13 +414,23 @@ __global__ __launch_bounds__(C::NT) void k_bwd_grad(GradArgs<typename C::Elem> a
   const int m0 = tm * C::BM, n0 = tn * C::BN;
   const bool skip = (*a.flag == 0);  // all labels of the token block ignored: dZ = 0
   if (skip && a.accumulate) return;
+  Opnd<T> A = a.A, B = a.B;
+  int K = a.K;
+  float* out = a.out;
+  if (gridDim.y > 1) {
+    const int k0 = static_cast<int>(blockIdx.y) * a.ksplit;
+    A = opnd_from_k<A_KMAJOR>(A, k0);
+    B = opnd_from_k<false>(B, k0);
+    K = min(a.ksplit, a.K - k0);
+    out += static_cast<int64_t>(blockIdx.y) * a.split_stride;
+  }
   Acc<C> acc;
   if (skip) {
     zero_acc(acc);
   } else {
     // K is the token count (dW, no K-major operand) or the block's vocabulary
     // coverage, a whole number of tiles (dX)
-    gemm_any<C, A_KMAJOR, false, true>(acc, a.A, a.B, m0, n0, a.K, lds, tid);
+    gemm_any<C, A_KMAJOR, false, true>(acc, A, B, m0, n0, K, lds, tid);
   }
   typedef AccMap<C> Map;
   const float s = a.ctrl->scale_bwd;
@@ -422,7 +443,7 @@ __global__ __launch_bounds__(C::NT) void k_bwd_grad(GradArgs<typename C::Elem> a
   const int rbase = wm * C::WTM;
   const int cbase = wn * C::WTN + Map::col(lane);
   const bool full = m0 + C::BM <= a.m_valid && n0 + C::BN <= a.n_valid;
-  float* tile = a.out + static_cast<int64_t>(m0) * a.ldo + n0;
+  float* tile = out + static_cast<int64_t>(m0) * a.ldo + n0;
 #pragma unroll
   for (int f0 = 0; f0 < C::FM; f0 += SLAB) {
     float old[SLAB][C::FN][C::NV];
@@ -451,6 +472,26 @@ __global__ __launch_bounds__(C::NT) void k_bwd_grad(GradArgs<typename C::Elem> a
           if (ok[j][fn][i])
             tile[static_cast<int64_t>(r) * a.ldo + c] = old[j][fn][i] + s * acc.v[f0 + j][fn][i];
         }
+  }
+}
+
+// dX rows of one block from the split partials: out (=|+=) sum over z of
+// part[z], in split order.  rows x cols fp32, cols a multiple of 4, row
+// pitch ldo for out and cols for the partials.
+__global__ __launch_bounds__(256) void k_dx_reduce(const float* __restrict__ part, int splits,
+                                                   int64_t split_stride, float* __restrict__ out,
+                                                   int64_t ldo, int rows, int cols,
+                                                   int accumulate) {
+  const int64_t nvec = static_cast<int64_t>(rows) * (cols / 4);
+  for (int64_t i = blockIdx.x * static_cast<int64_t>(blockDim.x) + threadIdx.x; i < nvec;
+       i += static_cast<int64_t>(gridDim.x) * blockDim.x) {
+    const int64_t r = i / (cols / 4), c = (i % (cols / 4)) * 4;
+    floatx4 s = *reinterpret_cast<const floatx4*>(part + r * cols + c);
+    for (int z = 1; z < splits; ++z)
+      s += *reinterpret_cast<const floatx4*>(part + z * split_stride + r * cols + c);
+    floatx4* o = reinterpret_cast<floatx4*>(out + r * ldo + c);
+    if (accumulate) s = *o + s;
+    *o = s;
   }
 }
 
@@ -714,12 +755,13 @@ hipError_t run_forward(const Plan& p, const T* X, const T* W, const int32_t* lab
 // The two gradient products of one logit block: dZ is [ntok][>= nvoc
 // rounded up to the tile] at dz with row pitch ldz, for tokens tok0.. and
 // vocabulary columns voc0...  acc_dw / acc_dx: add to the previous block's
-// values instead of storing.
+// values instead of storing.  dxpart: the plan's dx_splits partials of dX
+// ([splits][ntok][H] fp32) when it splits the dX product.
 template <typename T>
 hipError_t grad_products(const Plan& p, const T* X, const T* W, const T* dz, int64_t ldz,
                          int64_t tok0, int ntok, int64_t voc0, int nvoc, bool acc_dw, bool acc_dx,
                          const Ctrl* ctrl, const int32_t* flag, float* dX, float* dW,
-                         hipStream_t st, KernelTimer* timer, const char* name_dw,
+                         float* dxpart, hipStream_t st, KernelTimer* timer, const char* name_dw,
                          const char* name_dx) {
   typedef typename ShapeOf<T>::C C;
   const int64_t H = p.H;
@@ -744,6 +786,8 @@ hipError_t grad_products(const Plan& p, const T* X, const T* W, const T* dz, int
   gw.ctrl = ctrl;
   gw.accumulate = acc_dw;
   gw.flag = flag;
+  gw.ksplit = ntok;
+  gw.split_stride = 0;
   timer->begin(name_dw, blk_flops, st);
   k_bwd_grad<C, false><<<voc_tiles * h_tiles, C::NT, 0, st>>>(gw);
   FCE_CHECK_LAUNCH();
@@ -764,10 +808,28 @@ hipError_t grad_products(const Plan& p, const T* X, const T* W, const T* dz, int
   gx.ctrl = ctrl;
   gx.accumulate = acc_dx;
   gx.flag = flag;
+  gx.ksplit = nvoc_cov;
+  gx.split_stride = 0;
+  // split over the vocabulary when the plan asks for it: whole tiles per split
+  const int ksplit = cdiv_i(cdiv_i(nvoc_cov, static_cast<int>(p.dx_splits)), C::BM) * C::BM;
+  const int splits = cdiv_i(nvoc_cov, ksplit);
+  if (splits > 1) {
+    gx.ksplit = ksplit;
+    gx.out = dxpart;
+    gx.accumulate = 0;
+    gx.split_stride = static_cast<int64_t>(ntok) * H;
+  }
   timer->begin(name_dx, blk_flops, st);
-  k_bwd_grad<C, true><<<tok_tiles * h_tiles, C::NT, 0, st>>>(gx);
+  k_bwd_grad<C, true><<<dim3(tok_tiles * h_tiles, splits), C::NT, 0, st>>>(gx);
   FCE_CHECK_LAUNCH();
   timer->end(st);
+  if (splits > 1) {
+    timer->begin("dx_reduce", 0.0, st);
+    k_dx_reduce<<<1024, 256, 0, st>>>(dxpart, splits, gx.split_stride, dX + tok0 * H, H, ntok,
+                                      static_cast<int>(H), acc_dx);
+    FCE_CHECK_LAUNCH();
+    timer->end(st);
+  }
   return hipSuccess;
 }
 
@@ -781,6 +843,7 @@ hipError_t run_backward(const Plan& p, const T* X, const T* W, const int32_t* la
   const Ctrl* ctrl = reinterpret_cast<const Ctrl*>(ws + p.off_ctrl);
   const int32_t* flags = reinterpret_cast<const int32_t*>(ws + p.off_flags);
   T* dz = reinterpret_cast<T*>(ws + p.off_scratch);
+  float* dxpart = reinterpret_cast<float*>(ws + p.off_dxpart);
   const int64_t N = p.N, H = p.H, V = p.V;
   if (N == 0) {
     timer->begin("fill_zero", 0.0, st);
@@ -812,7 +875,7 @@ hipError_t run_backward(const Plan& p, const T* X, const T* W, const int32_t* la
       timer->end(st);
 
       const hipError_t e = grad_products<T>(p, X, W, dz, p.ldz, tok0, ntok, voc0, nvoc, ia > 0,
-                                            ib > 0, ctrl, flags + ia, dX, dW, st, timer,
+                                            ib > 0, ctrl, flags + ia, dX, dW, dxpart, st, timer,
                                             "bwd_dw", "bwd_dx");
       if (e != hipSuccess) return e;
     }
@@ -838,6 +901,7 @@ hipError_t run_fused_store(const Plan& p, const T* X, const T* W, const int32_t*
   float* blockloss = reinterpret_cast<float*>(ws + p.off_blockloss);
   floatx4* part = reinterpret_cast<floatx4*>(ws + p.off_part);
   T* zs = reinterpret_cast<T*>(ws + p.off_scratch);
+  float* dxpart = reinterpret_cast<float*>(ws + p.off_dxpart);
   const int64_t N = p.N, H = p.H, V = p.V;
   if (N == 0) {
     timer->begin("fill_zero", 0.0, st);
@@ -874,8 +938,8 @@ hipError_t run_fused_store(const Plan& p, const T* X, const T* W, const int32_t*
     FCE_CHECK_LAUNCH();
     timer->end(st);
     const hipError_t e = grad_products<T>(p, X, W, zs, p.ldz, tok0, ntok, 0, static_cast<int>(V),
-                                          ia > 0, false, ctrl, flags + ia, dX, dW, st, timer,
-                                          "sl_dw", "sl_dx");
+                                          ia > 0, false, ctrl, flags + ia, dX, dW, dxpart, st,
+                                          timer, "sl_dw", "sl_dx");
     if (e != hipSuccess) return e;
   }
   if (none) return hipSuccess;

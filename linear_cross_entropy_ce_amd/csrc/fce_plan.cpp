@@ -177,6 +177,16 @@ bool make_plan(int64_t N, int64_t H, int64_t V, Dtype dtype, int64_t chunk, Sche
   // by one 128-byte line.
   p.ldz = p.CV;
   if ((p.ldz * p.elem_bytes) % 1024 == 0) p.ldz += 128 / p.elem_bytes;
+  // ---- dX split: enough splits to fill the CUs with one wave, each at
+  // least kMinSplitTiles vocabulary tiles long
+  if (N > 0) {
+    constexpr int64_t kMinSplitTiles = 4;
+    const int64_t grid = cdiv(std::min(p.CN, N), BN) * cdiv(H, BN);
+    const int64_t ktiles = cdiv(std::min(p.CV, V), BM);
+    if (grid < kNumCUs)
+      p.dx_splits = std::max<int64_t>(
+          1, std::min(cdiv(kNumCUs, grid), ktiles / kMinSplitTiles));
+  }
   p.grad_rmw_bytes = (N == 0) ? 4 * V * H
                               : 4 * V * H * (2 * p.a - 1) + 4 * N * H * (2 * p.b - 1);
   if (store && N > 0) p.grad_rmw_bytes = 4 * V * H * (2 * p.a - 1) + 4 * N * H;
@@ -200,6 +210,12 @@ bool make_plan(int64_t N, int64_t H, int64_t V, Dtype dtype, int64_t chunk, Sche
                              : static_cast<size_t>(p.scratch_rows) * static_cast<size_t>(p.ldz) *
                                    static_cast<size_t>(p.elem_bytes);
   off = align_up(off + p.scratch_bytes);
+  p.off_dxpart = off;
+  p.dxpart_bytes = (p.dx_splits > 1) ? static_cast<size_t>(p.dx_splits) *
+                                           static_cast<size_t>(std::min(p.CN, N)) *
+                                           static_cast<size_t>(H) * sizeof(float)
+                                     : 0;
+  off = align_up(off + p.dxpart_bytes);
   p.total = off;
   *out = p;
   return true;

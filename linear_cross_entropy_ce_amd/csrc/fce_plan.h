@@ -33,11 +33,14 @@ struct Plan {
   int64_t CN = 0, CV = 0;
   int64_t a = 0, b = 0;  // number of token blocks, vocabulary blocks
   int64_t scratch_rows = 0, ldz = 0;
+  // dX product split over its contraction (the vocabulary) when its grid
+  // would not fill the CUs: each split writes an fp32 partial [C_N][H]
+  int64_t dx_splits = 1;
 
   // workspace layout (byte offsets, 256-byte aligned)
   size_t off_ctrl = 0, off_flags = 0, off_part = 0, off_blockloss = 0, off_lse = 0,
-         off_scratch = 0, total = 0;
-  size_t scratch_bytes = 0, partial_bytes = 0;
+         off_scratch = 0, off_dxpart = 0, total = 0;
+  size_t scratch_bytes = 0, partial_bytes = 0, dxpart_bytes = 0;
   int64_t n_loss_blocks = 0;
   int64_t grad_rmw_bytes = 0;
 };

@@ -117,7 +117,17 @@ def test_plan_invariants(N, H, V, dtype, chunk, sched):
         if sched == "vocab":
             assert a == 1
     assert p["grad_rmw_bytes"] == 4 * V * H * (2 * a - 1) + 4 * N * H * (2 * b - 1)
-    assert p["workspace_bytes"] >= p["scratch_bytes"] + p["partial_bytes"]
+    # the dX product splits over V only when its grid is under one wave of
+    # 256 CUs, then with enough splits to fill it, each at least 4 tiles long
+    grid = -(-min(CN, N) // tile) * -(-H // tile)
+    ktiles = -(-min(CV, V) // tile)
+    S = p["dx_splits"]
+    if grid >= 256 or ktiles < 8:
+        assert S == 1
+    else:
+        assert S == min(-(-256 // grid), ktiles // 4)
+    dxpart = S * min(CN, N) * H * 4 if S > 1 else 0
+    assert p["workspace_bytes"] >= p["scratch_bytes"] + p["partial_bytes"] + dxpart
 
 
 def test_plan_rejects_bad_arguments():
