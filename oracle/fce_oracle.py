@@ -24,7 +24,7 @@ Definitions used (notation of [LLMS]):
   dL/dz_ij = (softmax_ij - [j = y_i]) / N      [LLMS step 3; L27 "The gradient that makes fusion trivial"]
   dX = dZ W,  dW = dZ^T X                      [LLMS step 4; L27 "Trick 2"]
 
-Readings where the pages are silent or disagree (all listed in the design doc):
+Readings where the pages are silent or disagree:
   * label smoothing (named in [LLMS] "Numerical Considerations" item 3 and
     [L27] "Numerical traps" without a formula): target distribution
     q_ij = (1 - eps) [j = y_i] + eps / V, so
@@ -47,6 +47,9 @@ Readings where the pages are silent or disagree (all listed in the design doc):
   * the "Trick 1 only" path of [L27] ("Fused softmax+CE (keep logits, drop
     probs/dlogits)" in the logit-space memory table) is the same loss and
     dZ on logits the caller already holds: softmax_ce_on_logits below.
+
+  * gradient filtering (CCE, [LLMS] "Apple Cut Cross-Entropy (CCE)"): see
+    filtered_linear_cross_entropy for the block rule read from the page.
 
 Parity status: every function here is pinned by tests/test_oracle_pins.py
 (closed forms, invariants, finite differences and torch's fp64
@@ -193,6 +196,61 @@ def linear_cross_entropy(X, W, labels, ignore_index: int = -100, label_smoothing
         lse[idx] = lse_b
     loss = per_row if reduction == "none" else total / D
     return OracleResult(loss, lse, dX, dW, n_valid)
+
+
+@dataclasses.dataclass
+class FilteredResult:
+    result: OracleResult  # loss and LSE exact; dX and dW from the filtered dZ
+    keep: np.ndarray  # [ceil(N/tile), ceil(V/tile)] bool: tile kept
+    dZ: np.ndarray  # [N, V] the filtered dZ
+
+
+def filtered_linear_cross_entropy(X, W, labels, ignore_index: int = -100,
+                                  label_smoothing: float = 0.0, reduction: str = "mean",
+                                  grad_loss=1.0, z_loss: float = 0.0, tile: int = 256,
+                                  threshold: float = 2.0 ** -12) -> FilteredResult:
+    """Gradient filtering of Cut Cross-Entropy ([LLMS] "Apple Cut
+    Cross-Entropy (CCE)": non-target softmax values below 2^-12 are
+    negligible in bf16, and the backward skips the blocks they fill).
+
+    Reading (the pages name neither a block shape nor what happens to the
+    target term): dZ is cut into tile x tile blocks of (tokens, vocabulary)
+    at multiples of `tile`; a block is dropped, i.e. treated as zero in
+    dX = dZ W and dW = dZ^T X, when every softmax value p_ij of its valid
+    rows is below `threshold` and none of its valid rows has its label in
+    the block's columns (the target term is never dropped).  Loss and LSE
+    are those of linear_cross_entropy.  Materialises N x V: small shapes."""
+    full = linear_cross_entropy(X, W, labels, ignore_index, label_smoothing, reduction,
+                                grad_loss, z_loss=z_loss)
+    X = _as_f64(X)
+    W = _as_f64(W)
+    y = np.asarray(labels).astype(np.int64)
+    N, V = X.shape[0], W.shape[0]
+    keep_rows = valid_rows(y, V, ignore_index)
+    D = denominator(int(keep_rows.sum()), reduction)
+    scale = row_scales(grad_loss, N, D, reduction)
+    P = np.zeros((N, V))
+    dZ = np.zeros((N, V))
+    idx = np.nonzero(keep_rows)[0]
+    if idx.size:
+        Z = logits(X[idx], W)
+        lse = full.lse[idx]
+        P[idx] = np.exp(Z - lse[:, None])
+        dZ[idx] = dlogits(Z, lse, y[idx], label_smoothing, scale[idx], z_loss)
+    nt, nv = -(-N // tile), -(-V // tile)
+    keep = np.zeros((nt, nv), dtype=bool)
+    for I in range(nt):
+        r = slice(I * tile, min(N, (I + 1) * tile))
+        yl = y[r][keep_rows[r]]
+        for J in range(nv):
+            c0, c1 = J * tile, min(V, (J + 1) * tile)
+            has_label = bool(((yl >= c0) & (yl < c1)).any())
+            big = bool((P[r, c0:c1] >= threshold).any())
+            keep[I, J] = has_label or big
+            if not keep[I, J]:
+                dZ[r, c0:c1] = 0.0
+    res = OracleResult(full.loss, full.lse, dZ @ W, dZ.T @ X, full.n_valid)
+    return FilteredResult(res, keep, dZ)
 
 
 def forward(X, W, labels, ignore_index=-100, label_smoothing=0.0, reduction="mean", row_block=256,

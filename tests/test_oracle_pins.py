@@ -346,13 +346,98 @@ def check_logits_path_matches_torch():
         assert np.allclose(lse[v], torch.logsumexp(torch.tensor(Z), 1).numpy()[v], atol=1e-13)
 
 
+# ------------------------------------------------------- gradient filtering
+def check_filter_threshold_zero_keeps_everything():
+    # every softmax value is >= 0: nothing is dropped, the gradients are exact
+    X, W, y = _case(300, 6, 530, ignore=20, seed=41)
+    f = orc.filtered_linear_cross_entropy(X, W, y, label_smoothing=0.1, z_loss=1e-2, tile=64,
+                                          threshold=0.0)
+    r = orc.linear_cross_entropy(X, W, y, label_smoothing=0.1, z_loss=1e-2)
+    assert f.keep.all() and f.keep.shape == (5, 9)
+    assert np.allclose(f.result.dX, r.dX, atol=1e-14) and np.allclose(f.result.dW, r.dW, atol=1e-14)
+    assert f.result.loss == r.loss
+
+
+def _filter_brute_force(X, W, y, eps, al, tile, thr, ignore=-100):
+    # the block rule written out element by element with math.* (independent
+    # of the oracle's vectorised form)
+    N, H = X.shape
+    V = W.shape[0]
+    rows = [i for i in range(N) if y[i] != ignore]
+    D = max(len(rows), 1)
+    z = [[math.fsum(X[i, k] * W[j, k] for k in range(H)) for j in range(V)] for i in range(N)]
+    lse = {}
+    for i in rows:
+        m = max(z[i])
+        lse[i] = m + math.log(math.fsum(math.exp(v - m) for v in z[i]))
+    p = {(i, j): math.exp(z[i][j] - lse[i]) for i in rows for j in range(V)}
+    kept = {}
+    for I in range(-(-N // tile)):
+        for J in range(-(-V // tile)):
+            rr = [i for i in rows if I * tile <= i < (I + 1) * tile]
+            cc = range(J * tile, min(V, (J + 1) * tile))
+            kept[I, J] = any(y[i] in cc for i in rr) or any(p[i, j] >= thr for i in rr for j in cc)
+    dz = np.zeros((N, V))
+    for i in rows:
+        for j in range(V):
+            if kept[i // tile, j // tile]:
+                q = (1 - eps) * (j == y[i]) + eps / V
+                dz[i, j] = (p[i, j] * (1 + 2 * al * lse[i]) - q) / D
+    dX = [[math.fsum(dz[i, j] * W[j, k] for j in range(V)) for k in range(H)] for i in range(N)]
+    dW = [[math.fsum(dz[i, j] * X[i, k] for i in range(N)) for k in range(H)] for j in range(V)]
+    return kept, np.array(dX), np.array(dW)
+
+
+def check_filter_brute_force_tiny():
+    X, W, y = _case(7, 3, 9, ignore=2, seed=43, ws=0.9)
+    for thr in (0.08, 0.2):
+        f = orc.filtered_linear_cross_entropy(X, W, y, label_smoothing=0.1, z_loss=0.05, tile=2,
+                                              threshold=thr)
+        kept, dX, dW = _filter_brute_force(X, W, y, 0.1, 0.05, 2, thr)
+        assert {k: bool(f.keep[k]) for k in kept} == kept, thr
+        assert not all(kept.values()) and any(kept.values())
+        assert np.allclose(f.result.dX, dX, atol=1e-13) and np.allclose(f.result.dW, dW, atol=1e-13)
+
+
+def check_filter_dropped_entries_are_bounded():
+    # an entry of a dropped block is (p (1 + 2 alpha LSE) - eps/V) s with
+    # p < threshold: its magnitude is below s max(threshold (1 + 2 alpha LSE), eps/V)
+    # labels in the first block of columns, a flat softmax over V = 2000
+    X, W, y = _case(200, 8, 2000, ignore=10, seed=47, ws=0.2)
+    y = np.where(y == -100, y, y % 16)
+    eps, al, thr = 0.1, 0.02, 2.0 ** -9
+    f = orc.filtered_linear_cross_entropy(X, W, y, label_smoothing=eps, z_loss=al, tile=16,
+                                          threshold=thr)
+    r = orc.linear_cross_entropy(X, W, y, label_smoothing=eps, z_loss=al)
+    v = y != -100
+    Z = X[v] @ W.T
+    lse = r.lse[v]
+    full = orc.dlogits(Z, lse, y[v], eps, 1.0 / v.sum(), al)
+    diff = np.abs(full - f.dZ[v])
+    bound = np.maximum(thr * (1 + 2 * al * lse), eps / 2000) / v.sum()
+    assert (diff <= bound[:, None] + 1e-17).all()
+    assert (~f.keep).any()  # something was dropped
+
+
+def check_filter_infinite_threshold_keeps_label_blocks_only():
+    X, W, y = _case(260, 5, 1000, ignore=30, seed=53)
+    f = orc.filtered_linear_cross_entropy(X, W, y, tile=64, threshold=np.inf)
+    want = np.zeros_like(f.keep)
+    for i in np.nonzero(y != -100)[0]:
+        want[i // 64, y[i] // 64] = True
+    assert np.array_equal(f.keep, want)
+
+
 CHECKS = [check_zero_weights_give_log_V, check_two_class_closed_form, check_single_class_is_zero,
           check_uniform_logits_closed_form, check_matches_torch_cross_entropy,
           check_finite_differences, check_gradient_rows_sum_to_zero, check_ignored_rows_are_inert,
           check_shift_invariance, check_large_logits_stay_finite, check_all_ignored_gives_zero,
           check_row_block_invariance, check_zloss_zero_weights, check_zloss_two_class_closed_form,
           check_zloss_and_none_match_torch, check_zloss_none_finite_differences,
-          check_reductions_agree, check_logits_path_matches_torch]
+          check_reductions_agree, check_logits_path_matches_torch,
+          check_filter_threshold_zero_keeps_everything, check_filter_brute_force_tiny,
+          check_filter_dropped_entries_are_bounded,
+          check_filter_infinite_threshold_keeps_label_blocks_only]
 
 
 @pytest.mark.parametrize("check", CHECKS, ids=[c.__name__[6:] for c in CHECKS])
@@ -451,6 +536,47 @@ def _mutants():
     def logits_transposed_bad(X, W):
         return X @ W.T * 1.0000001
 
+    base_flt = orc.filtered_linear_cross_entropy
+
+    def _refilter(f, X, W, tile, keep):
+        # the same result with another kept-block set
+        dZ = f.dZ.copy()
+        for I in range(keep.shape[0]):
+            for J in range(keep.shape[1]):
+                if not keep[I, J]:
+                    dZ[I * tile:(I + 1) * tile, J * tile:(J + 1) * tile] = 0.0
+        res = orc.OracleResult(f.result.loss, f.result.lse, dZ @ np.asarray(W, float),
+                               dZ.T @ np.asarray(X, float), f.result.n_valid)
+        return orc.FilteredResult(res, keep, dZ)
+
+    def flt_drops_label_blocks(X, W, labels, ignore_index=-100, label_smoothing=0.0,
+                               reduction="mean", grad_loss=1.0, z_loss=0.0, tile=256,
+                               threshold=2.0 ** -12):
+        # the target term's block is dropped like any other
+        f = base_flt(X, W, labels, ignore_index, label_smoothing, reduction, grad_loss, z_loss,
+                     tile, 0.0)
+        y = np.asarray(labels)
+        V = np.asarray(W).shape[0]
+        v = y != ignore_index
+        Z = np.asarray(X, float)[v] @ np.asarray(W, float).T
+        P = np.zeros((len(y), V))
+        P[v] = np.exp(Z - f.result.lse[v][:, None])
+        keep = np.zeros_like(f.keep)
+        for I in range(keep.shape[0]):
+            for J in range(keep.shape[1]):
+                keep[I, J] = (P[I * tile:(I + 1) * tile, J * tile:(J + 1) * tile] >= threshold).any()
+        return _refilter(f, X, W, tile, keep)
+
+    def flt_shifted_blocks(X, W, labels, ignore_index=-100, label_smoothing=0.0,
+                           reduction="mean", grad_loss=1.0, z_loss=0.0, tile=256,
+                           threshold=2.0 ** -12):
+        # block flags computed one token too early (an off-by-one row index)
+        f = base_flt(X, W, labels, ignore_index, label_smoothing, reduction, grad_loss, z_loss,
+                     tile, threshold)
+        g = base_flt(np.roll(np.asarray(X), -1, axis=0), W, np.roll(np.asarray(labels), -1),
+                     ignore_index, label_smoothing, reduction, grad_loss, z_loss, tile, threshold)
+        return _refilter(f, X, W, tile, g.keep)
+
     return [("token_losses", tl_drop_smooth), ("token_losses", tl_sign),
             ("token_losses", tl_wrong_index), ("token_losses", tl_drop_zloss),
             ("token_losses", tl_zloss_not_squared), ("dlogits", dl_drop_smooth),
@@ -458,7 +584,9 @@ def _mutants():
             ("dlogits", dl_zloss_on_target), ("row_scales", rs_ignore_rows),
             ("denominator", den_all_rows),
             ("log_sum_exp", lse_no_max), ("log_sum_exp", lse_drop_max),
-            ("logits", logits_transposed_bad)]
+            ("logits", logits_transposed_bad),
+            ("filtered_linear_cross_entropy", flt_drops_label_blocks),
+            ("filtered_linear_cross_entropy", flt_shifted_blocks)]
 
 
 @pytest.mark.parametrize("name,fn", _mutants(), ids=lambda m: getattr(m, "__name__", str(m)))
