@@ -158,6 +158,7 @@ def run_side(torch, fce, wk, args, side, X, W, y, loss, lse, dX, dW, ws, step, s
     side["ms_per_step_by_chunk_schedule"] = sweep
     side["store_logits"] = store_logits_side(torch, fce, wk, args, X, W, y, loss, dX, dW, eps,
                                              stream)
+    side["filtered"] = filtered_side(torch, fce, wk, args, X, W, y, loss, dX, dW, eps, stream)
     side["ce_logits"] = ce_logits_side(torch, fce, wk, args, X, W, y, eps, stream)
     if not args.no_naive:
         try:
@@ -196,6 +197,48 @@ def store_logits_side(torch, fce, wk, args, X, W, y, loss, dX, dW, eps, stream):
             f"{res[f'chunk_{chunk}']['kernels_ms_per_step']}")
         del ws
         torch.cuda.empty_cache()
+    return res
+
+
+def filtered_side(torch, fce, wk, args, X, W, y, loss, dX, dW, eps, stream):
+    """Gradient filtering (an approximation): the filtered step against the
+    exact one on the same inputs, with the kept-tile fraction and the
+    gradients' deviation from the exact ones.  On this workload's logits and
+    on a flatter version of them (W scaled by 1/4), where most tiles hold only
+    softmax values below 2^-12."""
+    N, H = X.shape
+    V = W.shape[0]
+    k2 = args.side_steps
+    res = {"what": "filtered (CCE) vs exact recompute step; error = relative L2 of the "
+                   "filtered dX, dW against the exact ones on the same inputs"}
+    dX2, dW2 = torch.empty_like(dX), torch.empty_like(dW)
+    for name, Wc in (("workload", W), ("flat_logits_W_x0.25", W * 0.25)):
+        times = {}
+        for variant, gx, gw in (("recompute", dX, dW), ("filtered", dX2, dW2)):
+            opts = dict(ignore_index=wk.IGNORE_INDEX, label_smoothing=eps, chunk=args.chunk,
+                        variant=variant)
+            ws = fce.workspace_for(N, H, V, X.dtype, **opts)
+            fn = lambda: fce.fce_fused_fwd_bwd_ex(X, Wc, y, loss, gx, gw, ws, **opts)
+            fn()
+            fce.fce_timing_enable(True)
+            t, _ = time_steps(torch, fn, k2, stream)
+            kern = fce.fce_timing_read()
+            fce.fce_timing_enable(False)
+            times[variant] = t / k2
+            if variant == "filtered":
+                kept, total = fce.fce_get_filter_stats(ws)
+                kms = {k: round(r["total_ms"] / k2, 4) for k, r in kern.items()}
+            del ws
+        ex = ((dX2.double() - dX.double()).norm() / dX.double().norm()).item()
+        ew = ((dW2.double() - dW.double()).norm() / dW.double().norm()).item()
+        res[name] = {"ms_exact": round(times["recompute"], 4),
+                     "ms_filtered": round(times["filtered"], 4),
+                     "speedup": round(times["recompute"] / times["filtered"], 3),
+                     "kept_tiles": kept, "all_tiles": total, "filtered_kernels_ms": kms,
+                     "dX_rel_l2_vs_exact": ex, "dW_rel_l2_vs_exact": ew}
+        log(f"  filtered [{name}]: {res[name]}")
+    del dX2, dW2
+    torch.cuda.empty_cache()
     return res
 
 

@@ -95,8 +95,20 @@ typedef enum { FCE_SCHED_AUTO = 0, FCE_SCHED_TOKEN = 1, FCE_SCHED_VOCAB = 2 } fc
  *   workspace, and the backward overwrites them in place with dZ (6NVH FLOPs;
  *   llms.blog, "LinkedIn Liger Kernel").  C is `chunk` rounded up to 256
  *   tokens; the logit buffer is C x V elements, and dW is re-read once per
- *   chunk after the first. */
-typedef enum { FCE_VARIANT_RECOMPUTE = 0, FCE_VARIANT_STORE_LOGITS = 1 } fce_variant;
+ *   chunk after the first.
+ * FCE_VARIANT_FILTERED: FCE_BF16 only; the *_ex forward, backward, fused and
+ *   workspace calls.  RECOMPUTE with gradient filtering (llms.blog, "Apple Cut
+ *   Cross-Entropy (CCE)"): a 256 x 256 tile of dZ (tokens x vocabulary) in
+ *   which every softmax value is below 2^-12 and no token's label falls is
+ *   treated as zero and left out of dX and dW.  An approximation: dropped
+ *   entries are each below 2^-12 in magnitude (before the g/D scale); the loss
+ *   and LSE are exact as in RECOMPUTE.  fce_get_filter_stats reports how many
+ *   tiles were kept. */
+typedef enum {
+  FCE_VARIANT_RECOMPUTE = 0,
+  FCE_VARIANT_STORE_LOGITS = 1,
+  FCE_VARIANT_FILTERED = 2
+} fce_variant;
 
 /* The backward schedule chosen for a problem (host-only, no GPU needed). */
 typedef struct {
@@ -166,6 +178,13 @@ fce_status fce_fused_fwd_bwd(const void* X, const void* W, const int32_t* labels
  * call that used this workspace.  Synchronises `stream`. */
 fce_status fce_get_label_errors(const void* workspace, int32_t* host_count, hipStream_t stream);
 
+/* dZ tiles kept and tiles in all by the last backward with
+ * FCE_VARIANT_FILTERED that used this workspace (host outputs; token blocks
+ * whose labels are all ignored are counted as skipped).  Undefined after
+ * other calls.  Synchronises `stream`. */
+fce_status fce_get_filter_stats(const void* workspace, int64_t* kept_tiles, int64_t* all_tiles,
+                                hipStream_t stream);
+
 /* ---- Entry points with loss options (fce_options).
  *
  * The same operation as fce_forward / fce_backward / fce_fused_fwd_bwd, with
@@ -177,9 +196,10 @@ fce_status fce_get_label_errors(const void* workspace, int32_t* host_count, hipS
  * For FCE_NONE the loss output is float[N]: l_i for a valid row, 0 for an
  * ignored row, NaN for a label outside [0, V) that is not ignore_index.
  * `opt` is a host pointer; NULL is FCE_ERR_NULL.  A z_loss that is negative,
- * infinite or NaN, an unknown reduction, schedule or variant, chunk < 1, or
+ * infinite or NaN, an unknown reduction, schedule or variant, chunk < 1,
  * FCE_VARIANT_STORE_LOGITS anywhere but fce_fused_fwd_bwd_ex and
- * fce_workspace_size_ex is FCE_ERR_ARG.  With the default-valued options
+ * fce_workspace_size_ex, or FCE_VARIANT_FILTERED with FCE_F32 is FCE_ERR_ARG
+ * (the size query returns 0).  With the default-valued options
  * (z_loss 0, reduction mean or sum) they equal the entry points above
  * bitwise.  Everything else is as documented above. */
 

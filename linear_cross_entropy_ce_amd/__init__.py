@@ -23,6 +23,7 @@ from ._binding import (  # noqa: F401
     FCE_NONE,
     FCE_VARIANT_RECOMPUTE,
     FCE_VARIANT_STORE_LOGITS,
+    FCE_VARIANT_FILTERED,
     REDUCTIONS,
     VARIANTS,
     fce_backward,
@@ -36,6 +37,7 @@ from ._binding import (  # noqa: F401
     fce_workspace_size_ex,
     make_options,
     fce_get_label_errors,
+    fce_get_filter_stats,
     fce_plan,
     status_string,
     fce_timing_enable,

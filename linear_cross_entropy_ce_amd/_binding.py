@@ -32,13 +32,15 @@ SCHED_TOKEN = 1
 SCHED_VOCAB = 2
 SCHEDULES = {"auto": SCHED_AUTO, "token": SCHED_TOKEN, "vocab": SCHED_VOCAB}
 REDUCTIONS = {"mean": FCE_MEAN, "sum": FCE_SUM, "none": FCE_NONE}
-FCE_VARIANT_RECOMPUTE, FCE_VARIANT_STORE_LOGITS = 0, 1
-VARIANTS = {"recompute": FCE_VARIANT_RECOMPUTE, "store_logits": FCE_VARIANT_STORE_LOGITS}
+FCE_VARIANT_RECOMPUTE, FCE_VARIANT_STORE_LOGITS, FCE_VARIANT_FILTERED = 0, 1, 2
+VARIANTS = {"recompute": FCE_VARIANT_RECOMPUTE, "store_logits": FCE_VARIANT_STORE_LOGITS,
+            "filtered": FCE_VARIANT_FILTERED}
 
 EXPORTED = ("fce_workspace_size", "fce_plan", "fce_forward", "fce_backward", "fce_fused_fwd_bwd",
             "fce_workspace_size_ex", "fce_forward_ex", "fce_backward_ex", "fce_fused_fwd_bwd_ex",
             "fce_ce_logits_workspace_size", "fce_ce_logits",
-            "fce_get_label_errors", "fce_status_string", "fce_last_hip_error",
+            "fce_get_label_errors", "fce_get_filter_stats", "fce_status_string",
+            "fce_last_hip_error",
             "fce_timing_enable", "fce_timing_read")
 
 
@@ -129,6 +131,8 @@ def load_library(path: str = LIB_PATH):
     lib.fce_ce_logits.argtypes = [vp, i64, vp, i64, i64, i32, op, vp, vp, vp, i64, vp, vp, u64, vp]
     lib.fce_get_label_errors.restype = i32
     lib.fce_get_label_errors.argtypes = [vp, ctypes.POINTER(i32), vp]
+    lib.fce_get_filter_stats.restype = i32
+    lib.fce_get_filter_stats.argtypes = [vp, ctypes.POINTER(i64), ctypes.POINTER(i64), vp]
     lib.fce_status_string.restype = ctypes.c_char_p
     lib.fce_status_string.argtypes = [i32]
     lib.fce_last_hip_error.restype = ctypes.c_char_p
@@ -277,6 +281,15 @@ def fce_get_label_errors(workspace, stream=None) -> int:
     _check(load_library().fce_get_label_errors(_ptr(workspace), ctypes.byref(n), _stream(stream)),
            "fce_get_label_errors")
     return int(n.value)
+
+
+def fce_get_filter_stats(workspace, stream=None) -> tuple:
+    """(kept, all) dZ tiles of the last filtered backward on this workspace."""
+    kept, total = ctypes.c_int64(0), ctypes.c_int64(0)
+    _check(load_library().fce_get_filter_stats(_ptr(workspace), ctypes.byref(kept),
+                                               ctypes.byref(total), _stream(stream)),
+           "fce_get_filter_stats")
+    return int(kept.value), int(total.value)
 
 
 def fce_timing_enable(enable: bool):

@@ -101,9 +101,14 @@ fce_status check_device() {
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
+// Which fce_variant values an entry point accepts (bit v for variant v).
+constexpr unsigned kRecomputeOnly = 1u << FCE_VARIANT_RECOMPUTE;
+constexpr unsigned kSplitCalls = kRecomputeOnly | (1u << FCE_VARIANT_FILTERED);
+constexpr unsigned kAllVariants = kSplitCalls | (1u << FCE_VARIANT_STORE_LOGITS);
+
 // Options of one call, checked.  allow_none: the *_ex entry points;
-// allow_store: those that can run the store-logits variant.
-fce_status check_options(const fce_options* opt, bool allow_none, bool allow_store,
+// variants: the fce_variant values this entry point accepts.
+fce_status check_options(const fce_options* opt, bool allow_none, unsigned variants,
                          fce::LossOpts* lo) {
   if (opt == nullptr) return FCE_ERR_NULL;
   const int r = opt->reduction;
@@ -112,8 +117,7 @@ fce_status check_options(const fce_options* opt, bool allow_none, bool allow_sto
       opt->schedule != FCE_SCHED_VOCAB)
     return FCE_ERR_ARG;
   if (opt->chunk < 1) return FCE_ERR_ARG;
-  if (opt->variant != FCE_VARIANT_RECOMPUTE &&
-      !(allow_store && opt->variant == FCE_VARIANT_STORE_LOGITS))
+  if (opt->variant < 0 || opt->variant > 31 || !((variants >> opt->variant) & 1u))
     return FCE_ERR_ARG;
   const float eps = opt->label_smoothing;
   if (!(eps >= 0.0f && eps < 1.0f)) return FCE_ERR_ARG;  // also rejects NaN
@@ -128,13 +132,14 @@ fce_status check_options(const fce_options* opt, bool allow_none, bool allow_sto
 
 fce_status validate(const void* X, const void* W, const int32_t* labels, int64_t N, int64_t H,
                     int64_t V, fce_dtype dtype, const fce_options* opt, bool allow_none,
-                    bool allow_store, size_t ws_bytes, const void* ws, Plan* plan,
+                    unsigned variants, size_t ws_bytes, const void* ws, Plan* plan,
                     fce::LossOpts* lo) {
   if (N < 0 || H < 1 || V < 1) return FCE_ERR_SHAPE;
   if (W == nullptr || ws == nullptr) return FCE_ERR_NULL;
   if (N > 0 && (X == nullptr || labels == nullptr)) return FCE_ERR_NULL;
   if (dtype != FCE_F32 && dtype != FCE_BF16) return FCE_ERR_ARG;
-  if (fce_status s = check_options(opt, allow_none, allow_store, lo); s != FCE_OK) return s;
+  if (fce_status s = check_options(opt, allow_none, variants, lo); s != FCE_OK) return s;
+  if (opt->variant == FCE_VARIANT_FILTERED && dtype != FCE_BF16) return FCE_ERR_ARG;
   const int64_t vec = (dtype == FCE_BF16) ? 8 : 4;
   if (H % vec != 0) return FCE_ERR_ALIGN;
   if (!aligned16(W) || !aligned16(ws) || (N > 0 && !aligned16(X))) return FCE_ERR_ALIGN;
@@ -166,7 +171,8 @@ fce_status forward_impl(const void* X, const void* W, const int32_t* labels, int
                         hipStream_t stream) {
   Plan p;
   fce::LossOpts lo;
-  fce_status s = validate(X, W, labels, N, H, V, dtype, opt, allow_none, false, workspace_bytes,
+  fce_status s = validate(X, W, labels, N, H, V, dtype, opt, allow_none,
+                          allow_none ? kSplitCalls : kRecomputeOnly, workspace_bytes,
                           workspace, &p, &lo);
   if (s != FCE_OK) return s;
   const bool none = lo.reduction == fce::Reduction::None;
@@ -184,7 +190,8 @@ fce_status backward_impl(const void* X, const void* W, const int32_t* labels, in
                          void* workspace, size_t workspace_bytes, hipStream_t stream) {
   Plan p;
   fce::LossOpts lo;
-  fce_status s = validate(X, W, labels, N, H, V, dtype, opt, allow_none, false, workspace_bytes,
+  fce_status s = validate(X, W, labels, N, H, V, dtype, opt, allow_none,
+                          allow_none ? kSplitCalls : kRecomputeOnly, workspace_bytes,
                           workspace, &p, &lo);
   if (s != FCE_OK) return s;
   if (dW == nullptr || (N > 0 && (lse == nullptr || dX == nullptr))) return FCE_ERR_NULL;
@@ -206,8 +213,9 @@ fce_status fused_impl(const void* X, const void* W, const int32_t* labels, int64
                       hipStream_t stream) {
   Plan p;
   fce::LossOpts lo;
-  fce_status s = validate(X, W, labels, N, H, V, dtype, opt, allow_none, allow_none,
-                          workspace_bytes, workspace, &p, &lo);
+  fce_status s = validate(X, W, labels, N, H, V, dtype, opt, allow_none,
+                          allow_none ? kAllVariants : kRecomputeOnly, workspace_bytes, workspace,
+                          &p, &lo);
   if (s != FCE_OK) return s;
   const bool none = lo.reduction == fce::Reduction::None;
   if ((loss == nullptr && !(none && N == 0)) || dW == nullptr || (N > 0 && dX == nullptr))
@@ -244,7 +252,8 @@ size_t fce_workspace_size_ex(int64_t N, int64_t H, int64_t V, fce_dtype dtype,
                              const fce_options* opt) {
   if (dtype != FCE_F32 && dtype != FCE_BF16) return 0;
   fce::LossOpts lo;
-  if (check_options(opt, true, true, &lo) != FCE_OK) return 0;
+  if (check_options(opt, true, kAllVariants, &lo) != FCE_OK) return 0;
+  if (opt->variant == FCE_VARIANT_FILTERED && dtype != FCE_BF16) return 0;
   Plan p;
   if (!fce::make_plan(N, H, V, static_cast<Dtype>(dtype), opt->chunk,
                       static_cast<Schedule>(opt->schedule), &p,
@@ -345,7 +354,7 @@ fce_status fce_ce_logits(const void* Z, int64_t ldz, const int32_t* labels, int6
   if (N > 0 && (Z == nullptr || labels == nullptr || lse == nullptr)) return FCE_ERR_NULL;
   if (dtype != FCE_F32 && dtype != FCE_BF16) return FCE_ERR_ARG;
   fce::LossOpts lo;
-  if (fce_status s = check_options(opt, true, false, &lo); s != FCE_OK) return s;
+  if (fce_status s = check_options(opt, true, kRecomputeOnly, &lo); s != FCE_OK) return s;
   const bool none = lo.reduction == fce::Reduction::None;
   if (loss == nullptr && !(none && N == 0)) return FCE_ERR_NULL;
   const int64_t es = (dtype == FCE_BF16) ? 2 : 4;
@@ -382,6 +391,20 @@ fce_status fce_get_label_errors(const void* workspace, int32_t* host_count, hipS
     return from_hip(e);
   if (hipError_t e = hipStreamSynchronize(stream); e != hipSuccess) return from_hip(e);
   *host_count = h.n_invalid;
+  return FCE_OK;
+}
+
+fce_status fce_get_filter_stats(const void* workspace, int64_t* kept_tiles, int64_t* all_tiles,
+                                hipStream_t stream) {
+  if (workspace == nullptr || kept_tiles == nullptr || all_tiles == nullptr) return FCE_ERR_NULL;
+  unsigned long long h[2] = {0, 0};
+  const char* src = static_cast<const char*>(workspace) + fce::kOffFilterStats;
+  if (hipError_t e = hipMemcpyAsync(h, src, sizeof(h), hipMemcpyDeviceToHost, stream);
+      e != hipSuccess)
+    return from_hip(e);
+  if (hipError_t e = hipStreamSynchronize(stream); e != hipSuccess) return from_hip(e);
+  *kept_tiles = static_cast<int64_t>(h[0]);
+  *all_tiles = static_cast<int64_t>(h[1]);
   return FCE_OK;
 }
 

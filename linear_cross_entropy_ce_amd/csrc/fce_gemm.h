@@ -758,10 +758,17 @@ __device__ __forceinline__ void zero_acc(Acc<C>& acc) {
 // multiple of four the last trip runs on tiles past the end, whose stages
 // hold the zeros of out-of-range loads: their MFMAs add exact zeros.  Ends
 // with all DMA drained and a barrier, so the stages may be reused after it.
-template <class C, bool A_KMAJOR, bool B_KMAJOR, bool KFULL>
+//
+// MAPPED: the K loop runs over a list of kMapBlock-long K blocks instead of
+// 0 .. K-1: K counts the elements run (a multiple of kMapBlock) and K tile kt
+// reads from block kmap[kt / (kMapBlock / BK)] (a device array, read with
+// workgroup-uniform indices).
+constexpr int kMapBlock = 256;
+template <class C, bool A_KMAJOR, bool B_KMAJOR, bool KFULL, bool MAPPED = false>
 __device__ __forceinline__ void gemm_tile_dma(Acc<C>& acc, const Opnd<bf16>& A,
                                               const Opnd<bf16>& B, int m0, int n0, int K,
-                                              const DmaStages& st, int tid) {
+                                              const DmaStages& st, int tid,
+                                              const int* kmap = nullptr) {
   typedef DmaEngine<C, A_KMAJOR, B_KMAJOR, KFULL> E;
   constexpr int S = E::S, BK = E::BK;
   zero_acc(acc);
@@ -769,10 +776,20 @@ __device__ __forceinline__ void gemm_tile_dma(Acc<C>& acc, const Opnd<bf16>& A,
   if (nk <= 0) return;
   E e;
   e.init(A, B, m0, n0, tid);
+  auto koff = [&](int kt) -> int {
+    if constexpr (MAPPED) {
+      constexpr int KB = kMapBlock / BK;
+      static_assert(kMapBlock % BK == 0, "whole K tiles per mapped block");
+      return kt < nk ? kmap[kt / KB] * kMapBlock + (kt % KB) * BK : 0;
+    } else {
+      return kt * BK;
+    }
+  };
   auto issue = [&](char* stage, int kt) {
     const bool live = kt < nk;
-    e.da.load(stage, e.wave, A, kt * BK, live, KFULL);
-    e.db.load(stage + E::B_OFF, e.wave, B, kt * BK, live, KFULL);
+    const int k0 = koff(kt);
+    e.da.load(stage, e.wave, A, k0, live, KFULL);
+    e.db.load(stage + E::B_OFF, e.wave, B, k0, live, KFULL);
   };
   issue(st.s[0], 0);
   issue(st.s[1], 1);

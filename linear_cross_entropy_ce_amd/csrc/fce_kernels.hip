@@ -324,18 +324,30 @@ struct DzArgs {
   T* dz;
   int64_t ldz;
   const int32_t* flag;  // this token block's "has a valid label" flag
+  uint8_t* keep;        // FILTER: [tok_tiles][voc_tiles] tile kept (1) or skipped (0)
 };
 
-template <class C, bool KFULL>
+// Gradient filtering ("Cut Cross-Entropy", llms.blog, "Apple Cut
+// Cross-Entropy (CCE)"): a dZ tile is skipped when every softmax value in it
+// is below 2^-12 and it holds no label of its tokens (the target term is
+// never dropped).
+constexpr float kFilterP = 0.000244140625f;  // 2^-12
+
+// FILTER: also decide whether the tile is kept (see kFilterP), record it in
+// keep[], and store only kept tiles.
+template <class C, bool KFULL, bool FILTER>
 __global__ __launch_bounds__(C::NT) void k_bwd_dz(DzArgs<typename C::Elem> a) {
   typedef typename C::Elem T;
-  if (*a.flag == 0) return;  // every label of this token block is ignored
-  FCE_DMA_STAGES(lds);
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wm = wave / C::WAVES_N, wn = wave % C::WAVES_N;
   int vt, tt;
   grouped_tile(xcd_remap(blockIdx.x, a.voc_tiles * a.tok_tiles), a.voc_tiles, a.tok_tiles,
                a.group_m, vt, tt);
+  if (*a.flag == 0) {  // every label of this token block is ignored
+    if (FILTER && threadIdx.x == 0) a.keep[tt * a.voc_tiles + vt] = 0;
+    return;
+  }
+  FCE_DMA_STAGES(lds);
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave / C::WAVES_N, wn = wave % C::WAVES_N;
   const int m0 = vt * C::BM, n0 = tt * C::BN;
   const Opnd<T> A{a.W, a.H, a.nvoc, a.H};
   const Opnd<T> B{a.X, a.H, a.ntok, a.H};
@@ -345,6 +357,54 @@ __global__ __launch_bounds__(C::NT) void k_bwd_dz(DzArgs<typename C::Elem> a) {
   typedef AccMap<C> Map;
   const float eps_v = a.eps / static_cast<float>(a.V);
   const float one_m_eps = 1.0f - a.eps;
+  if constexpr (FILTER) {
+    // dZ in place of the accumulators, then one kept flag for the tile
+    bool keep = false;
+#pragma unroll
+    for (int fn = 0; fn < C::FN; ++fn) {
+      const int tl = n0 + wn * C::WTN + fn * C::NB + Map::col(lane);
+      const int y = tl < a.ntok ? a.labels[tl] : a.ignore;
+      const bool valid = tl < a.ntok && label_ok(y, a.ignore, a.V);
+      const float L = valid ? a.lse[tl] : 0.0f;
+      const int yl = valid ? y - a.voc0 : -1;
+      const float zf = 1.0f + 2.0f * a.zloss * L;
+      const float gi = (valid && a.gtok) ? a.gtok[tl] : 1.0f;
+      keep |= yl >= m0 && yl < m0 + C::BM;
+#pragma unroll
+      for (int fm = 0; fm < C::FM; ++fm)
+#pragma unroll
+        for (int i = 0; i < C::NV; ++i) {
+          const int v = m0 + wm * C::WTM + fm * C::MB + Map::row(lane, i >> 2) + (i & 3);
+          const bool in = valid && v < a.nvoc;
+          const float e = hw_exp2((acc.v[fm][fn][i] - L) * kLog2e);
+          keep |= in && e >= kFilterP;
+          float p = e * zf - eps_v;
+          if (v == yl) p -= one_m_eps;
+          acc.v[fm][fn][i] = in ? p * gi : 0.0f;
+        }
+    }
+    __shared__ int s_keep[C::NT / 64];
+    const bool wave_keep = __ballot(keep) != 0;  // every lane votes
+    if (lane == 0) s_keep[wave] = wave_keep;
+    __syncthreads();
+    int any = 0;
+#pragma unroll
+    for (int w = 0; w < C::NT / 64; ++w) any |= s_keep[w];
+    if (tid == 0) a.keep[tt * a.voc_tiles + vt] = static_cast<uint8_t>(any);
+    if (!any) return;
+#pragma unroll
+    for (int fn = 0; fn < C::FN; ++fn) {
+      const int tl = n0 + wn * C::WTN + fn * C::NB + Map::col(lane);
+      T* row = a.dz + static_cast<int64_t>(tl) * a.ldz;
+#pragma unroll
+      for (int fm = 0; fm < C::FM; ++fm)
+#pragma unroll
+        for (int g = 0; g < Map::NGRP; ++g)
+          store4(row + m0 + wm * C::WTM + fm * C::MB + Map::row(lane, g), acc.v[fm][fn][4 * g],
+                 acc.v[fm][fn][4 * g + 1], acc.v[fm][fn][4 * g + 2], acc.v[fm][fn][4 * g + 3]);
+    }
+    return;
+  }
 #pragma unroll
   for (int fn = 0; fn < C::FN; ++fn) {
     const int tl = n0 + wn * C::WTN + fn * C::NB + Map::col(lane);
@@ -393,6 +453,11 @@ struct GradArgs {
   // and writes its own output at out + z * split_stride
   int ksplit;
   int64_t split_stride;
+  // FILTER: the kept K blocks (kMapBlock long) of output row tile tm are
+  // klist[tm * list_ld + 0 .. kcount[tm]-1], ascending
+  const int* klist;
+  const int* kcount;
+  int list_ld;
 };
 
 // The part of an operand from contraction index k0 on.
@@ -402,7 +467,7 @@ __device__ __forceinline__ Opnd<T> opnd_from_k(const Opnd<T>& o, int k0) {
                  o.mn_ext, o.k_ext - k0};
 }
 
-template <class C, bool A_KMAJOR>
+template <class C, bool A_KMAJOR, bool FILTER>
 __global__ __launch_bounds__(C::NT) void k_bwd_grad(GradArgs<typename C::Elem> a) {
   typedef typename C::Elem T;
   FCE_DMA_STAGES(lds);
@@ -425,7 +490,19 @@ __global__ __launch_bounds__(C::NT) void k_bwd_grad(GradArgs<typename C::Elem> a
     out += static_cast<int64_t>(blockIdx.y) * a.split_stride;
   }
   Acc<C> acc;
-  if (skip) {
+  if constexpr (FILTER) {
+    static_assert(sizeof(T) == 2 && C::BM == kMapBlock && C::BN == kMapBlock,
+                  "filtered products: bf16 tiles one kept block long");
+    const int cnt = skip ? 0 : a.kcount[tm];
+    if (cnt == 0 && a.accumulate) return;
+    if (cnt == 0)
+      zero_acc(acc);
+    else if (cnt == (K + kMapBlock - 1) / kMapBlock)  // every block kept: the plain K loop
+      gemm_any<C, A_KMAJOR, false, true>(acc, A, B, m0, n0, K, lds, tid);
+    else
+      gemm_tile_dma<C, A_KMAJOR, false, true, true>(acc, A, B, m0, n0, cnt * kMapBlock, lds, tid,
+                                                    a.klist + tm * a.list_ld);
+  } else if (skip) {
     zero_acc(acc);
   } else {
     // K is the token count (dW, no K-major operand) or the block's vocabulary
@@ -473,6 +550,33 @@ __global__ __launch_bounds__(C::NT) void k_bwd_grad(GradArgs<typename C::Elem> a
             tile[static_cast<int64_t>(r) * a.ldo + c] = old[j][fn][i] + s * acc.v[f0 + j][fn][i];
         }
   }
+}
+
+// Kept-block lists of one logit block for the filtered products: per token
+// tile (rows of dX) the kept vocabulary tiles, per vocabulary tile (rows of
+// dW) the kept token tiles, ascending.  stats[0] += kept tiles, stats[1] +=
+// all tiles of the block.
+__global__ __launch_bounds__(256) void k_filter_lists(const uint8_t* __restrict__ keep, int tt,
+                                                      int vt, int* __restrict__ rowlist,
+                                                      int* __restrict__ rowcnt,
+                                                      int* __restrict__ collist,
+                                                      int* __restrict__ colcnt,
+                                                      unsigned long long* __restrict__ stats) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < tt) {
+    int c = 0;
+    for (int v = 0; v < vt; ++v)
+      if (keep[i * vt + v]) rowlist[i * vt + c++] = v;
+    rowcnt[i] = c;
+    atomicAdd(&stats[0], static_cast<unsigned long long>(c));
+  } else if (i < tt + vt) {
+    const int j = i - tt;
+    int c = 0;
+    for (int t = 0; t < tt; ++t)
+      if (keep[t * vt + j]) collist[j * tt + c++] = t;
+    colcnt[j] = c;
+  }
+  if (i == 0) atomicAdd(&stats[1], static_cast<unsigned long long>(tt) * vt);
 }
 
 // dX rows of one block from the split partials: out (=|+=) sum over z of
@@ -752,6 +856,15 @@ hipError_t run_forward(const Plan& p, const T* X, const T* W, const int32_t* lab
   return hipSuccess;
 }
 
+// Kept-block lists of one logit block (filtered products).
+struct FilterLists {
+  const int* rowlist;  // [tt][vt]: per token tile, kept vocabulary tiles
+  const int* rowcnt;
+  const int* collist;  // [vt][tt]: per vocabulary tile, kept token tiles
+  const int* colcnt;
+  int tt, vt;
+};
+
 // The two gradient products of one logit block: dZ is [ntok][>= nvoc
 // rounded up to the tile] at dz with row pitch ldz, for tokens tok0.. and
 // vocabulary columns voc0...  acc_dw / acc_dx: add to the previous block's
@@ -761,8 +874,8 @@ template <typename T>
 hipError_t grad_products(const Plan& p, const T* X, const T* W, const T* dz, int64_t ldz,
                          int64_t tok0, int ntok, int64_t voc0, int nvoc, bool acc_dw, bool acc_dx,
                          const Ctrl* ctrl, const int32_t* flag, float* dX, float* dW,
-                         float* dxpart, hipStream_t st, KernelTimer* timer, const char* name_dw,
-                         const char* name_dx) {
+                         float* dxpart, const FilterLists* fl, hipStream_t st,
+                         KernelTimer* timer, const char* name_dw, const char* name_dx) {
   typedef typename ShapeOf<T>::C C;
   const int64_t H = p.H;
   const int h_tiles = cdiv_i(H, C::BN);
@@ -788,8 +901,18 @@ hipError_t grad_products(const Plan& p, const T* X, const T* W, const T* dz, int
   gw.flag = flag;
   gw.ksplit = ntok;
   gw.split_stride = 0;
+  gw.klist = fl ? fl->collist : nullptr;
+  gw.kcount = fl ? fl->colcnt : nullptr;
+  gw.list_ld = fl ? fl->tt : 0;
   timer->begin(name_dw, blk_flops, st);
-  k_bwd_grad<C, false><<<voc_tiles * h_tiles, C::NT, 0, st>>>(gw);
+  if constexpr (sizeof(T) == 2) {
+    if (fl)
+      k_bwd_grad<C, false, true><<<voc_tiles * h_tiles, C::NT, 0, st>>>(gw);
+    else
+      k_bwd_grad<C, false, false><<<voc_tiles * h_tiles, C::NT, 0, st>>>(gw);
+  } else {
+    k_bwd_grad<C, false, false><<<voc_tiles * h_tiles, C::NT, 0, st>>>(gw);
+  }
   FCE_CHECK_LAUNCH();
   timer->end(st);
 
@@ -810,9 +933,12 @@ hipError_t grad_products(const Plan& p, const T* X, const T* W, const T* dz, int
   gx.flag = flag;
   gx.ksplit = nvoc_cov;
   gx.split_stride = 0;
+  gx.klist = fl ? fl->rowlist : nullptr;
+  gx.kcount = fl ? fl->rowcnt : nullptr;
+  gx.list_ld = fl ? fl->vt : 0;
   // split over the vocabulary when the plan asks for it: whole tiles per split
   const int ksplit = cdiv_i(cdiv_i(nvoc_cov, static_cast<int>(p.dx_splits)), C::BM) * C::BM;
-  const int splits = cdiv_i(nvoc_cov, ksplit);
+  const int splits = fl ? 1 : cdiv_i(nvoc_cov, ksplit);
   if (splits > 1) {
     gx.ksplit = ksplit;
     gx.out = dxpart;
@@ -820,7 +946,14 @@ hipError_t grad_products(const Plan& p, const T* X, const T* W, const T* dz, int
     gx.split_stride = static_cast<int64_t>(ntok) * H;
   }
   timer->begin(name_dx, blk_flops, st);
-  k_bwd_grad<C, true><<<dim3(tok_tiles * h_tiles, splits), C::NT, 0, st>>>(gx);
+  if constexpr (sizeof(T) == 2) {
+    if (fl)
+      k_bwd_grad<C, true, true><<<tok_tiles * h_tiles, C::NT, 0, st>>>(gx);
+    else
+      k_bwd_grad<C, true, false><<<dim3(tok_tiles * h_tiles, splits), C::NT, 0, st>>>(gx);
+  } else {
+    k_bwd_grad<C, true, false><<<dim3(tok_tiles * h_tiles, splits), C::NT, 0, st>>>(gx);
+  }
   FCE_CHECK_LAUNCH();
   timer->end(st);
   if (splits > 1) {
@@ -845,6 +978,16 @@ hipError_t run_backward(const Plan& p, const T* X, const T* W, const int32_t* la
   T* dz = reinterpret_cast<T*>(ws + p.off_scratch);
   float* dxpart = reinterpret_cast<float*>(ws + p.off_dxpart);
   const int64_t N = p.N, H = p.H, V = p.V;
+  const bool filt = sizeof(T) == 2 && p.variant == Variant::Filtered;
+  uint8_t* keep = reinterpret_cast<uint8_t*>(ws + p.off_keep);
+  unsigned long long* fstats = reinterpret_cast<unsigned long long*>(ws + p.off_ctrl +
+                                                                     kOffFilterStats);
+  if (filt) {  // kept / all tile counters of this call
+    timer->begin("fill_zero", 0.0, st);
+    k_fill_zero<<<1, 256, 0, st>>>(reinterpret_cast<float*>(fstats), 4);
+    FCE_CHECK_LAUNCH();
+    timer->end(st);
+  }
   if (N == 0) {
     timer->begin("fill_zero", 0.0, st);
     k_fill_zero<<<1024, 256, 0, st>>>(dW, V * H);
@@ -865,18 +1008,44 @@ hipError_t run_backward(const Plan& p, const T* X, const T* W, const int32_t* la
       DzArgs<T> da{X + tok0 * H, W + voc0 * H, labels + tok0, lse + tok0, ntok, nvoc,
                    static_cast<int>(voc0), static_cast<int>(H), static_cast<int>(V), ignore, eps,
                    o.zloss, grad_tok ? grad_tok + tok0 : nullptr, voc_tiles, tok_tiles, 4, dz,
-                   p.ldz, flags + ia};
+                   p.ldz, flags + ia, keep};
       timer->begin("bwd_dz", blk_flops, st);
-      if (H % 32 == 0)
-        k_bwd_dz<C, true><<<voc_tiles * tok_tiles, C::NT, 0, st>>>(da);
-      else
-        k_bwd_dz<C, false><<<voc_tiles * tok_tiles, C::NT, 0, st>>>(da);
+      if constexpr (sizeof(T) == 2) {
+        if (filt) {
+          if (H % 32 == 0)
+            k_bwd_dz<C, true, true><<<voc_tiles * tok_tiles, C::NT, 0, st>>>(da);
+          else
+            k_bwd_dz<C, false, true><<<voc_tiles * tok_tiles, C::NT, 0, st>>>(da);
+        } else if (H % 32 == 0) {
+          k_bwd_dz<C, true, false><<<voc_tiles * tok_tiles, C::NT, 0, st>>>(da);
+        } else {
+          k_bwd_dz<C, false, false><<<voc_tiles * tok_tiles, C::NT, 0, st>>>(da);
+        }
+      } else {
+        if (H % 32 == 0)
+          k_bwd_dz<C, true, false><<<voc_tiles * tok_tiles, C::NT, 0, st>>>(da);
+        else
+          k_bwd_dz<C, false, false><<<voc_tiles * tok_tiles, C::NT, 0, st>>>(da);
+      }
       FCE_CHECK_LAUNCH();
       timer->end(st);
 
+      FilterLists fl{reinterpret_cast<const int*>(ws + p.off_rowlist),
+                     reinterpret_cast<const int*>(ws + p.off_rowcnt),
+                     reinterpret_cast<const int*>(ws + p.off_collist),
+                     reinterpret_cast<const int*>(ws + p.off_colcnt), tok_tiles, voc_tiles};
+      if (filt) {
+        timer->begin("filter_lists", 0.0, st);
+        k_filter_lists<<<cdiv_i(tok_tiles + voc_tiles, 256), 256, 0, st>>>(
+            keep, tok_tiles, voc_tiles, reinterpret_cast<int*>(ws + p.off_rowlist),
+            reinterpret_cast<int*>(ws + p.off_rowcnt), reinterpret_cast<int*>(ws + p.off_collist),
+            reinterpret_cast<int*>(ws + p.off_colcnt), fstats);
+        FCE_CHECK_LAUNCH();
+        timer->end(st);
+      }
       const hipError_t e = grad_products<T>(p, X, W, dz, p.ldz, tok0, ntok, voc0, nvoc, ia > 0,
-                                            ib > 0, ctrl, flags + ia, dX, dW, dxpart, st, timer,
-                                            "bwd_dw", "bwd_dx");
+                                            ib > 0, ctrl, flags + ia, dX, dW, dxpart,
+                                            filt ? &fl : nullptr, st, timer, "bwd_dw", "bwd_dx");
       if (e != hipSuccess) return e;
     }
   }
@@ -938,8 +1107,8 @@ hipError_t run_fused_store(const Plan& p, const T* X, const T* W, const int32_t*
     FCE_CHECK_LAUNCH();
     timer->end(st);
     const hipError_t e = grad_products<T>(p, X, W, zs, p.ldz, tok0, ntok, 0, static_cast<int>(V),
-                                          ia > 0, false, ctrl, flags + ia, dX, dW, dxpart, st,
-                                          timer, "sl_dw", "sl_dx");
+                                          ia > 0, false, ctrl, flags + ia, dX, dW, dxpart,
+                                          nullptr, st, timer, "sl_dw", "sl_dx");
     if (e != hipSuccess) return e;
   }
   if (none) return hipSuccess;

@@ -59,7 +59,11 @@ double model_time(const Plan& p, int64_t CN, int64_t CV, int64_t a, int64_t b) {
 bool make_plan(int64_t N, int64_t H, int64_t V, Dtype dtype, int64_t chunk, Schedule sched,
                Plan* out, Variant variant) {
   if (!out || N < 0 || H < 1 || V < 1 || chunk < 1) return false;
-  if (variant != Variant::Recompute && variant != Variant::StoreLogits) return false;
+  if (variant != Variant::Recompute && variant != Variant::StoreLogits &&
+      variant != Variant::Filtered)
+    return false;
+  // the filtered products walk kept blocks of one bf16 tile
+  if (variant == Variant::Filtered && dtype != Dtype::BF16) return false;
   if (sched != Schedule::Auto && sched != Schedule::Token && sched != Schedule::Vocab) return false;
   // Index arithmetic inside the kernels uses 64-bit row offsets, but tile
   // coordinates are 32-bit: keep every extent comfortably inside int32.
@@ -183,7 +187,7 @@ bool make_plan(int64_t N, int64_t H, int64_t V, Dtype dtype, int64_t chunk, Sche
     constexpr int64_t kMinSplitTiles = 4;
     const int64_t grid = cdiv(std::min(p.CN, N), BN) * cdiv(H, BN);
     const int64_t ktiles = cdiv(std::min(p.CV, V), BM);
-    if (grid < kNumCUs)
+    if (grid < kNumCUs && variant != Variant::Filtered)
       p.dx_splits = std::max<int64_t>(
           1, std::min(cdiv(kNumCUs, grid), ktiles / kMinSplitTiles));
   }
@@ -216,6 +220,21 @@ bool make_plan(int64_t N, int64_t H, int64_t V, Dtype dtype, int64_t chunk, Sche
                                            static_cast<size_t>(H) * sizeof(float)
                                      : 0;
   off = align_up(off + p.dxpart_bytes);
+  if (variant == Variant::Filtered) {
+    p.filt_tt = cdiv(std::min(p.CN, std::max<int64_t>(N, 1)), BN);
+    p.filt_vt = cdiv(std::min(p.CV, V), BM);
+    const size_t tiles = static_cast<size_t>(p.filt_tt * p.filt_vt);
+    p.off_keep = off;
+    off = align_up(off + tiles);
+    p.off_rowlist = off;
+    off = align_up(off + 4 * tiles);
+    p.off_collist = off;
+    off = align_up(off + 4 * tiles);
+    p.off_rowcnt = off;
+    off = align_up(off + 4 * static_cast<size_t>(p.filt_tt));
+    p.off_colcnt = off;
+    off = align_up(off + 4 * static_cast<size_t>(p.filt_vt));
+  }
   p.total = off;
   *out = p;
   return true;

@@ -13,7 +13,9 @@ enum class Schedule : int { Auto = 0, Token = 1, Vocab = 2 };
 // Recompute: the backward rebuilds each logit block from X and W.
 // StoreLogits: the forward keeps a chunk's logits (chunk tokens x all V) in
 // the workspace and the backward turns them into dZ in place.
-enum class Variant : int { Recompute = 0, StoreLogits = 1 };
+// Filtered: Recompute, with dZ tiles whose softmax values are all below
+// 2^-12 (and that hold no label) left out of the gradient products (bf16).
+enum class Variant : int { Recompute = 0, StoreLogits = 1, Filtered = 2 };
 
 struct Plan {
   int64_t N = 0, H = 0, V = 0;
@@ -40,6 +42,9 @@ struct Plan {
   // workspace layout (byte offsets, 256-byte aligned)
   size_t off_ctrl = 0, off_flags = 0, off_part = 0, off_blockloss = 0, off_lse = 0,
          off_scratch = 0, off_dxpart = 0, total = 0;
+  // Filtered: per logit block, kept flags [tt][vt] and the kept-block lists
+  int64_t filt_tt = 0, filt_vt = 0;
+  size_t off_keep = 0, off_rowlist = 0, off_rowcnt = 0, off_collist = 0, off_colcnt = 0;
   size_t scratch_bytes = 0, partial_bytes = 0, dxpart_bytes = 0;
   int64_t n_loss_blocks = 0;
   int64_t grad_rmw_bytes = 0;
@@ -54,6 +59,9 @@ struct Ctrl {
 };
 
 constexpr int kLossBlock = 256;  // tokens per block of the loss reduction
+// Filtered: two uint64 counters (kept tiles, all tiles) inside the control slot
+constexpr size_t kOffFilterStats = 64;
+static_assert(sizeof(Ctrl) <= kOffFilterStats, "filter counters after the control block");
 
 // Returns false if the arguments are invalid (shapes, chunk, overflow).
 bool make_plan(int64_t N, int64_t H, int64_t V, Dtype dtype, int64_t chunk, Schedule sched,

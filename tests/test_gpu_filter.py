@@ -1,0 +1,186 @@
+"""GPU parity of the gradient-filtered backward (FCE_VARIANT_FILTERED)
+against the oracle's filtered_linear_cross_entropy: the kept-tile count
+exactly, the loss, dX and dW to the bf16 tolerances."""
+import numpy as np
+import pytest
+
+torch = pytest.importorskip("torch")
+
+import linear_cross_entropy_ce_amd as fce  # noqa: E402
+import oracle.fce_oracle as orc  # noqa: E402
+import workloads as wk  # noqa: E402
+
+pytestmark = pytest.mark.gpu
+
+THR = 2.0 ** -12
+TILE = 256
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _device():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    fce.load_library()
+    torch.cuda.set_device(0)
+
+
+def rel_l2(a, b):
+    a = np.asarray(a, dtype=np.float64)
+    b = np.asarray(b, dtype=np.float64)
+    nb = np.linalg.norm(b)
+    return np.linalg.norm(a - b) / (nb if nb > 0 else 1.0)
+
+
+def structured(seed, N=700, H=264, V=12000, hot=(5, 17, 30)):
+    """Inputs whose every block decision is clear of the threshold: a flat
+    softmax background (W ~ N(0, 0.01^2): p ~ 1/V, far below 2^-12), three
+    vocabulary tiles of large weights (p far above it for most tokens), one
+    token tile with flat logits everywhere, labels in the first two
+    vocabulary tiles, 5% of the rows ignored.  bf16-exact values."""
+    g = np.random.default_rng(seed)
+    X = g.standard_normal((N, H)).astype(np.float32)
+    X[256:512] *= 0.01
+    W = (g.standard_normal((V, H)) * 0.01).astype(np.float32)
+    for t in hot:
+        W[t * TILE:(t + 1) * TILE] *= 60.0
+    y = g.integers(0, 2 * TILE, N).astype(np.int32)
+    y[g.choice(N, N // 20, replace=False)] = -100
+    X = wk.bf16_bits_to_f32(wk.round_to_bf16_bits(X))
+    W = wk.bf16_bits_to_f32(wk.round_to_bf16_bits(W))
+    return X, W, y
+
+
+def sparse_hot(seed, N=700, H=264, V=12000, spots=40):
+    """A flat background with `spots` single hot entries: W_j points along
+    X_i, so z_ij ~ 0.15 |X_i| ~ 2.4 (p ~ 4 x 2^-12) while every other
+    token's logit against W_j stays below the threshold.  A tile is kept by
+    one entry held by one lane; labels in the first two vocabulary tiles."""
+    g = np.random.default_rng(seed)
+    X = g.standard_normal((N, H)).astype(np.float32)
+    W = (g.standard_normal((V, H)) * 0.01).astype(np.float32)
+    ii = g.choice(N, spots, replace=False)
+    jj = g.choice(np.arange(2 * TILE, V), spots, replace=False)
+    for i, j in zip(ii, jj):
+        W[j] = 0.15 * X[i] / np.linalg.norm(X[i])
+    y = g.integers(0, 2 * TILE, N).astype(np.int32)
+    y[g.choice(np.setdiff1d(np.arange(N), ii), N // 20, replace=False)] = -100
+    X = wk.bf16_bits_to_f32(wk.round_to_bf16_bits(X))
+    W = wk.bf16_bits_to_f32(wk.round_to_bf16_bits(W))
+    return X, W, y
+
+
+def to_dev(X, W, y):
+    b = lambda a: torch.from_numpy(a).to(torch.bfloat16).cuda()  # exact: values are bf16
+    return b(X), b(W), torch.from_numpy(y).cuda()
+
+
+def run(X, W, y, split=False, grad=None, **opts):
+    N, H = X.shape
+    V = W.shape[0]
+    none = opts.get("reduction", "mean") == "none"
+    ws = fce.workspace_for(N, H, V, torch.bfloat16, **opts)
+    loss = torch.full((N if none else 1,), float("nan"), device="cuda")
+    lse = torch.full((N,), float("nan"), device="cuda")
+    dX = torch.full((N, H), float("nan"), device="cuda")
+    dW = torch.full((V, H), float("nan"), device="cuda")
+    if split:
+        g = None if grad is None else torch.tensor(np.atleast_1d(grad), dtype=torch.float32,
+                                                   device="cuda")
+        fce.fce_forward_ex(X, W, y, loss, lse, ws, **opts)
+        fce.fce_backward_ex(X, W, y, lse, g, dX, dW, ws, **opts)
+    else:
+        fce.fce_fused_fwd_bwd_ex(X, W, y, loss, dX, dW, ws, **opts)
+    torch.cuda.synchronize()
+    kept, total = fce.fce_get_filter_stats(ws) if opts.get("variant") == "filtered" else (0, 0)
+    return dict(loss=loss.cpu().numpy(), dX=dX.cpu().numpy(), dW=dW.cpu().numpy(), kept=kept,
+                total=total)
+
+
+def _clear_of_threshold(X, W, y, **kw):
+    lo = orc.filtered_linear_cross_entropy(X, W, y, threshold=THR / 1.05, **kw).keep
+    hi = orc.filtered_linear_cross_entropy(X, W, y, threshold=THR * 1.05, **kw).keep
+    return np.array_equal(lo, hi)
+
+
+@pytest.mark.parametrize("chunk", [1024, 200])
+def test_filtered_against_oracle(chunk):
+    # chunk 200: token blocks of 256 and vocabulary blocks, so the tile grid
+    # spans several logit blocks
+    X, W, y = structured(0)
+    kw = dict(label_smoothing=0.05, z_loss=1e-3)
+    assert _clear_of_threshold(X, W, y, **kw)
+    ref = orc.filtered_linear_cross_entropy(X, W, y, threshold=THR, **kw)
+    full = orc.linear_cross_entropy(X, W, y, **kw)
+    # the filter matters on these inputs: vocabulary tiles dropped for every
+    # token tile have dW rows of exactly zero, where the exact dW has none
+    gone = np.repeat(~ref.keep.any(axis=0), TILE)[:W.shape[0]]
+    assert 0 < ref.keep.sum() < ref.keep.size and gone.any()
+    assert not ref.result.dW[gone].any() and np.abs(full.dW[gone]).min() > 0
+    got = run(*to_dev(X, W, y), chunk=chunk, variant="filtered", **kw)
+    assert not got["dW"][gone].any()
+    le = abs(got["loss"][0] - ref.result.loss) / abs(ref.result.loss)
+    ex, ew = rel_l2(got["dX"], ref.result.dX), rel_l2(got["dW"], ref.result.dW)
+    print(f"[filtered chunk {chunk}] kept {got['kept']}/{got['total']} (oracle "
+          f"{int(ref.keep.sum())}/{ref.keep.size}); loss {le:.2e}; dX {ex:.2e}; dW {ew:.2e}",
+          flush=True)
+    assert got["kept"] == int(ref.keep.sum()) and got["total"] == ref.keep.size
+    assert le <= 2e-3 and ex <= 2e-2 and ew <= 2e-2
+    assert np.all(got["dX"][y == -100] == 0.0)
+
+
+def test_filtered_isolated_hot_entries():
+    # every kept tile outside the label tiles is kept by a single entry, so
+    # each lane's vote counts
+    X, W, y = sparse_hot(0)
+    assert _clear_of_threshold(X, W, y)
+    ref = orc.filtered_linear_cross_entropy(X, W, y, threshold=THR)
+    v = y != -100
+    Z = X[v].astype(np.float64) @ W.T.astype(np.float64)
+    big = np.exp(Z - ref.result.lse[v][:, None]) >= THR
+    assert 20 <= big.sum() <= 40  # the planted entries, nothing else
+    got = run(*to_dev(X, W, y), chunk=1024, variant="filtered")
+    print(f"[filtered sparse] kept {got['kept']}/{got['total']} (oracle {int(ref.keep.sum())})",
+          flush=True)
+    assert got["kept"] == int(ref.keep.sum())
+    assert rel_l2(got["dX"], ref.result.dX) <= 2e-2 and rel_l2(got["dW"], ref.result.dW) <= 2e-2
+
+
+def test_filtered_split_calls_per_token_gradient():
+    X, W, y = structured(1)
+    g = np.random.default_rng(7).uniform(-2.0, 2.0, X.shape[0]).astype(np.float32)
+    kw = dict(reduction="none", z_loss=1e-3)
+    assert _clear_of_threshold(X, W, y, **kw)
+    ref = orc.filtered_linear_cross_entropy(X, W, y, grad_loss=g.astype(np.float64),
+                                            threshold=THR, **kw)
+    got = run(*to_dev(X, W, y), split=True, grad=g, chunk=512, variant="filtered", **kw)
+    valid = y != -100
+    assert got["kept"] == int(ref.keep.sum())
+    assert np.abs(got["loss"] - ref.result.loss).max() <= 2e-3 * np.abs(ref.result.loss[valid]).mean()
+    assert rel_l2(got["dX"], ref.result.dX) <= 2e-2 and rel_l2(got["dW"], ref.result.dW) <= 2e-2
+
+
+def test_filtered_all_ignored_block_counts_as_skipped():
+    X, W, y = structured(2)
+    y[:256] = -100  # the first token tile has no valid row
+    ref = orc.filtered_linear_cross_entropy(X, W, y, threshold=THR)
+    got = run(*to_dev(X, W, y), chunk=256, variant="filtered")
+    assert got["kept"] == int(ref.keep.sum()) and not ref.keep[0].any()
+    assert rel_l2(got["dX"], ref.result.dX) <= 2e-2 and rel_l2(got["dW"], ref.result.dW) <= 2e-2
+
+
+def test_filtered_full_size_llama3_shape():
+    # 8192 x 4096 x 128256: at this workload's logit spread nearly every
+    # tile holds a softmax value above 2^-12, so the filtered gradients must
+    # match the stored oracle values like the exact path's do.
+    import test_gpu_parity as tp
+
+    k = 3
+    g = tp._golden(k)
+    inp = tp._draw_cached(k)
+    X, W, yt = wk.to_torch(inp, "cuda")
+    got = run(X, W, yt, chunk=1024, variant="filtered")
+    print(f"[llama3-8b filtered] kept {got['kept']}/{got['total']}", flush=True)
+    got["loss"] = float(got["loss"][0])
+    got["lse"] = tp.run_ex_lse(inp)
+    tp.check_golden(inp, g, got)
+    assert 0 < got["kept"] <= got["total"] == 32 * 501  # ceil(N/256) x ceil(V/256)

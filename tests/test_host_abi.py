@@ -176,7 +176,7 @@ def _opts(**kw):
 @pytest.mark.parametrize("kw,status", [
     (dict(z_loss=-1e-3), B.FCE_ERR_ARG), (dict(z_loss=float("nan")), B.FCE_ERR_ARG),
     (dict(z_loss=float("inf")), B.FCE_ERR_ARG), (dict(reduction=3), B.FCE_ERR_ARG),
-    (dict(variant=2), B.FCE_ERR_ARG), (dict(chunk=0), B.FCE_ERR_ARG), (dict(schedule=5), B.FCE_ERR_ARG),
+    (dict(variant=3), B.FCE_ERR_ARG), (dict(chunk=0), B.FCE_ERR_ARG), (dict(schedule=5), B.FCE_ERR_ARG),
     (dict(label_smoothing=1.0), B.FCE_ERR_ARG)])
 def test_ex_rejects_bad_options(kw, status):
     lib = B.load_library()
@@ -207,6 +207,26 @@ def test_store_logits_variant_where_accepted_and_its_workspace():
                                FAKE, FAKE, sto, None) == B.FCE_ERR_ARG
     assert lib.fce_ce_logits(FAKE, V, FAKE, N, V, 1, ctypes.byref(o), FAKE, FAKE, None, 0, None,
                              FAKE, 1 << 20, None) == B.FCE_ERR_ARG
+
+
+def test_filtered_variant_is_bf16_only_and_not_for_given_logits():
+    lib = B.load_library()
+    N, H, V = 1000, 64, 5000
+    o = _opts(chunk=300, variant=2)
+    bf = lib.fce_workspace_size_ex(N, H, V, 1, ctypes.byref(o))
+    assert bf >= lib.fce_workspace_size_ex(N, H, V, 1, ctypes.byref(_opts(chunk=300)))
+    assert lib.fce_workspace_size_ex(N, H, V, 0, ctypes.byref(o)) == 0
+    for dtype, want in ((0, B.FCE_ERR_ARG), (1, B.FCE_ERR_WORKSPACE)):
+        assert lib.fce_forward_ex(FAKE, FAKE, FAKE, N, H, V, dtype, ctypes.byref(o), FAKE, FAKE,
+                                  FAKE, bf - 1, None) == want
+        assert lib.fce_backward_ex(FAKE, FAKE, FAKE, N, H, V, dtype, ctypes.byref(o), FAKE, None,
+                                   FAKE, FAKE, FAKE, bf - 1, None) == want
+        assert lib.fce_fused_fwd_bwd_ex(FAKE, FAKE, FAKE, N, H, V, dtype, ctypes.byref(o), FAKE,
+                                        FAKE, FAKE, FAKE, bf - 1, None) == want
+    assert lib.fce_ce_logits(FAKE, V, FAKE, N, V, 1, ctypes.byref(o), FAKE, FAKE, None, 0, None,
+                             FAKE, 1 << 20, None) == B.FCE_ERR_ARG
+    k, t = ctypes.c_int64(), ctypes.c_int64()
+    assert lib.fce_get_filter_stats(None, ctypes.byref(k), ctypes.byref(t), None) == B.FCE_ERR_NULL
 
 
 def test_ex_null_options_and_none_on_old_entry_points():
