@@ -6,6 +6,10 @@
         and ``--pmc WRITE_SIZE`` it calibrates those counters: every dispatch
         reads and writes exactly MIB MiB.
 
+    python -m linear_cross_entropy_ce_amd.profiling ce [--n 8192 --v 128256 --reps 5]
+        Runs the loss on given logits (dZ into another buffer) on seeded bf16
+        logits of that shape, for a kernel trace or counter pass of its own.
+
     python -m linear_cross_entropy_ce_amd.profiling traffic \\
             --fetch F.csv --write W.csv --copy-fetch CF.csv --copy-write CW.csv \\
             --copy-mib 1024 --workload NAME --out profiles [--command "..."]
@@ -28,6 +32,7 @@ import csv
 import hashlib
 import json
 import os
+import re
 import sys
 from collections import defaultdict
 
@@ -45,16 +50,28 @@ def source_digest() -> str:
     return h.hexdigest()[:16]
 
 
+def _flags(name: str) -> list[bool]:
+    """The bool template arguments of a kernel, in order (mangled Lb0E /
+    Lb1E, or demangled false / true after the tile configuration)."""
+    m = re.findall(r"Lb([01])E", name)
+    if m:
+        return [f == "1" for f in m]
+    tail = name.split(">,", 1)[-1]
+    return [w == "true" for w in re.findall(r"\b(true|false)\b", tail)]
+
+
 def kernel_key(name: str) -> str | None:
     """Map a (mangled or demangled) kernel name to the library's timer name."""
     if "k_bwd_grad" in name:
-        # template flag A_KMAJOR: false for dW (A = dZ^T), true for dX (A = dZ)
-        if "Lb0E" in name or "false>" in name:
-            return "bwd_dw"
-        if "Lb1E" in name or "true>" in name:
-            return "bwd_dx"
-        return None
-    for k in ("fwd_lse", "bwd_dz", "lse_merge", "loss_final", "label_scan", "fill_zero"):
+        # first flag A_KMAJOR: false for dW (A = dZ^T), true for dX (A = dZ)
+        f = _flags(name)
+        return None if not f else ("bwd_dx" if f[0] else "bwd_dw")
+    if "k_fwd_lse" in name:
+        # flags SMOOTH, STORE: the storing forward is the store-logits variant's
+        f = _flags(name)
+        return "sl_fwd" if len(f) > 1 and f[1] else "fwd_lse"
+    for k in ("bwd_dz", "lse_merge", "loss_final", "label_scan", "fill_zero", "ce_logits",
+              "dx_reduce", "filter_lists"):
         if f"k_{k}" in name:
             return k
     return None
@@ -98,6 +115,29 @@ def cmd_copy(args):
         torch.neg(src, out=dst)
     torch.cuda.synchronize()
     print(f"copy: {args.reps} x neg over {args.mib} MiB fp32 -> {args.mib} MiB", flush=True)
+
+
+def cmd_ce(args):
+    """The loss on given logits, dZ into another buffer, on seeded bf16
+    logits N(0, sigma^2) of the 8192 x 128256 logit shape."""
+    import torch
+
+    import linear_cross_entropy_ce_amd as fce
+
+    fce.load_library()
+    g = torch.Generator(device="cuda")
+    g.manual_seed(args.seed)
+    Z = (torch.randn((args.n, args.v), generator=g, device="cuda") * args.sigma).to(torch.bfloat16)
+    y = torch.randint(0, args.v, (args.n,), generator=g, device="cuda", dtype=torch.int32)
+    dZ = torch.empty_like(Z)
+    loss = torch.empty(1, device="cuda")
+    lse = torch.empty(args.n, device="cuda")
+    ws = torch.empty(fce.fce_ce_logits_workspace_size(args.n), dtype=torch.uint8, device="cuda")
+    for _ in range(args.reps):
+        fce.fce_ce_logits(Z, y, loss, lse, ws, dZ=dZ)
+    torch.cuda.synchronize()
+    print(f"ce_logits: {args.reps} calls on {args.n} x {args.v} bf16 logits, loss {loss.item():.5f}",
+          flush=True)
 
 
 def cmd_traffic(args):
@@ -170,6 +210,12 @@ def main(argv=None):
     c = sub.add_parser("copy")
     c.add_argument("--mib", type=int, default=1024)
     c.add_argument("--reps", type=int, default=3)
+    e = sub.add_parser("ce")
+    e.add_argument("--n", type=int, default=8192)
+    e.add_argument("--v", type=int, default=128256)
+    e.add_argument("--sigma", type=float, default=1.28)
+    e.add_argument("--seed", type=int, default=7)
+    e.add_argument("--reps", type=int, default=5)
     t = sub.add_parser("traffic")
     for a in ("--fetch", "--write", "--copy-fetch", "--copy-write", "--workload", "--out"):
         t.add_argument(a, required=True)
@@ -182,7 +228,7 @@ def main(argv=None):
     s.add_argument("--command", action="append")
     s.add_argument("--notes", action="append")
     args = ap.parse_args(argv)
-    {"copy": cmd_copy, "traffic": cmd_traffic, "stats": cmd_stats}[args.cmd](args)
+    {"copy": cmd_copy, "ce": cmd_ce, "traffic": cmd_traffic, "stats": cmd_stats}[args.cmd](args)
 
 
 if __name__ == "__main__":

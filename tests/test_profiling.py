@@ -7,11 +7,22 @@ from linear_cross_entropy_ce_amd import profiling as P
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
+_CFG = "INS_3CfgINS_9TileShapeILi256ELi256ELi64ELi2ELi4EEEDF16bEE"
+_DEM = "fce::Cfg<fce::TileShape<256, 256, 64, 2, 4>, __bf16>"
 MANGLED = {
-    "_ZN3fce12_GLOBAL__N_110k_bwd_gradINS_3CfgINS_9TileShapeILi256ELi256ELi64ELi4ELi2EEEDF16bEELb0EEEvNS0_8GradArgsINT_4ElemEEE": "bwd_dw",
-    "_ZN3fce12_GLOBAL__N_110k_bwd_gradINS_3CfgINS_9TileShapeILi256ELi256ELi64ELi4ELi2EEEDF16bEELb1EEEvNS0_8GradArgsINT_4ElemEEE": "bwd_dx",
-    "_ZN3fce12_GLOBAL__N_18k_bwd_dzINS_3CfgINS_9TileShapeILi256ELi256ELi64ELi4ELi2EEEDF16bEEEEvNS0_6DzArgsINT_4ElemEEE": "bwd_dz",
-    "_ZN3fce12_GLOBAL__N_19k_fwd_lseINS_3CfgINS_9TileShapeILi256ELi256ELi64ELi4ELi2EEEDF16bEELb0EEEvNS0_7FwdArgsINT_4ElemEEE": "fwd_lse",
+    # k_bwd_grad<C, A_KMAJOR, FILTER>: the first flag tells dW from dX
+    f"_ZN3fce12_GLOBAL__N_110k_bwd_grad{_CFG}Lb0ELb0EEEvNS0_8GradArgsINT_4ElemEEE": "bwd_dw",
+    f"_ZN3fce12_GLOBAL__N_110k_bwd_grad{_CFG}Lb0ELb1EEEvNS0_8GradArgsINT_4ElemEEE": "bwd_dw",
+    f"_ZN3fce12_GLOBAL__N_110k_bwd_grad{_CFG}Lb1ELb0EEEvNS0_8GradArgsINT_4ElemEEE": "bwd_dx",
+    f"_ZN3fce12_GLOBAL__N_110k_bwd_grad{_CFG}Lb1ELb1EEEvNS0_8GradArgsINT_4ElemEEE": "bwd_dx",
+    f"void fce::(anonymous namespace)::k_bwd_grad<{_DEM}, true, false>(GradArgs<__bf16>)": "bwd_dx",
+    f"void fce::(anonymous namespace)::k_bwd_grad<{_DEM}, false, true>(GradArgs<__bf16>)": "bwd_dw",
+    f"_ZN3fce12_GLOBAL__N_18k_bwd_dz{_CFG}Lb1ELb0EEEvNS0_6DzArgsINT_4ElemEEE": "bwd_dz",
+    # k_fwd_lse<C, SMOOTH, STORE>: the storing one belongs to store-logits
+    f"_ZN3fce12_GLOBAL__N_19k_fwd_lse{_CFG}Lb1ELb0EEEvNS0_7FwdArgsINT_4ElemEEE": "fwd_lse",
+    f"_ZN3fce12_GLOBAL__N_19k_fwd_lse{_CFG}Lb0ELb1EEEvNS0_7FwdArgsINT_4ElemEEE": "sl_fwd",
+    "_ZN3fce12_GLOBAL__N_111k_ce_logitsIDF16bLb0EEEvNS0_6CeArgsE": "ce_logits",
+    "fce::(anonymous namespace)::k_dx_reduce(float const*, int, long)": "dx_reduce",
     "fce::(anonymous namespace)::k_lse_merge(float __vector(4) const*, int, long)": "lse_merge",
     "__amd_rocclr_copyBuffer": None,
 }
