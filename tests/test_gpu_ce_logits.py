@@ -120,7 +120,7 @@ def test_reductions_zloss_smoothing(red):
     check(inp, got, grad=g, **opts)
 
 
-@pytest.mark.parametrize("V", [1, 7, 8, 9, 1000, 8193, 70001])
+@pytest.mark.parametrize("V", [1, 7, 8, 9, 1000, 8193, 70001, 140001])
 def test_ragged_rows_and_padding(V):
     wl = wk.custom(33, 16, V, "bf16", 0.5, "uniform", 1.1, 0.1, 0.0, seed=85 + V)
     inp = wk.draw_logits(wl)
@@ -131,6 +131,14 @@ def test_ragged_rows_and_padding(V):
     tail = (-V) % 8
     assert np.all(got["pad"][:, :tail] == 0.0)
     assert np.all(np.isnan(got["pad"][:, tail:]))
+
+
+@pytest.mark.parametrize("V", [5003, 40000])
+def test_fp32_rows(V):
+    wl = wk.custom(70, 64, V, "fp32", 0.05, "uniform", 1.1, 0.1, 0.0, seed=97)
+    inp = wk.draw_logits(wl)
+    got = run(inp, label_smoothing=0.1, z_loss=1e-3)
+    check(inp, got, label_smoothing=0.1, z_loss=1e-3)
 
 
 def test_invalid_and_ignored_rows():
