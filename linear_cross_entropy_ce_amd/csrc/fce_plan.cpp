@@ -28,8 +28,11 @@ size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 int64_t round_up(int64_t a, int64_t b) { return cdiv(a, b) * b; }
 
-// Modelled time of one backward schedule, in seconds.  Only the ranking of
-// candidates matters.
+// Modelled time of one backward schedule, in seconds: MFMA work of the
+// three products with each grid rounded up to whole waves over the CUs, plus
+// the fp32 read-modify-write bytes of dW and dX.  Only the ranking of
+// candidates matters.  Blocks are full except the last in each dimension,
+// so four block shapes cover the whole schedule.
 double model_time(const Plan& p, int64_t CN, int64_t CV, int64_t a, int64_t b) {
   const double peak = (p.dtype == Dtype::BF16) ? 2.5e15 : 1.5e14;
   const double bw = 5.0e12;
@@ -37,18 +40,16 @@ double model_time(const Plan& p, int64_t CN, int64_t CV, int64_t a, int64_t b) {
   const double per_cu = peak / kNumCUs;
   auto waves = [](int64_t tiles) { return static_cast<double>(cdiv(tiles, kNumCUs)); };
   const int64_t h_tiles = cdiv(p.H, p.tile);
-  double time = 0.0;
-  for (int64_t ia = 0; ia < a; ++ia) {
-    const int64_t cn = std::min(CN, p.N - ia * CN);
-    const int64_t tn = cdiv(cn, p.tile);
-    for (int64_t ib = 0; ib < b; ++ib) {
-      const int64_t cv = std::min(CV, p.V - ib * CV);
-      const int64_t tv = cdiv(cv, p.tile);
-      time += waves(tn * tv) * 2.0 * t * t * static_cast<double>(p.H) / per_cu;      // recompute
-      time += waves(tv * h_tiles) * 2.0 * t * t * static_cast<double>(tn * p.tile) / per_cu;  // dW
-      time += waves(tn * h_tiles) * 2.0 * t * t * static_cast<double>(tv * p.tile) / per_cu;  // dX
-    }
-  }
+  auto block = [&](int64_t cn, int64_t cv) {
+    const int64_t tn = cdiv(cn, p.tile), tv = cdiv(cv, p.tile);
+    return waves(tn * tv) * 2.0 * t * t * static_cast<double>(p.H) / per_cu +       // recompute
+           waves(tv * h_tiles) * 2.0 * t * t * static_cast<double>(tn * p.tile) / per_cu +  // dW
+           waves(tn * h_tiles) * 2.0 * t * t * static_cast<double>(tv * p.tile) / per_cu;   // dX
+  };
+  const int64_t cn_last = p.N - (a - 1) * CN, cv_last = p.V - (b - 1) * CV;
+  const double time = static_cast<double>((a - 1) * (b - 1)) * block(CN, CV) +
+                      static_cast<double>(a - 1) * block(CN, cv_last) +
+                      static_cast<double>(b - 1) * block(cn_last, CV) + block(cn_last, cv_last);
   const double rmw = 4.0 * static_cast<double>(p.V * p.H) * static_cast<double>(2 * a - 1) +
                      4.0 * static_cast<double>(p.N * p.H) * static_cast<double>(2 * b - 1);
   return time + rmw / bw;
@@ -145,31 +146,37 @@ bool make_plan(int64_t N, int64_t H, int64_t V, Dtype dtype, int64_t chunk, Sche
       p.a = 1;
       vocab_split(p.CN, &p.CV, &p.b);
     } else if (sched == Schedule::Auto) {
-      // Candidates: every block height, and for each the fewest vocabulary
-      // blocks the budget allows plus a few more (a narrower block can fill
-      // the 256 CUs with fewer partial waves).
+      // Candidates: every block height, and for each the balanced widths of
+      // the fewest vocabulary blocks the budget allows plus a few more, and
+      // every tile multiple from half the widest width up to it (a width
+      // whose grids are whole waves over the 256 CUs may leave a small last
+      // block and still win).
       double best = std::numeric_limits<double>::infinity();
+      auto consider = [&](int64_t CN, int64_t CV) {
+        const int64_t aa = cdiv(N, CN), bb = cdiv(V, CV);
+        const double t = model_time(p, CN, CV, aa, bb);
+        if (t < best * (1.0 - 1e-9)) {
+          best = t;
+          p.CN = CN;
+          p.CV = CV;
+          p.a = aa;
+          p.b = bb;
+        }
+      };
       const int64_t amax = cdiv(N, G);
       for (int64_t a = 1; a <= amax; ++a) {
         const int64_t CN = round_up(cdiv(N, a), G);
-        const int64_t aa = cdiv(N, CN);
-        if (aa != a) continue;  // same block height as a smaller a
+        if (cdiv(N, CN) != a) continue;  // same block height as a smaller a
         int64_t CV0, b0;
         vocab_split(CN, &CV0, &b0);
         for (int64_t b = b0; b <= b0 + 8; ++b) {
           const int64_t CV = round_up(cdiv(V, b), G);
           if (CV > CV0 && b != b0) continue;
-          const int64_t bb = cdiv(V, CV);
-          if (bb != b) continue;  // same block width as a smaller b
-          const double t = model_time(p, CN, CV, aa, bb);
-          if (t < best * (1.0 - 1e-9)) {
-            best = t;
-            p.CN = CN;
-            p.CV = CV;
-            p.a = aa;
-            p.b = bb;
-          }
+          if (cdiv(V, CV) != b) continue;  // same block width as a smaller b
+          consider(CN, CV);
         }
+        for (int64_t k = std::max<int64_t>(1, CV0 / G / 2); k * G <= CV0; ++k)
+          consider(CN, k * G);
       }
     } else {
       return false;
