@@ -176,6 +176,46 @@ def cmd_traffic(args):
     print("\n".join(lines))
 
 
+def cmd_counters(args):
+    """Per-kernel averages per dispatch of every counter in a
+    counter_collection.csv, as markdown, with derived ratios where the
+    counters for them are present."""
+    names = []
+    for r in _rows(args.csv):
+        if r["Counter_Name"] not in names:
+            names.append(r["Counter_Name"])
+    per = {n: per_dispatch(args.csv, n) for n in names}
+    kernels = sorted({k for d in per.values() for k in d})
+    out = [f"# {args.title}", "", "Commands (on the MI355X box, from the repository root, with "
+           "`cd /tmp && export TMPDIR=/tmp` first):", ""]
+    out += [f"    {c}" for c in (args.command or [])]
+    out += ["", "Average per dispatch (counters summed over shader engines).", "",
+            "| kernel | dispatches | " + " | ".join(names) + " |",
+            "|:--|--:|" + "--:|" * len(names)]
+    derived = []
+    for k in kernels:
+        avg = {n: (sum(per[n][k]) / len(per[n][k]) if per[n].get(k) else float("nan"))
+               for n in names}
+        ndisp = max(len(per[n].get(k, [])) for n in names)
+        out.append(f"| {k} | {ndisp} | " + " | ".join(f"{avg[n]:,.0f}" for n in names) + " |")
+        if "SQ_VALU_MFMA_BUSY_CYCLES" in avg and "SQ_BUSY_CYCLES" in avg:
+            # SQ_BUSY_CYCLES is summed over the 32 shader engines, the MFMA
+            # busy cycles over the 1024 SIMDs (32 per engine): their ratio over
+            # 32 is the fraction of busy cycles each SIMD's matrix pipe worked
+            derived.append(f"| {k} | {avg['SQ_VALU_MFMA_BUSY_CYCLES'] / max(32.0 * avg['SQ_BUSY_CYCLES'], 1):.3f} | "
+                           + (f"{avg['SQ_LDS_BANK_CONFLICT'] / max(avg.get('SQ_INSTS_LDS', 1), 1):.4f}"
+                              if "SQ_LDS_BANK_CONFLICT" in avg else "")
+                           + " |")
+    if derived:
+        out += ["", "| kernel | MFMA busy fraction per SIMD | LDS bank-conflict cycles per LDS instruction |",
+                "|:--|--:|--:|"] + derived
+    if args.notes:
+        out += [""] + args.notes
+    with open(args.out, "w") as fh:
+        fh.write("\n".join(out) + "\n")
+    print("\n".join(out))
+
+
 def cmd_stats(args):
     rows = list(_rows(args.csv))
     out = [f"# {args.title}", "", "Command (on the MI355X box, from the repository root, with "
@@ -221,6 +261,12 @@ def main(argv=None):
         t.add_argument(a, required=True)
     t.add_argument("--copy-mib", type=int, default=1024)
     t.add_argument("--command", action="append")
+    n = sub.add_parser("counters")
+    n.add_argument("--csv", required=True)
+    n.add_argument("--title", required=True)
+    n.add_argument("--out", required=True)
+    n.add_argument("--command", action="append")
+    n.add_argument("--notes", action="append")
     s = sub.add_parser("stats")
     s.add_argument("--csv", required=True)
     s.add_argument("--title", required=True)
@@ -228,7 +274,8 @@ def main(argv=None):
     s.add_argument("--command", action="append")
     s.add_argument("--notes", action="append")
     args = ap.parse_args(argv)
-    {"copy": cmd_copy, "ce": cmd_ce, "traffic": cmd_traffic, "stats": cmd_stats}[args.cmd](args)
+    {"copy": cmd_copy, "ce": cmd_ce, "traffic": cmd_traffic, "counters": cmd_counters,
+     "stats": cmd_stats}[args.cmd](args)
 
 
 if __name__ == "__main__":
