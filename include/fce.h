@@ -235,7 +235,8 @@ fce_status fce_fused_fwd_bwd_ex(const void* X, const void* W, const int32_t* lab
  * softmax+CE row, where probs and dlogits reuse the logits buffer).
  *
  * Z is DEVICE, row-major [N][ldz] with ldz >= V (elements), dtype FCE_BF16
- * or FCE_F32, 16-byte aligned with ldz * element size a multiple of 16.
+ * or FCE_F32, 16-byte aligned with ldz * element size a multiple of 16.  A
+ * row of V elements must be under 2 GiB (FCE_ERR_SHAPE otherwise).
  * Writes lse[N] and the loss (float[1], or float[N] for FCE_NONE) as in
  * fce_forward_ex.  If dZ is not NULL it also writes
  *   dZ_ij = (softmax_ij (1 + 2 alpha LSE_i) - (1-eps)[j = y_i] - eps/V) * s_i

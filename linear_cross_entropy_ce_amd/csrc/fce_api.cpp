@@ -358,6 +358,8 @@ fce_status fce_ce_logits(const void* Z, int64_t ldz, const int32_t* labels, int6
   const bool none = lo.reduction == fce::Reduction::None;
   if (loss == nullptr && !(none && N == 0)) return FCE_ERR_NULL;
   const int64_t es = (dtype == FCE_BF16) ? 2 : 4;
+  // the kernel addresses a row with 32-bit byte offsets
+  if (V * es >= (int64_t{1} << 31)) return FCE_ERR_SHAPE;
   if (ldz < V || (dZ != nullptr && lddz < V)) return FCE_ERR_SHAPE;
   if (dZ == Z && lddz != ldz) return FCE_ERR_ARG;
   if ((ldz * es) % 16 != 0 || (dZ != nullptr && (lddz * es) % 16 != 0)) return FCE_ERR_ALIGN;

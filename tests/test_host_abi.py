@@ -189,6 +189,17 @@ def test_ex_rejects_bad_options(kw, status):
     assert lib.fce_workspace_size_ex(64, 64, 100, 1, ctypes.byref(o)) == 0
 
 
+def test_ce_logits_rejects_rows_of_2_gib():
+    lib = B.load_library()
+    o = _opts()
+    V = 1 << 29  # fp32: 2 GiB per row; bf16 the same V is 1 GiB and passes this check
+    # (a one-byte workspace stops the bf16 call at the next check, before any launch)
+    args = lambda dtype: (FAKE, V, FAKE, 4, V, dtype, ctypes.byref(o), FAKE, FAKE, None, 0, None,
+                          FAKE, 1, None)
+    assert lib.fce_ce_logits(*args(0)) == B.FCE_ERR_SHAPE
+    assert lib.fce_ce_logits(*args(1)) == B.FCE_ERR_WORKSPACE
+
+
 def test_store_logits_variant_where_accepted_and_its_workspace():
     lib = B.load_library()
     N, H, V = 1000, 64, 5000
