@@ -75,7 +75,9 @@ extern "C" {
 typedef enum {
   FCE_OK = 0,
   FCE_ERR_NULL = -1,      /* a required pointer is NULL */
-  FCE_ERR_SHAPE = -2,     /* N < 0, H < 1, V < 1, or sizes overflow */
+  FCE_ERR_SHAPE = -2,     /* N < 0, H < 1, V < 1, N >= 2^30, or H or V near or above
+                             2^22 (bf16) / 2^21 (fp32): 256 rows of H or V elements
+                             must stay under 2 GiB */
   FCE_ERR_ARG = -3,       /* bad enum or option, chunk < 1, label_smoothing outside [0,1) */
   FCE_ERR_WORKSPACE = -4, /* workspace smaller than fce_workspace_size() */
   FCE_ERR_ALIGN = -5,     /* pointer not 16-byte aligned or H not a multiple of 8 / 4 */

@@ -70,6 +70,11 @@ bool make_plan(int64_t N, int64_t H, int64_t V, Dtype dtype, int64_t chunk, Sche
   // coordinates are 32-bit: keep every extent comfortably inside int32.
   const int64_t lim = static_cast<int64_t>(1) << 30;
   if (N >= lim || H >= lim || V >= lim) return false;
+  // The GEMM engine addresses a 256-row operand tile with 32-bit byte
+  // offsets: rows of H elements (X, W) and of the padded vocabulary width
+  // (the logit block) must keep 256 rows under 2 GiB.
+  const int64_t row_cap = (static_cast<int64_t>(1) << 31) / (256 * ((dtype == Dtype::BF16) ? 2 : 4));
+  if (H >= row_cap || V + 512 >= row_cap) return false;
   Plan p;
   p.N = N;
   p.H = H;

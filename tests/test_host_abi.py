@@ -133,6 +133,11 @@ def test_plan_invariants(N, H, V, dtype, chunk, sched):
 def test_plan_rejects_bad_arguments():
     lib = B.load_library()
     info = B.PlanInfo()
+    # 256 rows of H or V elements must stay under 2 GiB (32-bit tile offsets)
+    assert lib.fce_plan(1024, 1 << 22, 1000, 1, 1024, 0, ctypes.byref(info)) == B.FCE_ERR_SHAPE
+    assert lib.fce_plan(1024, 1024, 1 << 22, 1, 1024, 0, ctypes.byref(info)) == B.FCE_ERR_SHAPE
+    assert lib.fce_plan(1024, 1 << 21, 1000, 0, 1024, 0, ctypes.byref(info)) == B.FCE_ERR_SHAPE
+    assert lib.fce_plan(1024, 1 << 20, 1 << 21, 1, 1024, 0, ctypes.byref(info)) == B.FCE_OK
     assert lib.fce_plan(10, 8, 10, 1, 0, 0, ctypes.byref(info)) == B.FCE_ERR_ARG
     assert lib.fce_plan(-1, 8, 10, 1, 4, 0, ctypes.byref(info)) == B.FCE_ERR_SHAPE
     assert lib.fce_plan(10, 8, 10, 1, 4, 0, None) == B.FCE_ERR_NULL
