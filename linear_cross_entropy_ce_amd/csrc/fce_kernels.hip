@@ -454,10 +454,12 @@ struct GradArgs {
   int ksplit;
   int64_t split_stride;
   // FILTER: the kept K blocks (kMapBlock long) of output row tile tm are
-  // klist[tm * list_ld + 0 .. kcount[tm]-1], ascending
+  // klist[tm * list_ld + 0 .. kcount[tm]-1], ascending; korder lists the row
+  // tiles by descending kept count (longest first)
   const int* klist;
   const int* kcount;
   int list_ld;
+  const int* korder;
 };
 
 // The part of an operand from contraction index k0 on.
@@ -474,8 +476,14 @@ __global__ __launch_bounds__(C::NT) void k_bwd_grad(GradArgs<typename C::Elem> a
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave / C::WAVES_N, wn = wave % C::WAVES_N;
   int tm, tn;
-  grouped_tile(xcd_remap(blockIdx.x, a.tm_tiles * a.tn_tiles), a.tm_tiles, a.tn_tiles, a.group_m,
-               tm, tn);
+  if (FILTER && a.kcount[a.korder[0]] != a.kcount[a.korder[a.tm_tiles - 1]]) {
+    // rows of unequal length: the longest first, in dispatch order
+    tm = a.korder[blockIdx.x / a.tn_tiles];
+    tn = blockIdx.x % a.tn_tiles;
+  } else {
+    grouped_tile(xcd_remap(blockIdx.x, a.tm_tiles * a.tn_tiles), a.tm_tiles, a.tn_tiles,
+                 a.group_m, tm, tn);
+  }
   const int m0 = tm * C::BM, n0 = tn * C::BN;
   const bool skip = (*a.flag == 0);  // all labels of the token block ignored: dZ = 0
   if (skip && a.accumulate) return;
@@ -554,29 +562,53 @@ __global__ __launch_bounds__(C::NT) void k_bwd_grad(GradArgs<typename C::Elem> a
 
 // Kept-block lists of one logit block for the filtered products: per token
 // tile (rows of dX) the kept vocabulary tiles, per vocabulary tile (rows of
-// dW) the kept token tiles, ascending.  stats[0] += kept tiles, stats[1] +=
-// all tiles of the block.
-__global__ __launch_bounds__(256) void k_filter_lists(const uint8_t* __restrict__ keep, int tt,
-                                                      int vt, int* __restrict__ rowlist,
-                                                      int* __restrict__ rowcnt,
-                                                      int* __restrict__ collist,
-                                                      int* __restrict__ colcnt,
-                                                      unsigned long long* __restrict__ stats) {
-  const int i = blockIdx.x * blockDim.x + threadIdx.x;
-  if (i < tt) {
-    int c = 0;
-    for (int v = 0; v < vt; ++v)
-      if (keep[i * vt + v]) rowlist[i * vt + c++] = v;
-    rowcnt[i] = c;
-    atomicAdd(&stats[0], static_cast<unsigned long long>(c));
-  } else if (i < tt + vt) {
-    const int j = i - tt;
-    int c = 0;
-    for (int t = 0; t < tt; ++t)
-      if (keep[t * vt + j]) collist[j * tt + c++] = t;
-    colcnt[j] = c;
+// dW) the kept token tiles, ascending.  One wave per list: 64 flags at a
+// time, compacted with a ballot and a population count.  stats[0] += kept
+// tiles, stats[1] += all tiles of the block.
+__global__ __launch_bounds__(64) void k_filter_lists(const uint8_t* __restrict__ keep, int tt,
+                                                     int vt, int* __restrict__ rowlist,
+                                                     int* __restrict__ rowcnt,
+                                                     int* __restrict__ collist,
+                                                     int* __restrict__ colcnt,
+                                                     unsigned long long* __restrict__ stats) {
+  const int i = blockIdx.x, lane = threadIdx.x;
+  const bool is_row = i < tt;
+  const int len = is_row ? vt : tt;  // entries of this list
+  int* out = is_row ? rowlist + i * vt : collist + (i - tt) * tt;
+  int c = 0;
+  for (int base = 0; base < len; base += 64) {
+    const int e = base + lane;
+    const bool k = e < len && keep[is_row ? i * vt + e : e * vt + (i - tt)] != 0;
+    const unsigned long long m = __ballot(k);
+    if (k) out[c + __popcll(m & ((1ull << lane) - 1ull))] = e;
+    c += __popcll(m);
   }
-  if (i == 0) atomicAdd(&stats[1], static_cast<unsigned long long>(tt) * vt);
+  if (lane == 0) {
+    (is_row ? rowcnt[i] : colcnt[i - tt]) = c;
+    if (is_row) atomicAdd(&stats[0], static_cast<unsigned long long>(c));
+    if (i == 0) atomicAdd(&stats[1], static_cast<unsigned long long>(tt) * vt);
+  }
+}
+
+// Row tiles of the two filtered products by descending kept count (ties by
+// index): rank of row i = rows with a larger count, or an equal count and a
+// smaller index.  One workgroup; counts of at most a few hundred rows.
+__global__ __launch_bounds__(256) void k_filter_order(const int* __restrict__ rowcnt, int tt,
+                                                      int* __restrict__ roworder,
+                                                      const int* __restrict__ colcnt, int vt,
+                                                      int* __restrict__ colorder) {
+  for (int i = threadIdx.x; i < tt + vt; i += blockDim.x) {
+    const bool row = i < tt;
+    const int* cnt = row ? rowcnt : colcnt;
+    const int n = row ? tt : vt, k = row ? i : i - tt;
+    const int ck = cnt[k];
+    int rank = 0;
+    for (int j = 0; j < n; ++j) {
+      const int cj = cnt[j];
+      rank += (cj > ck || (cj == ck && j < k)) ? 1 : 0;
+    }
+    (row ? roworder : colorder)[rank] = k;
+  }
 }
 
 // dX rows of one block from the split partials: out (=|+=) sum over z of
@@ -860,8 +892,10 @@ hipError_t run_forward(const Plan& p, const T* X, const T* W, const int32_t* lab
 struct FilterLists {
   const int* rowlist;  // [tt][vt]: per token tile, kept vocabulary tiles
   const int* rowcnt;
+  const int* roworder;  // token tiles by descending kept count
   const int* collist;  // [vt][tt]: per vocabulary tile, kept token tiles
   const int* colcnt;
+  const int* colorder;  // vocabulary tiles by descending kept count
   int tt, vt;
 };
 
@@ -904,6 +938,7 @@ hipError_t grad_products(const Plan& p, const T* X, const T* W, const T* dz, int
   gw.klist = fl ? fl->collist : nullptr;
   gw.kcount = fl ? fl->colcnt : nullptr;
   gw.list_ld = fl ? fl->tt : 0;
+  gw.korder = fl ? fl->colorder : nullptr;
   timer->begin(name_dw, blk_flops, st);
   if constexpr (sizeof(T) == 2) {
     if (fl)
@@ -936,6 +971,7 @@ hipError_t grad_products(const Plan& p, const T* X, const T* W, const T* dz, int
   gx.klist = fl ? fl->rowlist : nullptr;
   gx.kcount = fl ? fl->rowcnt : nullptr;
   gx.list_ld = fl ? fl->vt : 0;
+  gx.korder = fl ? fl->roworder : nullptr;
   // split over the vocabulary when the plan asks for it: whole tiles per split
   const int ksplit = cdiv_i(cdiv_i(nvoc_cov, static_cast<int>(p.dx_splits)), C::BM) * C::BM;
   const int splits = fl ? 1 : cdiv_i(nvoc_cov, ksplit);
@@ -1032,14 +1068,22 @@ hipError_t run_backward(const Plan& p, const T* X, const T* W, const int32_t* la
 
       FilterLists fl{reinterpret_cast<const int*>(ws + p.off_rowlist),
                      reinterpret_cast<const int*>(ws + p.off_rowcnt),
+                     reinterpret_cast<const int*>(ws + p.off_roworder),
                      reinterpret_cast<const int*>(ws + p.off_collist),
-                     reinterpret_cast<const int*>(ws + p.off_colcnt), tok_tiles, voc_tiles};
+                     reinterpret_cast<const int*>(ws + p.off_colcnt),
+                     reinterpret_cast<const int*>(ws + p.off_colorder), tok_tiles, voc_tiles};
       if (filt) {
         timer->begin("filter_lists", 0.0, st);
-        k_filter_lists<<<cdiv_i(tok_tiles + voc_tiles, 256), 256, 0, st>>>(
+        k_filter_lists<<<tok_tiles + voc_tiles, 64, 0, st>>>(
             keep, tok_tiles, voc_tiles, reinterpret_cast<int*>(ws + p.off_rowlist),
             reinterpret_cast<int*>(ws + p.off_rowcnt), reinterpret_cast<int*>(ws + p.off_collist),
             reinterpret_cast<int*>(ws + p.off_colcnt), fstats);
+        FCE_CHECK_LAUNCH();
+        k_filter_order<<<1, 256, 0, st>>>(
+            reinterpret_cast<const int*>(ws + p.off_rowcnt), tok_tiles,
+            reinterpret_cast<int*>(ws + p.off_roworder),
+            reinterpret_cast<const int*>(ws + p.off_colcnt), voc_tiles,
+            reinterpret_cast<int*>(ws + p.off_colorder));
         FCE_CHECK_LAUNCH();
         timer->end(st);
       }

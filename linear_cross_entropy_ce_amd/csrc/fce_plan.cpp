@@ -246,6 +246,10 @@ bool make_plan(int64_t N, int64_t H, int64_t V, Dtype dtype, int64_t chunk, Sche
     off = align_up(off + 4 * static_cast<size_t>(p.filt_tt));
     p.off_colcnt = off;
     off = align_up(off + 4 * static_cast<size_t>(p.filt_vt));
+    p.off_roworder = off;
+    off = align_up(off + 4 * static_cast<size_t>(p.filt_tt));
+    p.off_colorder = off;
+    off = align_up(off + 4 * static_cast<size_t>(p.filt_vt));
   }
   p.total = off;
   *out = p;

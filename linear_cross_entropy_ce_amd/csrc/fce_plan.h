@@ -44,7 +44,8 @@ struct Plan {
          off_scratch = 0, off_dxpart = 0, total = 0;
   // Filtered: per logit block, kept flags [tt][vt] and the kept-block lists
   int64_t filt_tt = 0, filt_vt = 0;
-  size_t off_keep = 0, off_rowlist = 0, off_rowcnt = 0, off_collist = 0, off_colcnt = 0;
+  size_t off_keep = 0, off_rowlist = 0, off_rowcnt = 0, off_collist = 0, off_colcnt = 0,
+         off_roworder = 0, off_colorder = 0;
   size_t scratch_bytes = 0, partial_bytes = 0, dxpart_bytes = 0;
   int64_t n_loss_blocks = 0;
   int64_t grad_rmw_bytes = 0;
