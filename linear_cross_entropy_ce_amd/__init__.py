@@ -93,18 +93,31 @@ def _make_function():
             ws = torch.empty(n, dtype=torch.uint8, device=X.device)
             none = opts["reduction"] == "none"
             loss = torch.empty(N if none else 1, dtype=torch.float32, device=X.device)
+            ctx.cfg = (opts, hidden.shape, hidden.dtype, weight.dtype)
+            if opts["variant"] == "store_logits":
+                # gradients with an upstream gradient of 1, computed now; the
+                # backward scales them by the scalar it receives
+                dX = torch.empty((N, H), dtype=torch.float32, device=X.device)
+                dW = torch.empty(W.shape, dtype=torch.float32, device=X.device)
+                fce_fused_fwd_bwd_ex(X if N else None, W, y if N else None, loss,
+                                     dX if N else None, dW, ws, **opts)
+                ctx.save_for_backward(dX, dW)
+                return loss[0]
             lse = torch.empty(max(N, 1), dtype=torch.float32, device=X.device)
             fce_forward_ex(X if N else None, W, y if N else None, loss if loss.numel() else None,
                            lse, ws, **opts)
             ctx.save_for_backward(X, W, y, lse)
-            ctx.cfg = (opts, hidden.shape, hidden.dtype, weight.dtype)
             ctx.ws = ws
             return loss.reshape(labels.shape) if none else loss[0]
 
         @staticmethod
         def backward(ctx, g):
-            X, W, y, lse = ctx.saved_tensors
             opts, hshape, hdt, wdt = ctx.cfg
+            if opts["variant"] == "store_logits":
+                dX, dW = ctx.saved_tensors
+                gs = g.to(torch.float32)
+                return (dX * gs).to(hdt).reshape(hshape), (dW * gs).to(wdt), None, None
+            X, W, y, lse = ctx.saved_tensors
             N, H = X.shape
             g1 = g.reshape(-1).to(torch.float32).contiguous()
             dX = torch.empty((N, H), dtype=torch.float32, device=X.device)
@@ -121,19 +134,30 @@ _FN = None
 
 def linear_cross_entropy(hidden, weight, labels, ignore_index: int = -100,
                          label_smoothing: float = 0.0, reduction: str = "mean", chunk: int = 1024,
-                         schedule: str = "auto", z_loss: float = 0.0):
+                         schedule: str = "auto", z_loss: float = 0.0,
+                         variant: str = "recompute"):
     """Cross-entropy of ``hidden @ weight.T`` against ``labels``: a scalar for
     reduction "mean" or "sum", per-token losses (labels' shape) for "none".
 
     hidden [..., H] and weight [V, H] share a dtype (bfloat16 or float32);
     labels [...] are class indices, ``ignore_index`` rows carry no loss.
     ``z_loss`` = alpha adds alpha * logsumexp(z)^2 per token.  Gradients for
-    hidden and weight come from the fused backward."""
+    hidden and weight come from the fused backward.
+
+    variant: "recompute" (the backward rebuilds the logits), "filtered"
+    (bfloat16: the gradient filtering approximation, dZ tiles whose softmax
+    values are all below 2^-12 skipped) or "store_logits" (mean or sum only:
+    the forward computes the gradients too, keeping each chunk's logits, and
+    holds dX and dW in fp32 until the backward scales them)."""
     global _FN
     if _FN is None:
         _FN = _make_function()
     if reduction not in REDUCTIONS:
         raise ValueError(f"unknown reduction {reduction!r}")
+    if variant not in VARIANTS:
+        raise ValueError(f"unknown variant {variant!r}")
+    if variant == "store_logits" and reduction == "none":
+        raise ValueError("variant 'store_logits' needs a scalar loss (reduction mean or sum)")
     opts = dict(ignore_index=ignore_index, label_smoothing=label_smoothing, z_loss=z_loss,
-                reduction=reduction, chunk=chunk, schedule=schedule)
+                reduction=reduction, chunk=chunk, schedule=schedule, variant=variant)
     return _FN.apply(hidden, weight, labels, opts)

@@ -199,6 +199,26 @@ def test_autograd_wrapper():
     assert rel_l2(Wr.grad.cpu().numpy(), ref.dW) <= 1e-5
 
 
+@pytest.mark.parametrize("dtype,variant", [("fp32", "store_logits"), ("bf16", "store_logits"),
+                                           ("bf16", "filtered")])
+def test_autograd_wrapper_variants(dtype, variant):
+    # the gradients of the store-logits variant are computed in the forward
+    # and scaled by the upstream gradient (0.5 here) in the backward
+    wl = wk.custom(3 * 130, 64, 900, dtype, 0.1, ignore_frac=0.1, label_smoothing=0.1, seed=69)
+    inp = wk.draw(wl)
+    X, W, y = wk.to_torch(inp, "cuda")
+    Xr = X.reshape(3, 130, 64).clone().requires_grad_(True)
+    Wr = W.clone().requires_grad_(True)
+    loss = fce.linear_cross_entropy(Xr, Wr, y.reshape(3, 130).long(), label_smoothing=0.1,
+                                    chunk=100, z_loss=1e-3, variant=variant)
+    (loss * 0.5).backward()
+    ref = orc.linear_cross_entropy(inp.X, inp.W, inp.labels, -100, 0.1, "mean", 0.5, z_loss=1e-3)
+    tl, tg = TOL[dtype]
+    assert abs(loss.item() - ref.loss) <= tl * ref.loss
+    assert rel_l2(Xr.grad.reshape(-1, 64).float().cpu().numpy(), ref.dX) <= tg
+    assert rel_l2(Wr.grad.float().cpu().numpy(), ref.dW) <= tg
+
+
 # ------------------------------------------- z-loss and reduction "none"
 def run_ex(inp, grad=None, split=True, **opts):
     """The *_ex entry points; grad: per-token array for "none", scalar else."""

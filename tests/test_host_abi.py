@@ -293,3 +293,15 @@ def test_ce_logits_rejects_bad_arguments():
     assert f(o=_opts(z_loss=-1.0)) == B.FCE_ERR_ARG
     assert f(dtype=3) == B.FCE_ERR_ARG
     assert lib.fce_ce_logits_workspace_size(-1) == 0
+
+
+def test_autograd_wrapper_rejects_bad_variants_before_any_call():
+    import torch
+
+    X = torch.zeros((4, 8))
+    W = torch.zeros((10, 8))
+    y = torch.zeros(4, dtype=torch.long)
+    with pytest.raises(ValueError):
+        fce.linear_cross_entropy(X, W, y, variant="store_logits", reduction="none")
+    with pytest.raises(ValueError):
+        fce.linear_cross_entropy(X, W, y, variant="bogus")
