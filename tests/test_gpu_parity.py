@@ -459,7 +459,7 @@ def test_store_logits_degenerate_shapes(N, H, V):
 
 # The headline shape in one chunk (the whole 8192 x 128256 logits kept) and
 # in chunks of 1024, and the 4096 x 2048 x 32000 workload.
-@pytest.mark.parametrize("k,chunk", [(2, 1024), (3, 1024), (3, 8192)])
+@pytest.mark.parametrize("k,chunk", [(2, 1024), (3, 1024), (3, 8192), (4, 2048), (5, 1024)])
 def test_store_logits_full_size(k, chunk):
     wl = wk.WORKLOADS[k]
     g = _golden(k)
@@ -470,6 +470,29 @@ def test_store_logits_full_size(k, chunk):
     got["loss"] = float(got["loss"][0])
     # the LSE stays in the workspace; take it from the forward entry point
     got["lse"] = run_ex_lse(inp)
+    check_golden(inp, g, got)
+
+
+@pytest.mark.parametrize("k", [4, 5])
+def test_filtered_full_size(k):
+    # the filtered variant at the two largest workloads (label smoothing at
+    # 16384 x 3584 x 152064): against the stored oracle values
+    wl = wk.WORKLOADS[k]
+    g = _golden(k)
+    inp = _draw_cached(k)
+    assert str(g["digest"]) == inp.digest(), "input generator drifted from the stored goldens"
+    X, W, y = wk.to_torch(inp, "cuda")
+    ws = fce.workspace_for(wl.N, wl.H, wl.V, X.dtype, variant="filtered",
+                           label_smoothing=wl.label_smoothing)
+    loss = torch.empty(1, device="cuda")
+    dX = torch.empty((wl.N, wl.H), device="cuda")
+    dW = torch.empty((wl.V, wl.H), device="cuda")
+    fce.fce_fused_fwd_bwd_ex(X, W, y, loss, dX, dW, ws, variant="filtered",
+                             label_smoothing=wl.label_smoothing)
+    torch.cuda.synchronize()
+    kept, total = fce.fce_get_filter_stats(ws)
+    print(f"[{wl.name} filtered] kept {kept}/{total}", flush=True)
+    got = dict(loss=loss.item(), lse=run_ex_lse(inp), dX=dX.cpu().numpy(), dW=dW.cpu().numpy())
     check_golden(inp, g, got)
 
 
