@@ -806,6 +806,77 @@ __device__ __forceinline__ void gemm_tile_dma(Acc<C>& acc, const Opnd<bf16>& A,
   barrier_after_vmcnt<0>();
 }
 
+// Ping-pong K loop: the two wave groups (wm = 0 and wm = 1, one wave of each
+// per SIMD) alternate between an MFMA phase (a whole K tile from registers)
+// and a memory phase (the next tile's fragments into the single register
+// set, the DMA share of a tile three ahead), half a tile apart, with a
+// barrier per half step: while one group synchronises, the other feeds the
+// matrix pipe.  Group A reads tile 0 before the loop; then at half step 2t
+// A computes tile t while B loads tile t, at 2t+1 A loads tile t+1 while B
+// computes tile t.
+template <class C, bool A_KMAJOR, bool B_KMAJOR, bool KFULL>
+__device__ __forceinline__ void gemm_tile_pp(Acc<C>& acc, const Opnd<bf16>& A,
+                                             const Opnd<bf16>& B, int m0, int n0, int K,
+                                             const DmaStages& st, int tid) {
+  typedef DmaEngine<C, A_KMAJOR, B_KMAJOR, KFULL> E;
+  constexpr int BK = E::BK, NL = E::NL;
+  static_assert(C::WAVES_M == 2 && E::S == 4, "two wave groups, four stages");
+  zero_acc(acc);
+  const int nk = (K + BK - 1) / BK;
+  if (nk <= 0) return;
+  E e;
+  e.init(A, B, m0, n0, tid);
+  const bool ga = (e.wave / C::WAVES_N) == 0;  // group A (wave-uniform)
+  // stage of tile kt is kt % 4; the loop is unrolled by 4 so every stage
+  // index is a constant
+  auto issue = [&](char* stage, int kt) {
+    const bool live = kt < nk;
+    e.da.load(stage, e.wave, A, kt * BK, live, KFULL);
+    e.db.load(stage + E::B_OFF, e.wave, B, kt * BK, live, KFULL);
+  };
+  auto mma_all = [&]() {
+#pragma unroll
+    for (int r = 0; r < E::NRL; ++r) e.mma_row(acc, 0, r);
+  };
+  issue(st.s[0], 0);
+  issue(st.s[1], 1);
+  issue(st.s[2], 2);
+  if (ga) {
+    issue(st.s[3], 3);
+    barrier_after_vmcnt<3 * NL>();
+    e.read_all(0, st.s[0]);
+    for (int t = 0; t < nk; t += 4) {
+#define PP_A(J)                                                             \
+      if (t + J >= nk) break;                                               \
+      mma_all();                                                            \
+      __builtin_amdgcn_sched_barrier(0);                                    \
+      barrier_after_vmcnt<2 * NL>();                                        \
+      if (t + J + 1 < nk) e.read_all(0, st.s[(J + 1) & 3]);                 \
+      issue(st.s[J & 3], t + J + 4);                                        \
+      __builtin_amdgcn_sched_barrier(0);                                    \
+      barrier_after_vmcnt<3 * NL>();
+      PP_A(0) PP_A(1) PP_A(2) PP_A(3)
+#undef PP_A
+    }
+  } else {
+    barrier_after_vmcnt<2 * NL>();
+    for (int t = 0; t < nk; t += 4) {
+#define PP_B(J)                                                             \
+      if (t + J >= nk) break;                                               \
+      e.read_all(0, st.s[J & 3]);                                           \
+      issue(st.s[(J + 3) & 3], t + J + 3);                                  \
+      __builtin_amdgcn_sched_barrier(0);                                    \
+      barrier_after_vmcnt<2 * NL>();                                        \
+      mma_all();                                                            \
+      __builtin_amdgcn_sched_barrier(0);                                    \
+      barrier_after_vmcnt<2 * NL>();
+      PP_B(0) PP_B(1) PP_B(2) PP_B(3)
+#undef PP_B
+    }
+  }
+  barrier_after_vmcnt<0>();
+}
+
 // Consecutive BM-row M tiles mt_begin .. mt_end-1 (K-major A, full K each)
 // against one BN-column N tile of K-major B, as ONE stream of K tiles: the
 // DMA for the next M tile's first K tiles is issued while the current one
@@ -856,15 +927,20 @@ __device__ __forceinline__ void gemm_stream_dma(const Opnd<bf16>& A, const Opnd<
   barrier_after_vmcnt<0>();
 }
 
-// bf16 tiles take the DMA pipeline over the four stages, fp32 tiles the
-// register-staged one over stage 0 (which is large enough for both of its
-// LDS buffers).
+// bf16 tiles take the DMA pipeline over the four stages: the ping-pong loop
+// when A is K-major, the rolling one when A is M-major (its fragment reads
+// transpose both operands, and the longer memory phase then outlasts the
+// other group's MFMAs).  fp32 tiles take the register-staged pipeline over
+// stage 0 (which is large enough for both of its LDS buffers).
 template <class C, bool A_KMAJOR, bool B_KMAJOR, bool KFULL = false>
 __device__ __forceinline__ void gemm_any(Acc<C>& acc, const Opnd<typename C::Elem>& A,
                                          const Opnd<typename C::Elem>& B, int m0, int n0, int K,
                                          const DmaStages& st, int tid) {
   if constexpr (sizeof(typename C::Elem) == 2) {
-    gemm_tile_dma<C, A_KMAJOR, B_KMAJOR, KFULL>(acc, A, B, m0, n0, K, st, tid);
+    if constexpr (A_KMAJOR)
+      gemm_tile_pp<C, A_KMAJOR, B_KMAJOR, KFULL>(acc, A, B, m0, n0, K, st, tid);
+    else
+      gemm_tile_dma<C, A_KMAJOR, B_KMAJOR, KFULL>(acc, A, B, m0, n0, K, st, tid);
   } else {
     typedef typename C::Elem T;
     static_assert(C::STAGE * sizeof(T) <= 32768, "an fp32 stage fits one DMA stage");
