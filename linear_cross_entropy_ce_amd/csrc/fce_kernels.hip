@@ -23,6 +23,8 @@
 #include <hip/hip_runtime.h>
 #include <math.h>
 
+#include <type_traits>
+
 #include "fce_gemm.h"
 
 namespace fce {
@@ -99,9 +101,8 @@ __device__ __forceinline__ void store4(float* p, float a, float b, float c, floa
 }
 __device__ __forceinline__ void store4(bf16* p, float a, float b, float c, float d) {
   typedef bf16 bf16x4 __attribute__((ext_vector_type(4)));
-  bf16x4 v = {static_cast<bf16>(a), static_cast<bf16>(b), static_cast<bf16>(c),
-              static_cast<bf16>(d)};
-  *reinterpret_cast<bf16x4*>(p) = v;
+  const floatx4 f = {a, b, c, d};
+  *reinterpret_cast<bf16x4*>(p) = __builtin_convertvector(f, bf16x4);
 }
 
 template <typename T>
@@ -148,10 +149,11 @@ __global__ __launch_bounds__(C::NT) void k_fwd_lse(FwdArgs<typename C::Elem> a) 
   }
 
   // Running (max, sum-exp, target logit, logit sum) update of one logit tile
-  // whose rows are the vocabulary entries m0 .. m0+BM-1.
-  auto lse_update = [&](const Acc<C>& acc, int m0) {
+  // whose rows are the vocabulary entries m0 .. m0+BM-1.  FULL: no row past
+  // V (every tile but the last), so the loops take no masks.
+  auto update = [&](auto full_c, const Acc<C>& acc, int m0) {
+    constexpr bool FULL = decltype(full_c)::value;
     const int vbase = m0 + wm * C::WTM;
-    const bool full = m0 + C::BM <= a.V;
 #pragma unroll
     for (int fn = 0; fn < C::FN; ++fn) {
       if constexpr (STORE) {
@@ -166,36 +168,59 @@ __global__ __launch_bounds__(C::NT) void k_fwd_lse(FwdArgs<typename C::Elem> a) 
                      acc.v[fm][fn][4 * g + 1], acc.v[fm][fn][4 * g + 2], acc.v[fm][fn][4 * g + 3]);
         }
       }
+      // Element i of block fm sits at row vbase + row(lane, 0) + off with
+      // off = fm MB + row(lane, i / 4) - row(lane, 0) + i % 4, the same for
+      // every lane.  A token's label lies in this wave's WTM rows of one
+      // tile in about WTM / V of them: the search for the target logit runs
+      // only when some lane's does (a wave-uniform branch).
+      const int rel = yv[fn] - vbase - Map::row(lane, 0);
+      if (__ballot(static_cast<unsigned>(yv[fn] - vbase) < static_cast<unsigned>(C::WTM)) != 0) {
+        float tg = 0.0f;
+#pragma unroll
+        for (int fm = 0; fm < C::FM; ++fm)
+#pragma unroll
+          for (int i = 0; i < C::NV; ++i) {
+            const int off = fm * C::MB + Map::row(lane, i >> 2) - Map::row(lane, 0) + (i & 3);
+            tg += (rel == off) ? acc.v[fm][fn][i] : 0.0f;
+          }
+        rt[fn] += tg;
+      }
       float tmax = -INFINITY;
 #pragma unroll
       for (int fm = 0; fm < C::FM; ++fm)
 #pragma unroll
         for (int i = 0; i < C::NV; ++i) {
-          const int v = vbase + fm * C::MB + Map::row(lane, i >> 2) + (i & 3);
-          if (full || v < a.V) tmax = fmaxf(tmax, acc.v[fm][fn][i]);
+          const int off = fm * C::MB + Map::row(lane, i >> 2) - Map::row(lane, 0) + (i & 3);
+          if (FULL || vbase + Map::row(lane, 0) + off < a.V) tmax = fmaxf(tmax, acc.v[fm][fn][i]);
         }
       const float mnew = fmaxf(rm[fn], tmax);
       if (mnew == -INFINITY) continue;  // nothing valid seen yet in this lane
-      float s = 0.0f, zs = 0.0f, tg = 0.0f;
+      // exp(z - m) as exp2(z log2e - m log2e): one FMA per element
+      const float mb = mnew * kLog2e;
+      float s = 0.0f, zs = 0.0f;
 #pragma unroll
       for (int fm = 0; fm < C::FM; ++fm)
 #pragma unroll
         for (int i = 0; i < C::NV; ++i) {
-          const int v = vbase + fm * C::MB + Map::row(lane, i >> 2) + (i & 3);
+          const int off = fm * C::MB + Map::row(lane, i >> 2) - Map::row(lane, 0) + (i & 3);
           const float z = acc.v[fm][fn][i];
-          const bool ok = full || v < a.V;
-          s += ok ? hw_exp2((z - mnew) * kLog2e) : 0.0f;
+          const bool ok = FULL || vbase + Map::row(lane, 0) + off < a.V;
+          s += ok ? hw_exp2(__builtin_fmaf(z, kLog2e, -mb)) : 0.0f;
           if (SMOOTH) zs += ok ? z : 0.0f;
-          tg += (v == yv[fn]) ? z : 0.0f;
         }
       rl[fn] = rl[fn] * hw_exp2((rm[fn] - mnew) * kLog2e) + s;
       rm[fn] = mnew;
-      rt[fn] += tg;
       rz[fn] += zs;
       // one token column at a time: keeps the accumulator copies it needs,
       // not the whole tile's, in vector registers
       __builtin_amdgcn_sched_barrier(0);
     }
+  };
+  auto lse_update = [&](const Acc<C>& acc, int m0) {
+    if (m0 + C::BM <= a.V)
+      update(std::true_type{}, acc, m0);
+    else
+      update(std::false_type{}, acc, m0);
   };
   if (sizeof(T) == 2 && a.H % 128 == 0) {
     // bf16: all vocabulary tiles of this split as one DMA stream
@@ -357,32 +382,86 @@ __global__ __launch_bounds__(C::NT) void k_bwd_dz(DzArgs<typename C::Elem> a) {
   typedef AccMap<C> Map;
   const float eps_v = a.eps / static_cast<float>(a.V);
   const float one_m_eps = 1.0f - a.eps;
-  if constexpr (FILTER) {
-    // dZ in place of the accumulators, then one kept flag for the tile
-    bool keep = false;
+  // FULL: no column past nvoc in this tile (workgroup-uniform; only the
+  // block's last vocabulary tile can have them), so no column masks.
+  auto epilogue = [&](auto full_c) {
+    constexpr bool FULL = decltype(full_c)::value;
+    bool keep = false;  // FILTER: this lane's vote
 #pragma unroll
     for (int fn = 0; fn < C::FN; ++fn) {
       const int tl = n0 + wn * C::WTN + fn * C::NB + Map::col(lane);
       const int y = tl < a.ntok ? a.labels[tl] : a.ignore;
       const bool valid = tl < a.ntok && label_ok(y, a.ignore, a.V);
       const float L = valid ? a.lse[tl] : 0.0f;
-      const int yl = valid ? y - a.voc0 : -1;
-      const float zf = 1.0f + 2.0f * a.zloss * L;
-      const float gi = (valid && a.gtok) ? a.gtok[tl] : 1.0f;
-      keep |= yl >= m0 && yl < m0 + C::BM;
+      // d(alpha LSE^2)/dz = 2 alpha LSE p; reduction none scales the row by
+      // g_i.  dZ = (e zf - eps/V) g_i with e = exp2(z log2e - LSE log2e) is
+      // two FMAs; an ignored row takes exponent offset +inf (e = 0) and
+      // g_i = 0, so its dZ is exactly 0.
+      const float gi = valid ? (a.gtok ? a.gtok[tl] : 1.0f) : 0.0f;
+      const float lb = valid ? L * kLog2e : INFINITY;
+      const float c1 = (1.0f + 2.0f * a.zloss * L) * gi;
+      const float c0 = -eps_v * gi;
+      const int vrow = m0 + wm * C::WTM + Map::row(lane, 0);  // row of element 0
+      T* row = a.dz + static_cast<int64_t>(tl) * a.ldz + vrow;
+      // The one-hot term, (1 - eps) g_i at the label column.  Element i of
+      // block fm sits at row vrow + off(fm, i), off the same for every lane.
+      // The label lies in this wave's WTM rows of the tile for few tokens,
+      // so only then does the loop test for it (chosen once per column by a
+      // wave-uniform branch); subtracting 0 elsewhere would not change a bit.
+      const int rel = valid ? y - a.voc0 - vrow : -1 - C::WTM;
+      const float t = one_m_eps * gi;
+      if constexpr (FILTER) {
+        // dZ in place of the accumulators and this lane's vote; the tile is
+        // stored below if any lane of the workgroup votes to keep it
+        keep |= valid && static_cast<unsigned>(y - a.voc0 - m0) < static_cast<unsigned>(C::BM);
 #pragma unroll
-      for (int fm = 0; fm < C::FM; ++fm)
+        for (int fm = 0; fm < C::FM; ++fm)
 #pragma unroll
-        for (int i = 0; i < C::NV; ++i) {
-          const int v = m0 + wm * C::WTM + fm * C::MB + Map::row(lane, i >> 2) + (i & 3);
-          const bool in = valid && v < a.nvoc;
-          const float e = hw_exp2((acc.v[fm][fn][i] - L) * kLog2e);
-          keep |= in && e >= kFilterP;
-          float p = e * zf - eps_v;
-          if (v == yl) p -= one_m_eps;
-          acc.v[fm][fn][i] = in ? p * gi : 0.0f;
-        }
+          for (int i = 0; i < C::NV; ++i) {
+            const int off = fm * C::MB + Map::row(lane, i >> 2) - Map::row(lane, 0) + (i & 3);
+            const bool ok = FULL || vrow + off < a.nvoc;
+            const float e = hw_exp2(__builtin_fmaf(acc.v[fm][fn][i], kLog2e, -lb));
+            keep |= ok && e >= kFilterP;
+            float d = __builtin_fmaf(e, c1, c0);
+            d -= (rel == off) ? t : 0.0f;
+            acc.v[fm][fn][i] = ok ? d : 0.0f;
+          }
+      } else {
+        auto column = [&](auto label_c) {
+          constexpr bool LABEL = decltype(label_c)::value;
+#pragma unroll
+          for (int fm = 0; fm < C::FM; ++fm)
+#pragma unroll
+            for (int g = 0; g < Map::NGRP; ++g) {
+              const int off0 = fm * C::MB + Map::row(lane, g) - Map::row(lane, 0);
+              float d[4];
+#pragma unroll
+              for (int q = 0; q < 4; ++q) {
+                d[q] = __builtin_fmaf(
+                    hw_exp2(__builtin_fmaf(acc.v[fm][fn][4 * g + q], kLog2e, -lb)), c1, c0);
+                if (LABEL) d[q] -= (rel == off0 + q) ? t : 0.0f;
+                if (!FULL) d[q] = (vrow + off0 + q < a.nvoc) ? d[q] : 0.0f;
+              }
+              store4(row + off0, d[0], d[1], d[2], d[3]);
+            }
+        };
+        if (__ballot(static_cast<unsigned>(rel + Map::row(lane, 0)) <
+                     static_cast<unsigned>(C::WTM)) != 0)
+          column(std::true_type{});
+        else
+          column(std::false_type{});
+      }
     }
+    return keep;
+  };
+  // (the filtered path rewrites the accumulators in place: one masked copy,
+  // whose masks are all true in full tiles, keeps it in registers)
+  bool keep;
+  if (!FILTER && m0 + C::BM <= a.nvoc)
+    keep = epilogue(std::true_type{});
+  else
+    keep = epilogue(std::false_type{});
+  if constexpr (FILTER) {
     __shared__ int s_keep[C::NT / 64];
     const bool wave_keep = __ballot(keep) != 0;  // every lane votes
     if (lane == 0) s_keep[wave] = wave_keep;
@@ -402,36 +481,6 @@ __global__ __launch_bounds__(C::NT) void k_bwd_dz(DzArgs<typename C::Elem> a) {
         for (int g = 0; g < Map::NGRP; ++g)
           store4(row + m0 + wm * C::WTM + fm * C::MB + Map::row(lane, g), acc.v[fm][fn][4 * g],
                  acc.v[fm][fn][4 * g + 1], acc.v[fm][fn][4 * g + 2], acc.v[fm][fn][4 * g + 3]);
-    }
-    return;
-  }
-#pragma unroll
-  for (int fn = 0; fn < C::FN; ++fn) {
-    const int tl = n0 + wn * C::WTN + fn * C::NB + Map::col(lane);
-    const int y = tl < a.ntok ? a.labels[tl] : a.ignore;
-    const bool valid = tl < a.ntok && label_ok(y, a.ignore, a.V);
-    const float L = valid ? a.lse[tl] : 0.0f;
-    const int yl = valid ? y - a.voc0 : -1;  // label as a block-local column
-    // d(alpha LSE^2)/dz = 2 alpha LSE p; reduction none scales the row by g_i
-    const float zf = 1.0f + 2.0f * a.zloss * L;
-    const float gi = (valid && a.gtok) ? a.gtok[tl] : 1.0f;
-    T* row = a.dz + static_cast<int64_t>(tl) * a.ldz;
-#pragma unroll
-    for (int fm = 0; fm < C::FM; ++fm) {
-#pragma unroll
-      for (int g = 0; g < Map::NGRP; ++g) {
-        const int v0 = m0 + wm * C::WTM + fm * C::MB + Map::row(lane, g);
-        float d[4];
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const int v = v0 + q;
-          const float z = acc.v[fm][fn][4 * g + q];
-          float p = hw_exp2((z - L) * kLog2e) * zf - eps_v;
-          if (v == yl) p -= one_m_eps;
-          d[q] = (valid && v < a.nvoc) ? p * gi : 0.0f;
-        }
-        store4(row + v0, d[0], d[1], d[2], d[3]);
-      }
     }
   }
 }

@@ -159,6 +159,28 @@ def test_filtered_split_calls_per_token_gradient():
     assert rel_l2(got["dX"], ref.result.dX) <= 2e-2 and rel_l2(got["dW"], ref.result.dW) <= 2e-2
 
 
+def test_filtered_with_every_tile_kept_equals_exact_bitwise():
+    # A flat spread of logits (sd 0.8 over 3000 classes: every tile holds
+    # softmax values above 2^-12) keeps every tile, and the filtered dZ
+    # epilogue computes each element as the exact one does: the gradients
+    # must be the exact path's bits.  Ragged N and V, smoothing, z-loss and
+    # ignored rows; chunk 512 splits the logits into several blocks.
+    g = np.random.default_rng(11)
+    N, H, V = 600, 264, 3000
+    X = wk.bf16_bits_to_f32(wk.round_to_bf16_bits(g.standard_normal((N, H)).astype(np.float32)))
+    W = wk.bf16_bits_to_f32(wk.round_to_bf16_bits(
+        (0.05 * g.standard_normal((V, H))).astype(np.float32)))
+    y = g.integers(0, V, N).astype(np.int32)
+    y[g.choice(N, 30, replace=False)] = -100
+    kw = dict(chunk=512, label_smoothing=0.1, z_loss=1e-3)
+    dev = to_dev(X, W, y)
+    got = run(*dev, variant="filtered", **kw)
+    ref = run(*dev, variant="recompute", **kw)
+    assert got["kept"] == got["total"] == 3 * 12
+    assert np.array_equal(got["loss"], ref["loss"])
+    assert np.array_equal(got["dX"], ref["dX"]) and np.array_equal(got["dW"], ref["dW"])
+
+
 def test_filtered_all_ignored_block_counts_as_skipped():
     X, W, y = structured(2)
     y[:256] = -100  # the first token tile has no valid row
