@@ -878,26 +878,36 @@ __device__ __forceinline__ void gemm_tile_pp(Acc<C>& acc, const Opnd<bf16>& A,
 }
 
 // Consecutive BM-row M tiles mt_begin .. mt_end-1 (K-major A, full K each)
-// against one BN-column N tile of K-major B, as ONE stream of K tiles: the
-// DMA for the next M tile's first K tiles is issued while the current one
-// finishes, so the pipeline never drains between M tiles.  After each M tile
-// epi(acc, m0) consumes the accumulators (registers only; LDS stays with the
-// pipeline) and they restart from zero.  Needs K % 128 == 0 (M tile
-// boundaries on the unrolled-by-four trip).  Ends with all DMA drained and a
-// barrier.
+// against one BN-column N tile of K-major B, as ONE stream of K tiles on the
+// ping-pong loop of gemm_tile_pp: the DMA for the next M tile's first K
+// tiles is issued while the current one finishes, so the pipeline never
+// drains between M tiles.  After each M tile epi(acc, m0) consumes the
+// accumulators (registers only; LDS stays with the pipeline) and they
+// restart from zero.  Each group runs its epilogue at the start of one of
+// its own memory phases, before the fragment reads (so that the fragment
+// registers are free), while the other group's MFMAs run: group A right
+// after its last MFMA phase of the M tile, group B right after the barrier
+// that closes its own.  Needs K % 128 == 0: nk is then a multiple of 4, so
+// the stage of a K tile is kt % 4 in every M tile and the unrolled stage
+// indices hold across M tile boundaries.  Every quad of K tiles is straight-
+// line code with the epilogue only in the last one: a branch with the
+// accumulators live across it makes the register allocator copy them.
+// Ends with all DMA drained and a barrier.
 template <class C, class Epi>
-__device__ __forceinline__ void gemm_stream_dma(const Opnd<bf16>& A, const Opnd<bf16>& B,
-                                                int mt_begin, int mt_end, int n0, int K,
-                                                const DmaStages& st, int tid, Epi&& epi) {
+__device__ __forceinline__ void gemm_stream_pp(const Opnd<bf16>& A, const Opnd<bf16>& B,
+                                               int mt_begin, int mt_end, int n0, int K,
+                                               const DmaStages& st, int tid, Epi&& epi) {
   typedef DmaEngine<C, true, true, true> E;
-  constexpr int S = E::S, BK = E::BK;
+  constexpr int BK = E::BK, NL = E::NL;
+  static_assert(C::WAVES_M == 2 && E::S == 4, "two wave groups, four stages");
   const int nk = K / BK;
   Acc<C> acc;
   zero_acc(acc);
   if (mt_end <= mt_begin || nk <= 0) return;
   E e;
   e.init(A, B, mt_begin * C::BM, n0, tid);
-  // K tile kt of M tile mt; kt < nk + 3 (past the end it wraps into the next
+  const bool ga = (e.wave / C::WAVES_N) == 0;  // group A (wave-uniform)
+  // K tile kt of M tile mt; kt < nk + 4 (past the end it wraps into the next
   // M tile, past the last M tile the load is dead)
   auto issue = [&](char* stage, int mt, int kt) {
     int m = mt, k = kt;
@@ -909,20 +919,67 @@ __device__ __forceinline__ void gemm_stream_dma(const Opnd<bf16>& A, const Opnd<
     e.da.load_at(stage, e.wave, A, (live ? m : mt_begin) * C::BM, k * BK, live, true);
     e.db.load(stage + E::B_OFF, e.wave, B, k * BK, live, true);
   };
+  auto mma_all = [&]() {
+#pragma unroll
+    for (int r = 0; r < E::NRL; ++r) e.mma_row(acc, 0, r);
+  };
   issue(st.s[0], mt_begin, 0);
   issue(st.s[1], mt_begin, 1);
   issue(st.s[2], mt_begin, 2);
-  barrier_after_vmcnt<E::NL * (S - 2)>();
-  e.read_all(0, st.s[0]);
-  for (int mt = mt_begin; mt < mt_end; ++mt) {
-    for (int kt = 0; kt < nk; kt += S) {
-      e.template step<0>(acc, st.s[1], [&] { issue(st.s[3], mt, kt + 3); });
-      e.template step<1>(acc, st.s[2], [&] { issue(st.s[0], mt, kt + 4); });
-      e.template step<0>(acc, st.s[3], [&] { issue(st.s[1], mt, kt + 5); });
-      e.template step<1>(acc, st.s[0], [&] { issue(st.s[2], mt, kt + 6); });
+  if (ga) {
+    issue(st.s[3], mt_begin, 3);
+    barrier_after_vmcnt<3 * NL>();
+    e.read_all(0, st.s[0]);
+    for (int mt = mt_begin; mt < mt_end; ++mt) {
+      // four K tiles from t; the last four of the M tile end with its epilogue
+      auto quad = [&](int t, auto last_c) {
+        constexpr bool LAST = decltype(last_c)::value;
+#define PS_A(J)                                                             \
+        mma_all();                                                          \
+        __builtin_amdgcn_sched_barrier(0);                                  \
+        barrier_after_vmcnt<2 * NL>();                                      \
+        if constexpr (LAST && J == 3) {                                     \
+          epi(acc, mt * C::BM);                                             \
+          zero_acc(acc);                                                    \
+          __builtin_amdgcn_sched_barrier(0);                                \
+        }                                                                   \
+        e.read_all(0, st.s[(J + 1) & 3]);                                   \
+        issue(st.s[J & 3], mt, t + J + 4);                                  \
+        __builtin_amdgcn_sched_barrier(0);                                  \
+        barrier_after_vmcnt<3 * NL>();
+        PS_A(0) PS_A(1) PS_A(2) PS_A(3)
+#undef PS_A
+      };
+      for (int t = 0; t < nk - 4; t += 4) quad(t, std::false_type{});
+      quad(nk - 4, std::true_type{});
     }
-    epi(acc, mt * C::BM);
-    zero_acc(acc);
+  } else {
+    barrier_after_vmcnt<2 * NL>();
+    for (int mt = mt_begin; mt < mt_end; ++mt) {
+      // four K tiles from t; the last four of the M tile end with its
+      // epilogue, after the barrier that closes their last MFMA phase (so
+      // at the start of the group's next memory phase)
+      auto quad = [&](int t, auto last_c) {
+        constexpr bool LAST = decltype(last_c)::value;
+#define PS_B(J)                                                             \
+        e.read_all(0, st.s[J & 3]);                                         \
+        issue(st.s[(J + 3) & 3], mt, t + J + 3);                            \
+        __builtin_amdgcn_sched_barrier(0);                                  \
+        barrier_after_vmcnt<2 * NL>();                                      \
+        mma_all();                                                          \
+        __builtin_amdgcn_sched_barrier(0);                                  \
+        barrier_after_vmcnt<2 * NL>();                                      \
+        if constexpr (LAST && J == 3) {                                     \
+          epi(acc, mt * C::BM);                                             \
+          zero_acc(acc);                                                    \
+          __builtin_amdgcn_sched_barrier(0);                                \
+        }
+        PS_B(0) PS_B(1) PS_B(2) PS_B(3)
+#undef PS_B
+      };
+      for (int t = 0; t < nk - 4; t += 4) quad(t, std::false_type{});
+      quad(nk - 4, std::true_type{});
+    }
   }
   barrier_after_vmcnt<0>();
 }

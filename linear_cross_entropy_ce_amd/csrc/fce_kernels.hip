@@ -121,7 +121,9 @@ struct FwdArgs {
 // STORE: also write every logit tile, rounded to T, to zout (the logits of
 // the store-logits variant).  Columns past V hold 0 (W rows past V load as
 // zeros), so a row is written up to the vocabulary tile coverage.
-template <class C, bool SMOOTH, bool STORE>
+// STREAM (bf16, H % 128 == 0): all vocabulary tiles of the split as one DMA
+// stream; otherwise one GEMM tile and its epilogue per vocabulary tile.
+template <class C, bool SMOOTH, bool STORE, bool STREAM>
 __global__ __launch_bounds__(C::NT) void k_fwd_lse(FwdArgs<typename C::Elem> a) {
   typedef typename C::Elem T;
   FCE_DMA_STAGES(lds);
@@ -222,10 +224,9 @@ __global__ __launch_bounds__(C::NT) void k_fwd_lse(FwdArgs<typename C::Elem> a) 
     else
       update(std::false_type{}, acc, m0);
   };
-  if (sizeof(T) == 2 && a.H % 128 == 0) {
-    // bf16: all vocabulary tiles of this split as one DMA stream
-    if constexpr (sizeof(T) == 2)
-      gemm_stream_dma<C>(A, B, vt_begin, vt_end, n0, a.H, lds, tid, lse_update);
+  if constexpr (STREAM) {
+    static_assert(sizeof(T) == 2, "the stream is bf16");
+    gemm_stream_pp<C>(A, B, vt_begin, vt_end, n0, a.H, lds, tid, lse_update);
   } else {
     Acc<C> acc;
     for (int vt = vt_begin; vt < vt_end; ++vt) {
@@ -273,6 +274,18 @@ __global__ __launch_bounds__(C::NT) void k_fwd_lse(FwdArgs<typename C::Elem> a) 
       if (tok < a.N) a.part[static_cast<int64_t>(sp) * a.n_pad + tok] = st;
     }
   }
+}
+
+// The forward over grid workgroups: the stream when the operands allow it.
+template <class C, bool SMOOTH, bool STORE>
+void launch_fwd_lse(const FwdArgs<typename C::Elem>& fa, int grid, hipStream_t st) {
+  if constexpr (sizeof(typename C::Elem) == 2) {
+    if (fa.H % 128 == 0) {
+      k_fwd_lse<C, SMOOTH, STORE, true><<<grid, C::NT, 0, st>>>(fa);
+      return;
+    }
+  }
+  k_fwd_lse<C, SMOOTH, STORE, false><<<grid, C::NT, 0, st>>>(fa);
 }
 
 // Per token: LSE from the split partials, the loss term
@@ -927,9 +940,9 @@ hipError_t run_forward(const Plan& p, const T* X, const T* W, const int32_t* lab
     const double flops = 2.0 * static_cast<double>(p.N) * p.V * p.H;
     timer->begin("fwd_lse", flops, st);
     if (eps != 0.0f)
-      k_fwd_lse<C, true, false><<<grid, C::NT, 0, st>>>(fa);
+      launch_fwd_lse<C, true, false>(fa, grid, st);
     else
-      k_fwd_lse<C, false, false><<<grid, C::NT, 0, st>>>(fa);
+      launch_fwd_lse<C, false, false>(fa, grid, st);
     FCE_CHECK_LAUNCH();
     timer->end(st);
     timer->begin("lse_merge", 0.0, st);
@@ -1192,9 +1205,9 @@ hipError_t run_fused_store(const Plan& p, const T* X, const T* W, const int32_t*
     const double blk_flops = 2.0 * static_cast<double>(ntok) * V * H;
     timer->begin("sl_fwd", blk_flops, st);
     if (o.eps != 0.0f)
-      k_fwd_lse<C, true, true><<<fa.tok_tiles * fa.splits, C::NT, 0, st>>>(fa);
+      launch_fwd_lse<C, true, true>(fa, fa.tok_tiles * fa.splits, st);
     else
-      k_fwd_lse<C, false, true><<<fa.tok_tiles * fa.splits, C::NT, 0, st>>>(fa);
+      launch_fwd_lse<C, false, true>(fa, fa.tok_tiles * fa.splits, st);
     FCE_CHECK_LAUNCH();
     timer->end(st);
     timer->begin("lse_merge", 0.0, st);
