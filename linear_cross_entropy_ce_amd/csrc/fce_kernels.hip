@@ -21,6 +21,7 @@
 #include "fce_kernels.h"
 
 #include <hip/hip_runtime.h>
+#include <limits.h>
 #include <math.h>
 
 #include <type_traits>
@@ -496,6 +497,124 @@ __global__ __launch_bounds__(C::NT) void k_bwd_dz(DzArgs<typename C::Elem> a) {
                  acc.v[fm][fn][4 * g + 1], acc.v[fm][fn][4 * g + 2], acc.v[fm][fn][4 * g + 3]);
     }
   }
+}
+
+// dZ as one DMA stream per workgroup (bf16, H % 128 == 0, no filtering):
+// one token tile against vocabulary tiles vt_begin .. vt_end-1 of the block,
+// the recompute of each logit tile on the ping-pong stream of gemm_stream_pp
+// and its dZ epilogue in the memory phase of each wave group, so the K
+// pipeline stays full across vocabulary tiles and one group's epilogue runs
+// beside the other group's MFMAs.  Same dZ bits as k_bwd_dz: the per-token
+// factors are computed once, before the stream, with the same expressions.
+template <class C>
+__global__ __launch_bounds__(C::NT) void k_bwd_dz_stream(DzArgs<bf16> a, int splits) {
+  int tt, sp;
+  grouped_tile(xcd_remap(blockIdx.x, a.tok_tiles * splits), a.tok_tiles, splits, a.group_m, tt,
+               sp);
+  if (*a.flag == 0) return;  // every label of this token block is ignored
+  FCE_DMA_STAGES(lds);
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave / C::WAVES_N, wn = wave % C::WAVES_N;
+  const int n0 = tt * C::BN;
+  const int vt_begin = static_cast<int>(static_cast<int64_t>(sp) * a.voc_tiles / splits);
+  const int vt_end = static_cast<int>(static_cast<int64_t>(sp + 1) * a.voc_tiles / splits);
+  const Opnd<bf16> A{a.W, a.H, a.nvoc, a.H};
+  const Opnd<bf16> B{a.X, a.H, a.ntok, a.H};
+  typedef AccMap<C> Map;
+  const float eps_v = a.eps / static_cast<float>(a.V);
+  const float one_m_eps = 1.0f - a.eps;
+  // Per token column of the tile, kept in LDS beside the four stages (so
+  // that nothing live across the stream is spilled): the exponent offset
+  // LSE log2e (+inf for an ignored row), dZ = exp * c1 + c0, the one-hot
+  // term t at the label, and the label's row in the block (far out of range
+  // for an ignored row).
+  __shared__ float s_lb[C::BN], s_c1[C::BN], s_c0[C::BN], s_tk[C::BN];
+  __shared__ int s_yv[C::BN];
+  for (int c = tid; c < C::BN; c += C::NT) {
+    const int tl = n0 + c;
+    const int y = tl < a.ntok ? a.labels[tl] : a.ignore;
+    const bool valid = tl < a.ntok && label_ok(y, a.ignore, a.V);
+    const float L = valid ? a.lse[tl] : 0.0f;
+    const float gi = valid ? (a.gtok ? a.gtok[tl] : 1.0f) : 0.0f;
+    s_lb[c] = valid ? L * kLog2e : INFINITY;
+    s_c1[c] = (1.0f + 2.0f * a.zloss * L) * gi;
+    s_c0[c] = -eps_v * gi;
+    s_tk[c] = one_m_eps * gi;
+    s_yv[c] = valid ? y - a.voc0 : INT_MIN / 2;
+  }
+  __syncthreads();
+  const int rbase = wm * C::WTM + Map::row(lane, 0);
+  // Store staging: one 16-token column of a wave's WTM-row strip at a time
+  // passes through LDS, so that each store writes 16-byte pieces of whole
+  // token-row segments (2 WTM bytes) instead of 8-byte pieces scattered
+  // over 16 rows.  Region wn serves the two waves of column wn, whose
+  // epilogues are half a K step apart with a workgroup barrier between
+  // them (and the LDS operations of a wave run in order).  Rows are padded
+  // by 16 bytes, which spreads the writes of the 16 tokens over the banks.
+  constexpr int kRowB = 2 * C::WTM, kPitch = kRowB + 16, kPieces = kRowB / 16;
+  static_assert(C::NB == 16 && Map::NGRP == 1 && 64 % kPieces == 0, "staging geometry");
+  __shared__ __attribute__((aligned(16))) char s_stage[C::WAVES_N][C::NB * kPitch];
+  char* const stg = s_stage[wn];
+  typedef bf16 bf16x4 __attribute__((ext_vector_type(4)));
+  auto epilogue = [&](auto full_c, const Acc<C>& acc, int m0) {
+    constexpr bool FULL = decltype(full_c)::value;
+    const int vrow = m0 + rbase;  // row of element 0
+#pragma unroll
+    for (int fn = 0; fn < C::FN; ++fn) {
+      const int c = wn * C::WTN + fn * C::NB + Map::col(lane);
+      const float lb = s_lb[c], c1 = s_c1[c], c0 = s_c0[c], tk = s_tk[c];
+      const int rel = s_yv[c] - vrow;
+      auto column = [&](auto label_c) {
+        constexpr bool LABEL = decltype(label_c)::value;
+#pragma unroll
+        for (int fm = 0; fm < C::FM; ++fm) {
+          const int off0 = fm * C::MB;
+          floatx4 d;
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            float v = __builtin_fmaf(
+                hw_exp2(__builtin_fmaf(acc.v[fm][fn][q], kLog2e, -lb)), c1, c0);
+            if (LABEL) v -= (rel == off0 + q) ? tk : 0.0f;
+            if (!FULL) v = (vrow + off0 + q < a.nvoc) ? v : 0.0f;
+            d[q] = v;
+          }
+          *reinterpret_cast<bf16x4*>(stg + Map::col(lane) * kPitch +
+                                     2 * (off0 + Map::row(lane, 0))) =
+              __builtin_convertvector(d, bf16x4);
+        }
+      };
+      if (__ballot(static_cast<unsigned>(rel + Map::row(lane, 0)) <
+                   static_cast<unsigned>(C::WTM)) != 0)
+        column(std::true_type{});
+      else
+        column(std::false_type{});
+      // the strip's 16 token rows, 64 / kPieces of them per store, through a
+      // buffer resource based at this wave's strip of the tile (wave-uniform)
+      // so that the lane offset is one 32-bit register and the row offset a
+      // scalar
+      const __amdgpu_buffer_rsrc_t rs = make_rsrc(
+          a.dz + static_cast<int64_t>(n0 + wn * C::WTN) * a.ldz + m0 + wm * C::WTM,
+          static_cast<int64_t>(C::WTN) * a.ldz * 2);
+      const uint32_t ldz_b = static_cast<uint32_t>(a.ldz) * 2u;
+      const uint32_t voff = static_cast<uint32_t>(lane / kPieces) * ldz_b + 16u * (lane % kPieces);
+#pragma unroll
+      for (int j = 0; j < C::NB * kPieces / 64; ++j) {
+        const int t = j * (64 / kPieces) + lane / kPieces, piece = lane % kPieces;
+        const u32x4 v = *reinterpret_cast<const u32x4*>(stg + t * kPitch + 16 * piece);
+        __builtin_amdgcn_raw_buffer_store_b128(
+            v, rs, voff, static_cast<uint32_t>(fn * C::NB + j * (64 / kPieces)) * ldz_b, 0);
+      }
+      // one token column at a time (keeps the live values of one column)
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+  gemm_stream_pp<C>(A, B, vt_begin, vt_end, n0, a.H, lds, tid,
+                    [&](const Acc<C>& acc, int m0) {
+                      if (m0 + C::BM <= a.nvoc)
+                        epilogue(std::true_type{}, acc, m0);
+                      else
+                        epilogue(std::false_type{}, acc, m0);
+                    });
 }
 
 // ---------------------------------------------------- backward: dW and dX
@@ -1125,6 +1244,11 @@ hipError_t run_backward(const Plan& p, const T* X, const T* W, const int32_t* la
             k_bwd_dz<C, true, true><<<voc_tiles * tok_tiles, C::NT, 0, st>>>(da);
           else
             k_bwd_dz<C, false, true><<<voc_tiles * tok_tiles, C::NT, 0, st>>>(da);
+        } else if (H % 128 == 0) {
+          // about one workgroup per CU, each streaming a run of vocabulary tiles
+          const int splits = std::max(1, std::min(voc_tiles, kNumCUs / tok_tiles));
+          da.group_m = std::max(1, 32 / splits);
+          k_bwd_dz_stream<C><<<tok_tiles * splits, C::NT, 0, st>>>(da, splits);
         } else if (H % 32 == 0) {
           k_bwd_dz<C, true, false><<<voc_tiles * tok_tiles, C::NT, 0, st>>>(da);
         } else {
