@@ -106,6 +106,50 @@ __device__ __forceinline__ void store4(bf16* p, float a, float b, float c, float
   *reinterpret_cast<bf16x4*>(p) = __builtin_convertvector(f, bf16x4);
 }
 
+// Global-memory byte pointer.
+typedef __attribute__((address_space(1))) char gchar;
+
+// The same address in scalar registers as a global pointer (the caller
+// guarantees that p is wave-uniform), so that loads and stores address it as
+// a scalar base plus a 32-bit lane offset.
+template <typename P>
+__device__ __forceinline__ gchar* wave_uniform(P* p) {
+  const uint64_t b = reinterpret_cast<uint64_t>(p);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(b));
+  const uint32_t hi = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(b >> 32));
+  return reinterpret_cast<gchar*>((static_cast<uint64_t>(hi) << 32) | lo);
+}
+
+// 16-byte stores at base + off bytes, global or through a buffer resource.
+// The buffer form passes the whole offset in the vector register and a
+// constant 0 as the scalar offset: with a register scalar offset, a VALU
+// write of the data registers right after the store was seen to reach the
+// last lanes' copy of the first word, and the compiler only separates the
+// two when the scalar offset is a constant.
+__device__ __forceinline__ void store16(gchar* base, uint32_t off, u32x4 v) {
+  *reinterpret_cast<__attribute__((address_space(1))) u32x4*>(base + off) = v;
+}
+__device__ __forceinline__ void store16(__amdgpu_buffer_rsrc_t r, uint32_t off, u32x4 v) {
+  __builtin_amdgcn_raw_buffer_store_b128(v, r, off, 0, 0);
+}
+
+// a + b (b wave-uniform) computed where it is used: kept out of loop-invariant
+// hoisting, which would hold one register per use across the whole loop.
+__device__ __forceinline__ uint32_t add_at_use(uint32_t a, uint32_t b) {
+  uint32_t r;
+  asm volatile("v_add_u32 %0, %1, %2" : "=v"(r) : "s"(b), "v"(a));
+  return r;
+}
+
+// Waits until this wave's LDS reads have returned their data, as a compiler
+// memory barrier too.  Used where a staging region is read back in 16-byte
+// pieces and then rewritten: without the wait, writes issued right after
+// the reads have been seen to overwrite words those reads had not yet
+// returned.
+__device__ __forceinline__ void lds_reads_done() {
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+}
+
 template <typename T>
 struct FwdArgs {
   const T* X;
@@ -589,21 +633,25 @@ __global__ __launch_bounds__(C::NT) void k_bwd_dz_stream(DzArgs<bf16> a, int spl
       else
         column(std::false_type{});
       // the strip's 16 token rows, 64 / kPieces of them per store, through a
-      // buffer resource based at this wave's strip of the tile (wave-uniform)
-      // so that the lane offset is one 32-bit register and the row offset a
-      // scalar
+      // buffer resource based at this wave's strip of the tile, with 32-bit
+      // lane offsets
       const __amdgpu_buffer_rsrc_t rs = make_rsrc(
           a.dz + static_cast<int64_t>(n0 + wn * C::WTN) * a.ldz + m0 + wm * C::WTM,
           static_cast<int64_t>(C::WTN) * a.ldz * 2);
       const uint32_t ldz_b = static_cast<uint32_t>(a.ldz) * 2u;
       const uint32_t voff = static_cast<uint32_t>(lane / kPieces) * ldz_b + 16u * (lane % kPieces);
+      constexpr int NJ = C::NB * kPieces / 64;
+      u32x4 v[NJ];
 #pragma unroll
-      for (int j = 0; j < C::NB * kPieces / 64; ++j) {
+      for (int j = 0; j < NJ; ++j) {
         const int t = j * (64 / kPieces) + lane / kPieces, piece = lane % kPieces;
-        const u32x4 v = *reinterpret_cast<const u32x4*>(stg + t * kPitch + 16 * piece);
-        __builtin_amdgcn_raw_buffer_store_b128(
-            v, rs, voff, static_cast<uint32_t>(fn * C::NB + j * (64 / kPieces)) * ldz_b, 0);
+        v[j] = *reinterpret_cast<const u32x4*>(stg + t * kPitch + 16 * piece);
       }
+      lds_reads_done();  // before the next column's writes to the region
+#pragma unroll
+      for (int j = 0; j < NJ; ++j)
+        store16(rs, add_at_use(voff, static_cast<uint32_t>(fn * C::NB + j * (64 / kPieces)) * ldz_b),
+                v[j]);
       // one token column at a time (keeps the live values of one column)
       __builtin_amdgcn_sched_barrier(0);
     }
@@ -648,6 +696,65 @@ template <bool KMAJOR, typename T>
 __device__ __forceinline__ Opnd<T> opnd_from_k(const Opnd<T>& o, int k0) {
   return Opnd<T>{o.p + (KMAJOR ? static_cast<int64_t>(k0) : static_cast<int64_t>(k0) * o.ld), o.ld,
                  o.mn_ext, o.k_ext - k0};
+}
+
+// fp32 output of one full bf16 tile (16 x 16 blocks), scaled by s, stored
+// or added to the values in place, through LDS: each wave stages 32 rows of
+// its WTM x WTN strip at a time in a region of its own within the DMA stages
+// (free once the K loop has drained), then moves whole row segments of WTN
+// floats with 16-byte loads and stores.  The lane-per-element epilogue moves
+// 4-byte pieces over four rows per instruction instead.  Same arithmetic, in
+// the same order, as that epilogue: out = old + s acc, or s acc.
+template <class C>
+__device__ __forceinline__ void store_grad_tile_staged(const Acc<C>& acc, float s, float* tile,
+                                                       int64_t ldo, bool accumulate,
+                                                       const DmaStages& st, int wave, int lane) {
+  typedef AccMap<C> Map;
+  constexpr int kRows = 32, kRowB = 4 * C::WTN, kPitch = kRowB + 16, kPieces = kRowB / 16;
+  constexpr int kRowsPer = 64 / kPieces;  // rows per 16-byte instruction
+  static_assert(C::MB == 16 && C::NB == 16 && Map::NGRP == 1 && C::WTM % kRows == 0 &&
+                    64 % kPieces == 0 && 2 * kRows * kPitch <= 32768 && C::NT / 64 <= 8,
+                "staging geometry: two waves per 32 KiB stage");
+  const int wm = wave / C::WAVES_N, wn = wave % C::WAVES_N;
+  const int w2 = wave >> 1;  // (constant indices: the stage table is not an array in memory)
+  char* const reg = (w2 == 0 ? st.s[0] : w2 == 1 ? st.s[1] : w2 == 2 ? st.s[2] : st.s[3]) +
+                    (wave & 1) * (kRows * kPitch);
+  gchar* const sb = wave_uniform(tile + static_cast<int64_t>(wm * C::WTM) * ldo + wn * C::WTN);
+  const uint32_t ldo_b = static_cast<uint32_t>(ldo) * 4u;
+  const uint32_t voff = static_cast<uint32_t>(lane / kPieces) * ldo_b + 16u * (lane % kPieces);
+#pragma unroll
+  for (int rr = 0; rr < C::WTM / kRows; ++rr) {
+    // element (fm, fn, q): row fm MB + row(lane, 0) + q, column fn NB + col(lane)
+#pragma unroll
+    for (int j = 0; j < kRows / C::MB; ++j)
+#pragma unroll
+      for (int fn = 0; fn < C::FN; ++fn)
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          *reinterpret_cast<float*>(reg + (j * C::MB + Map::row(lane, 0) + q) * kPitch +
+                                    4 * (fn * C::NB + Map::col(lane))) =
+              s * acc.v[rr * (kRows / C::MB) + j][fn][q];
+    constexpr int NI = kRows / kRowsPer;
+    floatx4 v[NI], old[NI];
+#pragma unroll
+    for (int t = 0; t < NI; ++t) {
+      const uint32_t soff = static_cast<uint32_t>(rr * kRows + t * kRowsPer) * ldo_b;
+      old[t] = accumulate
+                   ? *reinterpret_cast<const __attribute__((address_space(1))) floatx4*>(sb + voff + soff)
+                          : floatx4{0.0f, 0.0f, 0.0f, 0.0f};
+    }
+#pragma unroll
+    for (int t = 0; t < NI; ++t)
+      v[t] = *reinterpret_cast<const floatx4*>(
+          reg + (t * kRowsPer + lane / kPieces) * kPitch + 16 * (lane % kPieces));
+    lds_reads_done();  // before the next round's writes to the region
+#pragma unroll
+    for (int t = 0; t < NI; ++t) {
+      const uint32_t soff = static_cast<uint32_t>(rr * kRows + t * kRowsPer) * ldo_b;
+      const floatx4 o = accumulate ? old[t] + v[t] : v[t];
+      store16(sb, voff + soff, __builtin_bit_cast(u32x4, o));
+    }
+  }
 }
 
 template <class C, bool A_KMAJOR, bool FILTER>
@@ -710,6 +817,12 @@ __global__ __launch_bounds__(C::NT) void k_bwd_grad(GradArgs<typename C::Elem> a
   const int cbase = wn * C::WTN + Map::col(lane);
   const bool full = m0 + C::BM <= a.m_valid && n0 + C::BN <= a.n_valid;
   float* tile = out + static_cast<int64_t>(m0) * a.ldo + n0;
+  if constexpr (sizeof(T) == 2) {
+    if (full) {
+      store_grad_tile_staged<C>(acc, s, tile, a.ldo, a.accumulate != 0, lds, wave, lane);
+      return;
+    }
+  }
 #pragma unroll
   for (int f0 = 0; f0 < C::FM; f0 += SLAB) {
     float old[SLAB][C::FN][C::NV];
