@@ -140,10 +140,13 @@ def test_all_labels_ignored():
     assert not got["dX"].any() and not got["dW"].any()
 
 
-def test_one_token_block_all_ignored():
-    wl = wk.custom(600, 64, 700, "bf16", seed=53, ignore_frac=0.0)
+@pytest.mark.parametrize("H,block", [(64, 0), (256, 0), (256, 1)])
+def test_one_token_block_all_ignored(H, block):
+    # H = 64 takes the per-tile dZ kernel, H = 256 the streamed one; with the
+    # middle block ignored, dW is accumulated both before and after it
+    wl = wk.custom(700, H, 3000, "bf16", seed=53, ignore_frac=0.0)
     inp = wk.draw(wl)
-    inp.labels[:256] = -100  # the first 256-token block has no valid label
+    inp.labels[256 * block:256 * (block + 1)] = -100  # one 256-token block has no valid label
     got = run(inp, chunk=256, schedule="token")
     check_against_oracle(inp, got)
 
