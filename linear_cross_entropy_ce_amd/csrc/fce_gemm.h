@@ -984,6 +984,121 @@ __device__ __forceinline__ void gemm_stream_pp(const Opnd<bf16>& A, const Opnd<b
   barrier_after_vmcnt<0>();
 }
 
+// gemm_stream_pp for an epilogue that stores: epi issues at least NS
+// vector-memory instructions per wave (its stores, all of them
+// unconditional).  gfx950 retires vector loads and stores in issue order
+// against vmcnt, so a wait that aims at a DMA issued before an epilogue's
+// stores must count them as outstanding, or it holds the wave until the
+// newer prefetches and the stores have landed.  After an epilogue that is
+// the last wait of group A's epilogue quad and the first four waits of the
+// next quad of either group.  So that the first M tile runs the same code,
+// each wave first issues NS stores that the hardware drops (a buffer
+// resource of zero bytes) where an epilogue's stores would sit, and the
+// prologue waits count them too.  Needs K % 128 == 0 and K >= 256 (two quads
+// or more per M tile, so a quad never both follows and holds an epilogue).
+template <class C, int NS, class Epi>
+__device__ __forceinline__ void gemm_stream_pp_st(const Opnd<bf16>& A, const Opnd<bf16>& B,
+                                                  int mt_begin, int mt_end, int n0, int K,
+                                                  const DmaStages& st, int tid, Epi&& epi) {
+  typedef DmaEngine<C, true, true, true> E;
+  constexpr int BK = E::BK, NL = E::NL;
+  static_assert(C::WAVES_M == 2 && E::S == 4, "two wave groups, four stages");
+  static_assert(NS > 0 && 3 * NL + NS <= 63, "vmcnt counts up to 63");
+  const int nk = K / BK;
+  Acc<C> acc;
+  zero_acc(acc);
+  if (mt_end <= mt_begin || nk < 8) return;
+  E e;
+  e.init(A, B, mt_begin * C::BM, n0, tid);
+  const bool ga = (e.wave / C::WAVES_N) == 0;  // group A (wave-uniform)
+  auto issue = [&](char* stage, int mt, int kt) {
+    int m = mt, k = kt;
+    if (k >= nk) {
+      k -= nk;
+      ++m;
+    }
+    const bool live = m < mt_end;
+    e.da.load_at(stage, e.wave, A, (live ? m : mt_begin) * C::BM, k * BK, live, true);
+    e.db.load(stage + E::B_OFF, e.wave, B, k * BK, live, true);
+  };
+  auto mma_all = [&]() {
+#pragma unroll
+    for (int r = 0; r < E::NRL; ++r) e.mma_row(acc, 0, r);
+  };
+  issue(st.s[0], mt_begin, 0);
+  issue(st.s[1], mt_begin, 1);
+  issue(st.s[2], mt_begin, 2);
+  {
+    // NS dropped stores in place of a previous epilogue's (distinct offsets
+    // and volatile, so that the compiler keeps every one of them)
+    const __amdgpu_buffer_rsrc_t none = make_rsrc(A.p, 0);
+    constexpr int kVolatile = static_cast<int>(1u << 31);  // intrinsic aux bit 31
+#pragma unroll
+    for (int i = 0; i < NS; ++i) __builtin_amdgcn_raw_buffer_store_b32(0u, none, 4 * i, 0, kVolatile);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  if (ga) {
+    issue(st.s[3], mt_begin, 3);
+    barrier_after_vmcnt<3 * NL + NS>();
+    e.read_all(0, st.s[0]);
+    for (int mt = mt_begin; mt < mt_end; ++mt) {
+      // four K tiles from t; LAST: the last four of the M tile, ending with
+      // its epilogue; AFTER: the first four, after the previous epilogue
+      auto quad = [&](int t, auto last_c, auto after_c) {
+        constexpr bool LAST = decltype(last_c)::value;
+        constexpr bool AFTER = decltype(after_c)::value;
+#define PS_A(J)                                                             \
+        mma_all();                                                          \
+        __builtin_amdgcn_sched_barrier(0);                                  \
+        barrier_after_vmcnt<2 * NL + ((AFTER && J < 2) ? NS : 0)>();        \
+        if constexpr (LAST && J == 3) {                                     \
+          epi(acc, mt * C::BM);                                             \
+          zero_acc(acc);                                                    \
+          __builtin_amdgcn_sched_barrier(0);                                \
+        }                                                                   \
+        e.read_all(0, st.s[(J + 1) & 3]);                                   \
+        issue(st.s[J & 3], mt, t + J + 4);                                  \
+        __builtin_amdgcn_sched_barrier(0);                                  \
+        barrier_after_vmcnt<3 * NL + (((AFTER && J < 2) || (LAST && J == 3)) ? NS : 0)>();
+        PS_A(0) PS_A(1) PS_A(2) PS_A(3)
+#undef PS_A
+      };
+      quad(0, std::false_type{}, std::true_type{});
+      for (int t = 4; t < nk - 4; t += 4) quad(t, std::false_type{}, std::false_type{});
+      quad(nk - 4, std::true_type{}, std::false_type{});
+    }
+  } else {
+    barrier_after_vmcnt<2 * NL + NS>();
+    for (int mt = mt_begin; mt < mt_end; ++mt) {
+      // as for group A; the epilogue comes after the barrier that closes the
+      // last MFMA phase of the M tile
+      auto quad = [&](int t, auto last_c, auto after_c) {
+        constexpr bool LAST = decltype(last_c)::value;
+        constexpr bool AFTER = decltype(after_c)::value;
+#define PS_B(J)                                                             \
+        e.read_all(0, st.s[J & 3]);                                         \
+        issue(st.s[(J + 3) & 3], mt, t + J + 3);                            \
+        __builtin_amdgcn_sched_barrier(0);                                  \
+        barrier_after_vmcnt<2 * NL + ((AFTER && J < 2) ? NS : 0)>();        \
+        mma_all();                                                          \
+        __builtin_amdgcn_sched_barrier(0);                                  \
+        barrier_after_vmcnt<2 * NL + ((AFTER && J < 2) ? NS : 0)>();        \
+        if constexpr (LAST && J == 3) {                                     \
+          epi(acc, mt * C::BM);                                             \
+          zero_acc(acc);                                                    \
+          __builtin_amdgcn_sched_barrier(0);                                \
+        }
+        PS_B(0) PS_B(1) PS_B(2) PS_B(3)
+#undef PS_B
+      };
+      quad(0, std::false_type{}, std::true_type{});
+      for (int t = 4; t < nk - 4; t += 4) quad(t, std::false_type{}, std::false_type{});
+      quad(nk - 4, std::true_type{}, std::false_type{});
+    }
+  }
+  barrier_after_vmcnt<0>();
+}
+
 // bf16 tiles take the DMA pipeline over the four stages: the ping-pong loop
 // when A is K-major, the rolling one when A is M-major (its fragment reads
 // transpose both operands, and the longer memory phase then outlasts the

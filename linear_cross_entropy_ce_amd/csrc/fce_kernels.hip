@@ -138,11 +138,23 @@ __device__ __forceinline__ void store16(__amdgpu_buffer_rsrc_t r, uint32_t off, 
   __builtin_amdgcn_raw_buffer_store_b128(v, r, off, 0, kBufNonTemporal);
 }
 
+// Buffer resource at a wave-uniform base with a record count the caller has
+// already clamped to [0, 2^31 - 1]; every field goes through readfirstlane,
+// so it is legal wherever the compiler keeps the inputs.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc_n(const void* base, uint32_t n) {
+  const uint64_t b = reinterpret_cast<uint64_t>(base);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(b));
+  const uint32_t hi = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(b >> 32));
+  void* bs = reinterpret_cast<void*>((static_cast<uint64_t>(hi) << 32) | lo);
+  return __builtin_amdgcn_make_buffer_rsrc(
+      bs, 0, static_cast<int>(__builtin_amdgcn_readfirstlane(n)), 0x00020000);
+}
+
 // a + b (b wave-uniform) computed where it is used: kept out of loop-invariant
 // hoisting, which would hold one register per use across the whole loop.
 __device__ __forceinline__ uint32_t add_at_use(uint32_t a, uint32_t b) {
   uint32_t r;
-  asm volatile("v_add_u32 %0, %1, %2" : "=v"(r) : "s"(b), "v"(a));
+  asm volatile("v_add_u32 %0, %1, %2" : "=v"(r) : "v"(b), "v"(a));
   return r;
 }
 
@@ -548,7 +560,8 @@ __global__ __launch_bounds__(C::NT) void k_bwd_dz(DzArgs<typename C::Elem> a) {
   }
 }
 
-// dZ as one DMA stream per workgroup (bf16, H % 128 == 0, no filtering):
+// dZ as one DMA stream per workgroup (bf16, H % 128 == 0 and H >= 256, no
+// filtering):
 // one token tile against vocabulary tiles vt_begin .. vt_end-1 of the block,
 // the recompute of each logit tile on the ping-pong stream of gemm_stream_pp
 // and its dZ epilogue in the memory phase of each wave group, so the K
@@ -562,7 +575,8 @@ __global__ __launch_bounds__(C::NT) void k_bwd_dz_stream(DzArgs<bf16> a, int spl
                sp);
   if (*a.flag == 0) return;  // every label of this token block is ignored
   FCE_DMA_STAGES(lds);
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // scalar: staging bases stay scalar
   const int wm = wave / C::WAVES_N, wn = wave % C::WAVES_N;
   const int n0 = tt * C::BN;
   const int vt_begin = static_cast<int>(static_cast<int64_t>(sp) * a.voc_tiles / splits);
@@ -593,6 +607,9 @@ __global__ __launch_bounds__(C::NT) void k_bwd_dz_stream(DzArgs<bf16> a, int spl
   }
   __syncthreads();
   const int rbase = wm * C::WTM + Map::row(lane, 0);
+  // bytes from a wave's strip origin to the end of its WTN token rows
+  const uint32_t strip_bytes = static_cast<uint32_t>(
+      min(static_cast<int64_t>(C::WTN) * a.ldz * 2, static_cast<int64_t>(0x7fffffff)));
   // Store staging: one 16-token column of a wave's WTM-row strip at a time
   // passes through LDS, so that each store writes 16-byte pieces of whole
   // token-row segments (2 WTM bytes) instead of 8-byte pieces scattered
@@ -640,9 +657,8 @@ __global__ __launch_bounds__(C::NT) void k_bwd_dz_stream(DzArgs<bf16> a, int spl
       // the strip's 16 token rows, 64 / kPieces of them per store, through a
       // buffer resource based at this wave's strip of the tile, with 32-bit
       // lane offsets
-      const __amdgpu_buffer_rsrc_t rs = make_rsrc(
-          a.dz + static_cast<int64_t>(n0 + wn * C::WTN) * a.ldz + m0 + wm * C::WTM,
-          static_cast<int64_t>(C::WTN) * a.ldz * 2);
+      const __amdgpu_buffer_rsrc_t rs = make_rsrc_n(
+          a.dz + static_cast<int64_t>(n0 + wn * C::WTN) * a.ldz + m0 + wm * C::WTM, strip_bytes);
       const uint32_t ldz_b = static_cast<uint32_t>(a.ldz) * 2u;
       const uint32_t voff = static_cast<uint32_t>(lane / kPieces) * ldz_b + 16u * (lane % kPieces);
       constexpr int NJ = C::NB * kPieces / 64;
@@ -661,13 +677,16 @@ __global__ __launch_bounds__(C::NT) void k_bwd_dz_stream(DzArgs<bf16> a, int spl
       __builtin_amdgcn_sched_barrier(0);
     }
   };
-  gemm_stream_pp<C>(A, B, vt_begin, vt_end, n0, a.H, lds, tid,
-                    [&](const Acc<C>& acc, int m0) {
-                      if (m0 + C::BM <= a.nvoc)
-                        epilogue(std::true_type{}, acc, m0);
-                      else
-                        epilogue(std::false_type{}, acc, m0);
-                    });
+  // the epilogue's stores per wave, every one unconditional (masked columns
+  // store zeros)
+  constexpr int kStores = C::FN * (C::NB * kPieces / 64);
+  gemm_stream_pp_st<C, kStores>(A, B, vt_begin, vt_end, n0, a.H, lds, tid,
+                             [&](const Acc<C>& acc, int m0) {
+                               if (m0 + C::BM <= a.nvoc)
+                                 epilogue(std::true_type{}, acc, m0);
+                               else
+                                 epilogue(std::false_type{}, acc, m0);
+                             });
 }
 
 // ---------------------------------------------------- backward: dW and dX
@@ -1362,7 +1381,7 @@ hipError_t run_backward(const Plan& p, const T* X, const T* W, const int32_t* la
             k_bwd_dz<C, true, true><<<voc_tiles * tok_tiles, C::NT, 0, st>>>(da);
           else
             k_bwd_dz<C, false, true><<<voc_tiles * tok_tiles, C::NT, 0, st>>>(da);
-        } else if (H % 128 == 0) {
+        } else if (H % 128 == 0 && H >= 256) {
           // about one workgroup per CU, each streaming a run of vocabulary tiles
           const int splits = std::max(1, std::min(voc_tiles, kNumCUs / tok_tiles));
           da.group_m = std::max(1, 32 / splits);
