@@ -31,43 +31,65 @@ using fce::Plan;
 using fce::Schedule;
 
 // --------------------------------------------------------------- timing
-struct EventPair {
-  hipEvent_t start = nullptr, stop = nullptr;
-};
-
+// Kernel durations from HIP events on the caller's stream.  Within one call
+// the timed launches follow each other with nothing between them, so a
+// launch's start is the previous launch's stop: one event per boundary
+// (each record on the stream costs a few microseconds of its time).  Every
+// entry point calls new_call() first, so work the caller enqueues between
+// calls never falls inside a timed interval.
 struct Record {
   std::string name;
   double flops;
-  int pair;
+  int start, stop;  // event indices
 };
 
 class EventTimer final : public fce::KernelTimer {
  public:
   bool enabled = false;
-  std::vector<EventPair> pool;
+  std::vector<hipEvent_t> pool;
+  int used = 0;            // events recorded since the last read
   std::vector<Record> records;
-  int open = -1;
+  int open = -1;           // record waiting for its stop event
+  int last_stop = -1;      // stop event of the previous launch of this call
+  hipStream_t last_stream = nullptr;
   bool failed = false;
 
-  void begin(const char* name, double flops, hipStream_t st) override {
-    if (!enabled) return;
-    const int idx = static_cast<int>(records.size());
-    if (idx >= static_cast<int>(pool.size())) {
-      EventPair e;
-      if (hipEventCreate(&e.start) != hipSuccess || hipEventCreate(&e.stop) != hipSuccess) {
+  void new_call() { last_stop = -1; }
+  int next_event() {
+    if (used >= static_cast<int>(pool.size())) {
+      hipEvent_t e;
+      if (hipEventCreate(&e) != hipSuccess) {
         failed = true;
-        return;
+        return -1;
       }
       pool.push_back(e);
     }
-    records.push_back(Record{name, flops, idx});
-    open = idx;
-    if (hipEventRecord(pool[idx].start, st) != hipSuccess) failed = true;
+    return used++;
+  }
+  void begin(const char* name, double flops, hipStream_t st) override {
+    if (!enabled) return;
+    int start = (last_stop >= 0 && st == last_stream) ? last_stop : -1;
+    if (start < 0) {
+      start = next_event();
+      if (start < 0) return;
+      if (hipEventRecord(pool[start], st) != hipSuccess) failed = true;
+    }
+    records.push_back(Record{name, flops, start, -1});
+    open = static_cast<int>(records.size()) - 1;
   }
   void end(hipStream_t st) override {
     if (!enabled || open < 0) return;
-    if (hipEventRecord(pool[open].stop, st) != hipSuccess) failed = true;
+    const int stop = next_event();
+    if (stop < 0) {
+      records.pop_back();
+      open = -1;
+      return;
+    }
+    if (hipEventRecord(pool[stop], st) != hipSuccess) failed = true;
+    records[open].stop = stop;
     open = -1;
+    last_stop = stop;
+    last_stream = st;
   }
 };
 
@@ -82,8 +104,12 @@ NullTimer g_null_timer;
 std::mutex g_arch_mu;
 int g_arch_ok[64] = {0};  // 0 unknown, 1 gfx950, -1 other
 
+// The timer for one entry-point call (each call starts its own chain of
+// boundary events).
 fce::KernelTimer* timer() {
-  return g_timer.enabled ? static_cast<fce::KernelTimer*>(&g_timer) : &g_null_timer;
+  if (!g_timer.enabled) return &g_null_timer;
+  g_timer.new_call();
+  return &g_timer;
 }
 
 fce_status check_device() {
@@ -442,10 +468,9 @@ fce_status fce_timing_read(fce_kernel_timing* out, int cap, int* count) {
   std::vector<fce_kernel_timing> agg;
   bool failed = g_timer.failed;
   for (const Record& r : g_timer.records) {
-    const EventPair& e = g_timer.pool[r.pair];
     float ms = 0.0f;
-    if (hipEventSynchronize(e.stop) != hipSuccess ||
-        hipEventElapsedTime(&ms, e.start, e.stop) != hipSuccess) {
+    if (r.stop < 0 || hipEventSynchronize(g_timer.pool[r.stop]) != hipSuccess ||
+        hipEventElapsedTime(&ms, g_timer.pool[r.start], g_timer.pool[r.stop]) != hipSuccess) {
       failed = true;
       continue;
     }
@@ -464,7 +489,9 @@ fce_status fce_timing_read(fce_kernel_timing* out, int cap, int* count) {
     slot->flops += r.flops;
   }
   g_timer.records.clear();
+  g_timer.used = 0;
   g_timer.open = -1;
+  g_timer.last_stop = -1;
   g_timer.failed = false;
   const int n = static_cast<int>(agg.size());
   for (int i = 0; i < n && i < cap; ++i) out[i] = agg[i];
