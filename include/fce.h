@@ -268,9 +268,13 @@ const char* fce_status_string(fce_status status);
 const char* fce_last_hip_error(void);
 
 /* Per-kernel timing.  While enabled, every kernel the library launches is
- * bracketed by HIP events on the caller's stream.  fce_timing_read
- * synchronises on the recorded events, fills up to `cap` entries and resets
- * the counters.  Not thread-safe: meant for one benchmarking thread. */
+ * bracketed by HIP events on the caller's stream; within one call,
+ * consecutive kernels share the event between them (one event per kernel
+ * boundary), and each call starts with an event of its own, so work the
+ * caller enqueues between calls is never counted.  The events cost the
+ * stream a few microseconds each.  fce_timing_read synchronises on the
+ * recorded events, fills up to `cap` entries and resets the counters.  Not
+ * thread-safe: meant for one benchmarking thread. */
 typedef struct {
   char name[32];        /* kernel family: "fwd_lse", "bwd_dz", "bwd_dw", "bwd_dx", ... */
   int64_t launches;     /* launches recorded                                      */

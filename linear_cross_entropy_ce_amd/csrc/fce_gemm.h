@@ -987,11 +987,12 @@ __device__ __forceinline__ void gemm_stream_pp(const Opnd<bf16>& A, const Opnd<b
 // gemm_stream_pp for an epilogue that stores: epi issues at least NS
 // vector-memory instructions per wave (its stores, all of them
 // unconditional).  gfx950 retires vector loads and stores in issue order
-// against vmcnt, so a wait that aims at a DMA issued before an epilogue's
-// stores must count them as outstanding, or it holds the wave until the
-// newer prefetches and the stores have landed.  After an epilogue that is
-// the last wait of group A's epilogue quad and the first four waits of the
-// next quad of either group.  So that the first M tile runs the same code,
+// against vmcnt, so a wait for a DMA issued before an epilogue's stores may
+// leave those stores outstanding: its count includes them (NS more), where
+// a count of DMA issues alone would hold the wave until the newer prefetches
+// and the stores had landed.  After an epilogue that is the last wait of
+// group A's epilogue quad and the first four waits of the next quad of
+// either group.  So that the first M tile runs the same code,
 // each wave first issues NS stores that the hardware drops (a buffer
 // resource of zero bytes) where an epilogue's stores would sit, and the
 // prologue waits count them too.  Needs K % 128 == 0 and K >= 256 (two quads

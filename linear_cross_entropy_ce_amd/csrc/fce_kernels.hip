@@ -158,11 +158,11 @@ __device__ __forceinline__ uint32_t add_at_use(uint32_t a, uint32_t b) {
   return r;
 }
 
-// Waits until this wave's LDS reads have returned their data, as a compiler
-// memory barrier too.  Used where a staging region is read back in 16-byte
-// pieces and then rewritten: without the wait, writes issued right after
-// the reads have been seen to overwrite words those reads had not yet
-// returned.
+// Waits until this wave's LDS reads have returned their data, and keeps the
+// compiler from moving memory operations across (a staging region is
+// written through float or bf16 pointers and read back through 16-byte
+// vectors, types that alias analysis would let it reorder).  Used before a
+// staging region is rewritten.
 __device__ __forceinline__ void lds_reads_done() {
   asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
 }
@@ -561,13 +561,13 @@ __global__ __launch_bounds__(C::NT) void k_bwd_dz(DzArgs<typename C::Elem> a) {
 }
 
 // dZ as one DMA stream per workgroup (bf16, H % 128 == 0 and H >= 256, no
-// filtering):
-// one token tile against vocabulary tiles vt_begin .. vt_end-1 of the block,
-// the recompute of each logit tile on the ping-pong stream of gemm_stream_pp
-// and its dZ epilogue in the memory phase of each wave group, so the K
-// pipeline stays full across vocabulary tiles and one group's epilogue runs
-// beside the other group's MFMAs.  Same dZ bits as k_bwd_dz: the per-token
-// factors are computed once, before the stream, with the same expressions.
+// filtering): one token tile against vocabulary tiles vt_begin .. vt_end-1
+// of the block, the recompute of each logit tile on the ping-pong stream of
+// gemm_stream_pp_st and its dZ epilogue in the memory phase of each wave
+// group, so the K pipeline stays full across vocabulary tiles and one
+// group's epilogue runs beside the other group's MFMAs.  Same dZ bits as
+// k_bwd_dz: the per-token factors are computed once, before the stream,
+// with the same expressions.
 template <class C>
 __global__ __launch_bounds__(C::NT) void k_bwd_dz_stream(DzArgs<bf16> a, int splits) {
   int tt, sp;
