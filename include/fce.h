@@ -91,7 +91,9 @@ typedef enum { FCE_MEAN = 0, FCE_SUM = 1, FCE_NONE = 2 } fce_reduction;
 typedef enum { FCE_SCHED_AUTO = 0, FCE_SCHED_TOKEN = 1, FCE_SCHED_VOCAB = 2 } fce_schedule;
 /* How the backward gets its logits (fce_options.variant).
  * FCE_VARIANT_RECOMPUTE: rebuild each logit block from X and W (8NVH FLOPs
- *   per forward + backward; lesson 27, "Trick 2").
+ *   per forward + backward; lesson 27, "Trick 2").  With FCE_BF16 the
+ *   workspace also holds X^T, H x (N rounded up to 256) bf16, written once
+ *   per backward for the dW products.
  * FCE_VARIANT_STORE_LOGITS: fce_fused_fwd_bwd_ex only.  The forward keeps each
  *   chunk's logits, [C][V rounded up to the tile] in the dtype of X, in the
  *   workspace, and the backward overwrites them in place with dZ (6NVH FLOPs;

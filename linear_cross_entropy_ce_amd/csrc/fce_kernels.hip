@@ -781,7 +781,103 @@ __device__ __forceinline__ void store_grad_tile_staged(const Acc<C>& acc, float 
   }
 }
 
-template <class C, bool A_KMAJOR, bool FILTER>
+// Xt[h][n] = X[n][h] for n < N, 0 for N <= n < ldt: X^T for the dW product
+// as (dW)^T = X^T dZ, whose K-major A operand it is.  64 x 64 tiles through
+// LDS; 16-byte loads along h and 16-byte stores along n.
+__global__ __launch_bounds__(256) void k_transpose_x(const bf16* __restrict__ X, int N, int H,
+                                                     bf16* __restrict__ Xt, int64_t ldt) {
+  __shared__ uint16_t t[64][64 + 2];
+  const int n0 = blockIdx.x * 64, h0 = blockIdx.y * 64;
+  const int tid = threadIdx.x;
+  // load: 64 rows (n) x 8 vectors of 8 (h); thread -> (row, vector)
+#pragma unroll
+  for (int r = 0; r < 2; ++r) {
+    const int i = tid + 256 * r;
+    const int n = n0 + i / 8, hv = 8 * (i % 8);
+    u32x4 v = {0u, 0u, 0u, 0u};
+    if (n < N && h0 + hv < H) v = *reinterpret_cast<const u32x4*>(X + static_cast<int64_t>(n) * H + h0 + hv);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      t[i / 8][hv + 2 * j] = static_cast<uint16_t>(v[j] & 0xffffu);
+      t[i / 8][hv + 2 * j + 1] = static_cast<uint16_t>(v[j] >> 16);
+    }
+  }
+  __syncthreads();
+  // store: 64 rows (h) x 8 vectors of 8 (n)
+#pragma unroll
+  for (int r = 0; r < 2; ++r) {
+    const int i = tid + 256 * r;
+    const int h = h0 + i / 8, nv = 8 * (i % 8);
+    if (h >= H || n0 + nv >= ldt) continue;
+    u32x4 v;
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      v[j] = static_cast<uint32_t>(t[nv + 2 * j][i / 8]) |
+             (static_cast<uint32_t>(t[nv + 2 * j + 1][i / 8]) << 16);
+    *reinterpret_cast<u32x4*>(Xt + static_cast<int64_t>(h) * ldt + n0 + nv) = v;
+  }
+}
+
+// The transposed counterpart of store_grad_tile_staged, for a tile computed
+// as (out)^T: the tile's M runs along the columns of out and its N along the
+// rows, out element (n, m) at tile + n ldo + m.  A lane holds 4 consecutive m
+// of one n, so each wave stages one 16-row block of n (its 16 x WTM floats)
+// at a time with 16-byte LDS writes, then moves whole row segments of WTM
+// floats with 16-byte loads and stores.  Same arithmetic, in the same order:
+// out = old + s acc, or s acc.
+template <class C>
+__device__ __forceinline__ void store_grad_tile_staged_t(const Acc<C>& acc, float s, float* tile,
+                                                         int64_t ldo, bool accumulate,
+                                                         const DmaStages& st, int wave, int lane) {
+  typedef AccMap<C> Map;
+  constexpr int kRowB = 4 * C::WTM, kPitch = kRowB + 16, kPieces = kRowB / 16;
+  constexpr int kRowsPer = 64 / kPieces;  // rows per 16-byte instruction
+  constexpr int NI = C::NB / kRowsPer;
+  static_assert(C::MB == 16 && C::NB == 16 && Map::NGRP == 1 && 64 % kPieces == 0 &&
+                    2 * C::NB * kPitch <= 32768 && C::NT / 64 <= 8,
+                "staging geometry: two waves per 32 KiB stage");
+  const int wm = wave / C::WAVES_N, wn = wave % C::WAVES_N;
+  const int w2 = wave >> 1;  // (constant indices: the stage table is not an array in memory)
+  char* const reg = (w2 == 0 ? st.s[0] : w2 == 1 ? st.s[1] : w2 == 2 ? st.s[2] : st.s[3]) +
+                    (wave & 1) * (C::NB * kPitch);
+  gchar* const sb = wave_uniform(tile + static_cast<int64_t>(wn * C::WTN) * ldo + wm * C::WTM);
+  const uint32_t ldo_b = static_cast<uint32_t>(ldo) * 4u;
+  const uint32_t voff = static_cast<uint32_t>(lane / kPieces) * ldo_b + 16u * (lane % kPieces);
+#pragma unroll
+  for (int fn = 0; fn < C::FN; ++fn) {
+    // element (fm, fn, q): m = fm MB + row(lane, 0) + q, n = fn NB + col(lane)
+#pragma unroll
+    for (int fm = 0; fm < C::FM; ++fm) {
+      const floatx4 v = {s * acc.v[fm][fn][0], s * acc.v[fm][fn][1], s * acc.v[fm][fn][2],
+                         s * acc.v[fm][fn][3]};
+      *reinterpret_cast<floatx4*>(reg + Map::col(lane) * kPitch +
+                                  4 * (fm * C::MB + Map::row(lane, 0))) = v;
+    }
+    floatx4 v[NI], old[NI];
+#pragma unroll
+    for (int t = 0; t < NI; ++t) {
+      const uint32_t soff = static_cast<uint32_t>(fn * C::NB + t * kRowsPer) * ldo_b;
+      old[t] = accumulate
+                   ? *reinterpret_cast<const __attribute__((address_space(1))) floatx4*>(sb + voff + soff)
+                   : floatx4{0.0f, 0.0f, 0.0f, 0.0f};
+    }
+#pragma unroll
+    for (int t = 0; t < NI; ++t)
+      v[t] = *reinterpret_cast<const floatx4*>(
+          reg + (t * kRowsPer + lane / kPieces) * kPitch + 16 * (lane % kPieces));
+    lds_reads_done();  // before the next block's writes to the region
+#pragma unroll
+    for (int t = 0; t < NI; ++t) {
+      const uint32_t soff = static_cast<uint32_t>(fn * C::NB + t * kRowsPer) * ldo_b;
+      const floatx4 o = accumulate ? old[t] + v[t] : v[t];
+      store16(sb, voff + soff, __builtin_bit_cast(u32x4, o));
+    }
+  }
+}
+
+// TRANS: the tile is (out)^T, out element (n, m) at out + n ldo + m (the dW
+// product computed as X^T dZ).
+template <class C, bool A_KMAJOR, bool FILTER, bool TRANS = false>
 __global__ __launch_bounds__(C::NT) void k_bwd_grad(GradArgs<typename C::Elem> a) {
   typedef typename C::Elem T;
   FCE_DMA_STAGES(lds);
@@ -840,10 +936,14 @@ __global__ __launch_bounds__(C::NT) void k_bwd_grad(GradArgs<typename C::Elem> a
   const int rbase = wm * C::WTM;
   const int cbase = wn * C::WTN + Map::col(lane);
   const bool full = m0 + C::BM <= a.m_valid && n0 + C::BN <= a.n_valid;
-  float* tile = out + static_cast<int64_t>(m0) * a.ldo + n0;
+  float* tile = TRANS ? out + static_cast<int64_t>(n0) * a.ldo + m0
+                      : out + static_cast<int64_t>(m0) * a.ldo + n0;
   if constexpr (sizeof(T) == 2) {
     if (full) {
-      store_grad_tile_staged<C>(acc, s, tile, a.ldo, a.accumulate != 0, lds, wave, lane);
+      if constexpr (TRANS)
+        store_grad_tile_staged_t<C>(acc, s, tile, a.ldo, a.accumulate != 0, lds, wave, lane);
+      else
+        store_grad_tile_staged<C>(acc, s, tile, a.ldo, a.accumulate != 0, lds, wave, lane);
       return;
     }
   }
@@ -862,7 +962,8 @@ __global__ __launch_bounds__(C::NT) void k_bwd_grad(GradArgs<typename C::Elem> a
           ok[j][fn][i] = full || (m0 + r < a.m_valid && n0 + c < a.n_valid);
           old[j][fn][i] = 0.0f;
           if (a.accumulate && ok[j][fn][i])
-            old[j][fn][i] = tile[static_cast<int64_t>(r) * a.ldo + c];
+            old[j][fn][i] = TRANS ? tile[static_cast<int64_t>(c) * a.ldo + r]
+                                  : tile[static_cast<int64_t>(r) * a.ldo + c];
         }
 #pragma unroll
     for (int j = 0; j < SLAB; ++j)
@@ -873,7 +974,8 @@ __global__ __launch_bounds__(C::NT) void k_bwd_grad(GradArgs<typename C::Elem> a
           const int r = rbase + (f0 + j) * C::MB + Map::row(lane, i >> 2) + (i & 3);
           const int c = cbase + fn * C::NB;
           if (ok[j][fn][i])
-            tile[static_cast<int64_t>(r) * a.ldo + c] = old[j][fn][i] + s * acc.v[f0 + j][fn][i];
+            tile[TRANS ? static_cast<int64_t>(c) * a.ldo + r : static_cast<int64_t>(r) * a.ldo + c] =
+                old[j][fn][i] + s * acc.v[f0 + j][fn][i];
         }
   }
 }
@@ -1237,8 +1339,9 @@ template <typename T>
 hipError_t grad_products(const Plan& p, const T* X, const T* W, const T* dz, int64_t ldz,
                          int64_t tok0, int ntok, int64_t voc0, int nvoc, bool acc_dw, bool acc_dx,
                          const Ctrl* ctrl, const int32_t* flag, float* dX, float* dW,
-                         float* dxpart, const FilterLists* fl, hipStream_t st,
-                         KernelTimer* timer, const char* name_dw, const char* name_dx) {
+                         float* dxpart, const FilterLists* fl, const T* Xt, int64_t ldxt,
+                         hipStream_t st, KernelTimer* timer, const char* name_dw,
+                         const char* name_dx) {
   typedef typename ShapeOf<T>::C C;
   const int64_t H = p.H;
   const int h_tiles = cdiv_i(H, C::BN);
@@ -1268,10 +1371,28 @@ hipError_t grad_products(const Plan& p, const T* X, const T* W, const T* dz, int
   gw.kcount = fl ? fl->colcnt : nullptr;
   gw.list_ld = fl ? fl->tt : 0;
   gw.korder = fl ? fl->colorder : nullptr;
+  // With X^T at hand (bf16, unfiltered): (dW)^T = X^T dZ, whose A operand
+  // (X^T, rows h) is K-major, so the product takes the ping-pong K loop of
+  // the dX product; the tile is written transposed.  K runs over the token
+  // tiles: X^T is zero past N and dZ^T rows past the block's tokens load as
+  // zero, so the extra columns add nothing.
+  GradArgs<T> gt = gw;
+  if (Xt != nullptr && fl == nullptr) {
+    gt.A = Opnd<T>{Xt + tok0, ldxt, static_cast<int>(H), tok_tiles * C::BN};  // (h, t) at Xt[h*ldxt + t]
+    gt.B = Opnd<T>{dz, ldz, nvoc, ntok};                                      // (v, t) at dz[t*ldz + v]
+    gt.K = tok_tiles * C::BN;
+    gt.m_valid = static_cast<int>(H);
+    gt.n_valid = nvoc;
+    gt.tm_tiles = h_tiles;
+    gt.tn_tiles = voc_tiles;
+    gt.ksplit = gt.K;
+  }
   timer->begin(name_dw, blk_flops, st);
   if constexpr (sizeof(T) == 2) {
     if (fl)
       k_bwd_grad<C, false, true><<<voc_tiles * h_tiles, C::NT, 0, st>>>(gw);
+    else if (Xt != nullptr)
+      k_bwd_grad<C, true, false, true><<<voc_tiles * h_tiles, C::NT, 0, st>>>(gt);
     else
       k_bwd_grad<C, false, false><<<voc_tiles * h_tiles, C::NT, 0, st>>>(gw);
   } else {
@@ -1360,6 +1481,20 @@ hipError_t run_backward(const Plan& p, const T* X, const T* W, const int32_t* la
     timer->end(st);
     return hipSuccess;
   }
+  // X^T for the dW products (when the plan has room for it)
+  const T* xt = nullptr;
+  if constexpr (sizeof(T) == 2) {
+    if (p.xt_bytes > 0 && !filt) {
+      T* xtw = reinterpret_cast<T*>(ws + p.off_xt);
+      timer->begin("x_transpose", 0.0, st);
+      k_transpose_x<<<dim3(static_cast<unsigned>(cdiv_i(p.ldxt, 64)),
+                           static_cast<unsigned>(cdiv_i(H, 64))),
+                      256, 0, st>>>(X, static_cast<int>(N), static_cast<int>(H), xtw, p.ldxt);
+      FCE_CHECK_LAUNCH();
+      timer->end(st);
+      xt = xtw;
+    }
+  }
   for (int64_t ia = 0; ia < p.a; ++ia) {
     const int64_t tok0 = ia * p.CN;
     const int ntok = static_cast<int>(std::min(p.CN, N - tok0));
@@ -1423,7 +1558,8 @@ hipError_t run_backward(const Plan& p, const T* X, const T* W, const int32_t* la
       }
       const hipError_t e = grad_products<T>(p, X, W, dz, p.ldz, tok0, ntok, voc0, nvoc, ia > 0,
                                             ib > 0, ctrl, flags + ia, dX, dW, dxpart,
-                                            filt ? &fl : nullptr, st, timer, "bwd_dw", "bwd_dx");
+                                            filt ? &fl : nullptr, xt, p.ldxt, st, timer, "bwd_dw",
+                                            "bwd_dx");
       if (e != hipSuccess) return e;
     }
   }
@@ -1486,7 +1622,7 @@ hipError_t run_fused_store(const Plan& p, const T* X, const T* W, const int32_t*
     timer->end(st);
     const hipError_t e = grad_products<T>(p, X, W, zs, p.ldz, tok0, ntok, 0, static_cast<int>(V),
                                           ia > 0, false, ctrl, flags + ia, dX, dW, dxpart,
-                                          nullptr, st, timer, "sl_dw", "sl_dx");
+                                          nullptr, nullptr, 0, st, timer, "sl_dw", "sl_dx");
     if (e != hipSuccess) return e;
   }
   if (none) return hipSuccess;

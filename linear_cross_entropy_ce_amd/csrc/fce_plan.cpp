@@ -232,6 +232,19 @@ bool make_plan(int64_t N, int64_t H, int64_t V, Dtype dtype, int64_t chunk, Sche
                                            static_cast<size_t>(H) * sizeof(float)
                                      : 0;
   off = align_up(off + p.dxpart_bytes);
+  // X^T for the dW product of the bf16 recompute path: rows of the token
+  // extent rounded up to a tile, so that the product's K loop runs whole
+  // tiles over zeros past N; 256 rows of it stay under 2 GiB (32-bit tile
+  // offsets), else dW keeps the untransposed product
+  if (dtype == Dtype::BF16 && variant == Variant::Recompute && N > 0) {
+    const int64_t ldxt = round_up(N, G);
+    if (ldxt < row_cap) {
+      p.ldxt = ldxt;
+      p.off_xt = off;
+      p.xt_bytes = static_cast<size_t>(H) * static_cast<size_t>(ldxt) * 2u;
+      off = align_up(off + p.xt_bytes);
+    }
+  }
   if (variant == Variant::Filtered) {
     p.filt_tt = cdiv(std::min(p.CN, std::max<int64_t>(N, 1)), BN);
     p.filt_vt = cdiv(std::min(p.CV, V), BM);

@@ -63,9 +63,14 @@ def _flags(name: str) -> list[bool]:
 def kernel_key(name: str) -> str | None:
     """Map a (mangled or demangled) kernel name to the library's timer name."""
     if "k_bwd_grad" in name:
-        # first flag A_KMAJOR: false for dW (A = dZ^T), true for dX (A = dZ)
+        # flags A_KMAJOR, FILTER, TRANS: dX has a K-major A (dZ); dW has an
+        # M-major one (dZ^T), or is the transposed product X^T dZ (TRANS)
         f = _flags(name)
-        return None if not f else ("bwd_dx" if f[0] else "bwd_dw")
+        if not f:
+            return None
+        return "bwd_dw" if (len(f) > 2 and f[2]) or not f[0] else "bwd_dx"
+    if "k_transpose_x" in name:
+        return "x_transpose"
     if "k_fwd_lse" in name:
         # flags SMOOTH, STORE: the storing forward is the store-logits variant's
         f = _flags(name)
