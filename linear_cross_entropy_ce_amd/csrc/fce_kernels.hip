@@ -1452,6 +1452,27 @@ hipError_t grad_products(const Plan& p, const T* X, const T* W, const T* dz, int
   return hipSuccess;
 }
 
+// Writes X^T into the workspace for the dW products and points *xt at it,
+// when the plan has room for it (bf16); *xt = nullptr otherwise.
+template <typename T>
+hipError_t transpose_x(const Plan& p, const T* X, char* ws, hipStream_t st, KernelTimer* timer,
+                       const T** xt) {
+  *xt = nullptr;
+  if constexpr (sizeof(T) == 2) {
+    if (p.xt_bytes > 0) {
+      T* out = reinterpret_cast<T*>(ws + p.off_xt);
+      timer->begin("x_transpose", 0.0, st);
+      k_transpose_x<<<dim3(static_cast<unsigned>(cdiv_i(p.ldxt, 64)),
+                           static_cast<unsigned>(cdiv_i(p.H, 64))),
+                      256, 0, st>>>(X, static_cast<int>(p.N), static_cast<int>(p.H), out, p.ldxt);
+      FCE_CHECK_LAUNCH();
+      timer->end(st);
+      *xt = out;
+    }
+  }
+  return hipSuccess;
+}
+
 template <typename T>
 hipError_t run_backward(const Plan& p, const T* X, const T* W, const int32_t* labels,
                         const LossOpts& o, const float* lse, const float* grad_tok, float* dX,
@@ -1483,17 +1504,9 @@ hipError_t run_backward(const Plan& p, const T* X, const T* W, const int32_t* la
   }
   // X^T for the dW products (when the plan has room for it)
   const T* xt = nullptr;
-  if constexpr (sizeof(T) == 2) {
-    if (p.xt_bytes > 0 && !filt) {
-      T* xtw = reinterpret_cast<T*>(ws + p.off_xt);
-      timer->begin("x_transpose", 0.0, st);
-      k_transpose_x<<<dim3(static_cast<unsigned>(cdiv_i(p.ldxt, 64)),
-                           static_cast<unsigned>(cdiv_i(H, 64))),
-                      256, 0, st>>>(X, static_cast<int>(N), static_cast<int>(H), xtw, p.ldxt);
-      FCE_CHECK_LAUNCH();
-      timer->end(st);
-      xt = xtw;
-    }
+  if (!filt) {
+    const hipError_t e = transpose_x(p, X, ws, st, timer, &xt);
+    if (e != hipSuccess) return e;
   }
   for (int64_t ia = 0; ia < p.a; ++ia) {
     const int64_t tok0 = ia * p.CN;
@@ -1592,6 +1605,11 @@ hipError_t run_fused_store(const Plan& p, const T* X, const T* W, const int32_t*
     FCE_CHECK_LAUNCH();
     timer->end(st);
   }
+  const T* xt = nullptr;
+  if (N > 0) {
+    const hipError_t e = transpose_x(p, X, ws, st, timer, &xt);
+    if (e != hipSuccess) return e;
+  }
   for (int64_t ia = 0; ia < p.a; ++ia) {
     const int64_t tok0 = ia * p.CN;  // a multiple of kLossBlock
     const int ntok = static_cast<int>(std::min(p.CN, N - tok0));
@@ -1622,7 +1640,7 @@ hipError_t run_fused_store(const Plan& p, const T* X, const T* W, const int32_t*
     timer->end(st);
     const hipError_t e = grad_products<T>(p, X, W, zs, p.ldz, tok0, ntok, 0, static_cast<int>(V),
                                           ia > 0, false, ctrl, flags + ia, dX, dW, dxpart,
-                                          nullptr, nullptr, 0, st, timer, "sl_dw", "sl_dx");
+                                          nullptr, xt, p.ldxt, st, timer, "sl_dw", "sl_dx");
     if (e != hipSuccess) return e;
   }
   if (none) return hipSuccess;

@@ -48,7 +48,8 @@ struct Plan {
          off_roworder = 0, off_colorder = 0;
   size_t scratch_bytes = 0, partial_bytes = 0, dxpart_bytes = 0;
   // X transposed ([H][ldxt] in the input dtype, zero past N), for the dW
-  // product as (dW)^T = X^T dZ: bf16 recompute only, 0 bytes otherwise
+  // product as (dW)^T = X^T dZ: bf16 recompute and store-logits only, 0 bytes
+  // otherwise
   int64_t ldxt = 0;
   size_t off_xt = 0, xt_bytes = 0;
   int64_t n_loss_blocks = 0;

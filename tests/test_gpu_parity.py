@@ -151,6 +151,22 @@ def test_one_token_block_all_ignored(H, block):
     check_against_oracle(inp, got)
 
 
+@pytest.mark.parametrize("H,variant", [(384, "recompute"), (320, "store_logits")])
+def test_transposed_dw_over_accumulating_token_blocks(H, variant):
+    # token blocks of 8192 take dW as X^T dZ: three blocks (8192, 8192, 300)
+    # accumulate into dW, with a partial H tile and a partial vocabulary tile
+    wl = wk.custom(2 * 8192 + 300, H, 2000, "bf16", ignore_frac=0.1, seed=61)
+    inp = wk.draw(wl)
+    if variant == "recompute":
+        got = run(inp, chunk=8192, schedule="token")
+    else:
+        got = run_ex(inp, split=False, chunk=8192, variant="store_logits")
+        # the fused store-logits call returns the loss; its LSE stays in the workspace
+        got["loss"] = float(got["loss"][0])
+        got["lse"] = np.empty(0)
+    check_against_oracle(inp, got)
+
+
 def test_empty_batch():
     wl = wk.custom(0, 64, 700, "bf16", seed=55)
     inp = wk.draw(wl)
