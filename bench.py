@@ -13,7 +13,7 @@ torch step that materialises the logits.
 Prints ONE JSON line on stdout; progress goes to stderr.
 
     python bench.py [--gpus 1] [--steps 20] [--warmup 3] [--workload 3]
-                    [--chunk 1024] [--schedule auto] [--cpu-sample-tokens 4096]
+                    [--chunk 1024] [--schedule auto] [--cpu-sample-tokens 0]
                     [--sweep-chunks 256,512] [--no-naive] [--no-cpu-baseline]
 """
 from __future__ import annotations
@@ -52,9 +52,28 @@ def read_traffic(kernel: str, workload: str, launches_per_step: float):
     return rec.get("hbm_bytes_per_launch")
 
 
+# fp64 FLOPs the CPU baseline may execute by default (about 30 s on 16 host
+# cores): the whole 8192 x 4096 x 128256 workload (25.8 TFLOP) fits, larger
+# workloads take their first tokens
+CPU_BUDGET_FLOPS = 30e12
+
+
+def cpu_tokens(wl, requested: int) -> int:
+    """Tokens of the CPU baseline: ``requested`` if positive, else the whole
+    workload when its 6NVH fp64 FLOPs fit CPU_BUDGET_FLOPS, else the most
+    whole 256-token tiles that do."""
+    if requested > 0:
+        return min(requested, wl.N)
+    per_token = 6.0 * wl.V * wl.H
+    if per_token * wl.N <= CPU_BUDGET_FLOPS:
+        return wl.N
+    return max(256, int(CPU_BUDGET_FLOPS / per_token) // 256 * 256)
+
+
 def cpu_baseline(wl, inp, n_tokens: int):
     """The fp64 oracle as it stands, on the first n_tokens rows of the same
-    workload (full vocabulary and hidden size)."""
+    workload (full vocabulary and hidden size; all rows: one full oracle
+    call)."""
     import oracle.fce_oracle as orc
     import workloads as wk
 
@@ -76,9 +95,12 @@ def cpu_baseline(wl, inp, n_tokens: int):
     t0 = time.perf_counter()
     orc.linear_cross_entropy(X, inp.W, y, wk.IGNORE_INDEX, wl.label_smoothing, "mean")
     dt = time.perf_counter() - t0
+    what = (f"one full oracle call on all {n} tokens of {wl.name}" if n == wl.N else
+            f"first {n} of {wl.N} tokens of {wl.name}")
     return {"value": n / dt, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"first {n} of {wl.N} tokens of {wl.name} (full V={wl.V}, H={wl.H}); "
-                      f"fp64 numpy on {model}, {6 * n * wl.V * wl.H / 1e12:.2f} TFLOP executed in {dt:.1f} s"}
+            "seconds": round(dt, 2), "cpu_model": model,
+            "sample": f"{what} (full V={wl.V}, H={wl.H}): loss, dX and dW in fp64 numpy on "
+                      f"{model}, {6 * n * wl.V * wl.H / 1e12:.2f} TFLOP executed in {dt:.1f} s"}
 
 
 def time_steps(torch, fn, steps, stream):
@@ -287,7 +309,9 @@ def main():
     ap.add_argument("--workload", type=int, default=3)
     ap.add_argument("--chunk", type=int, default=1024)
     ap.add_argument("--schedule", default="auto", choices=["auto", "token", "vocab"])
-    ap.add_argument("--cpu-sample-tokens", type=int, default=4096)
+    ap.add_argument("--cpu-sample-tokens", type=int, default=0,
+                    help="tokens of the CPU oracle baseline (0: the whole workload if it fits "
+                         "about 30 s of host time, else the first tokens that do)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--sweep-chunks", default="256,512")
     ap.add_argument("--side-steps", type=int, default=10)
@@ -386,8 +410,9 @@ def main():
 
     cpu = None
     if not args.no_cpu_baseline:
-        log(f"timing the CPU oracle on {args.cpu_sample_tokens} tokens ...")
-        cpu = cpu_baseline(wl, inp, args.cpu_sample_tokens)
+        n_cpu = cpu_tokens(wl, args.cpu_sample_tokens)
+        log(f"timing the CPU oracle on {n_cpu} of {wl.N} tokens ...")
+        cpu = cpu_baseline(wl, inp, n_cpu)
         log(f"  {cpu}")
 
     out = {

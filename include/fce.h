@@ -171,12 +171,34 @@ fce_status fce_backward(const void* X, const void* W, const int32_t* labels, int
                         void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /* Forward then backward with g = 1 in one call; the LSE stays in the
- * workspace.  Bitwise identical to fce_forward followed by fce_backward. */
+ * workspace.  With FCE_BF16, bitwise identical to fce_forward followed by
+ * fce_backward.  With FCE_F32 the backward takes its exponents from the
+ * forward's split row statistics (row max m and log2 of the sum of
+ * exp(z - m), kept in the workspace) as (z - m) log2e - log2 l, exact near
+ * the max at any |LSE|; the split calls pass the LSE as one rounded fp32
+ * value per row instead, which puts a relative error of up to |LSE| 2^-25
+ * on every softmax value of the row, so the two agree to that rounding
+ * ("Cut Cross-Entropy ... Guide", "Numerical Stability and Maximum
+ * Subtraction on Chip": subtract the row maximum before exponentiating). */
 fce_status fce_fused_fwd_bwd(const void* X, const void* W, const int32_t* labels, int64_t N,
                              int64_t H, int64_t V, fce_dtype dtype, int32_t ignore_index,
                              float label_smoothing, fce_reduction reduction, int64_t chunk,
                              fce_schedule schedule, float* loss, float* dX, float* dW,
                              void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* Applies the upstream scalar gradient to gradients computed with g = 1:
+ * dX[i] *= g for i < n_dx and dW[j] *= g for j < n_dw, in place, where g is
+ * the device scalar grad_loss[0] (chain rule of the loss scale; llms.blog,
+ * "Mathematical Mechanics", step 3, with the upstream gradient of an
+ * autograd backward).  For the store-logits variant, whose fused call
+ * computes dX and dW in the forward pass of a training step, before the
+ * upstream gradient exists ("LinkedIn Liger Kernel").  All pointers DEVICE;
+ * dX and dW 16-byte aligned when their count is positive.  Errors:
+ * FCE_ERR_SHAPE for a negative count, FCE_ERR_NULL for grad_loss or a
+ * needed array NULL, FCE_ERR_ALIGN, FCE_ERR_DEVICE; nothing is enqueued
+ * then.  Enqueued on `stream`, no synchronisation. */
+fce_status fce_scale_grads(float* dX, int64_t n_dx, float* dW, int64_t n_dw,
+                           const float* grad_loss, hipStream_t stream);
 
 /* Number of labels outside [0, V) that were not ignore_index in the last
  * call that used this workspace.  Synchronises `stream`. */
@@ -275,8 +297,11 @@ const char* fce_last_hip_error(void);
  * boundary), and each call starts with an event of its own, so work the
  * caller enqueues between calls is never counted.  The events cost the
  * stream a few microseconds each.  fce_timing_read synchronises on the
- * recorded events, fills up to `cap` entries and resets the counters.  Not
- * thread-safe: meant for one benchmarking thread. */
+ * recorded events, fills up to `cap` entries and resets the counters.  The
+ * timer is process-wide and guarded by a mutex: while it is enabled, each
+ * entry point holds that mutex while it enqueues its launches, so calls
+ * from several threads are serialised and their records do not interleave;
+ * while it is disabled no lock is taken. */
 typedef struct {
   char name[32];        /* kernel family: "fwd_lse", "bwd_dz", "bwd_dw", "bwd_dx", ... */
   int64_t launches;     /* launches recorded                                      */

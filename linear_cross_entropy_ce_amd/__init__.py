@@ -39,6 +39,7 @@ from ._binding import (  # noqa: F401
     fce_get_label_errors,
     fce_get_filter_stats,
     fce_plan,
+    fce_scale_grads,
     status_string,
     fce_timing_enable,
     fce_timing_read,
@@ -96,12 +97,14 @@ def _make_function():
             ctx.cfg = (opts, hidden.shape, hidden.dtype, weight.dtype)
             if opts["variant"] == "store_logits":
                 # gradients with an upstream gradient of 1, computed now; the
-                # backward scales them by the scalar it receives
+                # backward has the library scale them by the scalar it
+                # receives (once: they are freed there, as autograd frees
+                # saved buffers after a backward)
                 dX = torch.empty((N, H), dtype=torch.float32, device=X.device)
                 dW = torch.empty(W.shape, dtype=torch.float32, device=X.device)
                 fce_fused_fwd_bwd_ex(X if N else None, W, y if N else None, loss,
                                      dX if N else None, dW, ws, **opts)
-                ctx.save_for_backward(dX, dW)
+                ctx.grads = (dX, dW)
                 return loss[0]
             lse = torch.empty(max(N, 1), dtype=torch.float32, device=X.device)
             fce_forward_ex(X if N else None, W, y if N else None, loss if loss.numel() else None,
@@ -114,9 +117,14 @@ def _make_function():
         def backward(ctx, g):
             opts, hshape, hdt, wdt = ctx.cfg
             if opts["variant"] == "store_logits":
-                dX, dW = ctx.saved_tensors
-                gs = g.to(torch.float32)
-                return (dX * gs).to(hdt).reshape(hshape), (dW * gs).to(wdt), None, None
+                if ctx.grads is None:
+                    raise RuntimeError("the store_logits variant keeps its gradients for one "
+                                       "backward pass only")
+                dX, dW = ctx.grads
+                ctx.grads = None
+                g1 = g.reshape(1).to(torch.float32).contiguous()
+                fce_scale_grads(dX if dX.numel() else None, dW, g1)
+                return dX.to(hdt).reshape(hshape), dW.to(wdt), None, None
             X, W, y, lse = ctx.saved_tensors
             N, H = X.shape
             g1 = g.reshape(-1).to(torch.float32).contiguous()
@@ -148,7 +156,8 @@ def linear_cross_entropy(hidden, weight, labels, ignore_index: int = -100,
     (bfloat16: the gradient filtering approximation, dZ tiles whose softmax
     values are all below 2^-12 skipped) or "store_logits" (mean or sum only:
     the forward computes the gradients too, keeping each chunk's logits, and
-    holds dX and dW in fp32 until the backward scales them)."""
+    holds dX and dW in fp32 until the backward, where the library scales
+    them by the upstream gradient; one backward per forward)."""
     global _FN
     if _FN is None:
         _FN = _make_function()

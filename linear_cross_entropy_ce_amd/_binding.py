@@ -39,7 +39,8 @@ VARIANTS = {"recompute": FCE_VARIANT_RECOMPUTE, "store_logits": FCE_VARIANT_STOR
 EXPORTED = ("fce_workspace_size", "fce_plan", "fce_forward", "fce_backward", "fce_fused_fwd_bwd",
             "fce_workspace_size_ex", "fce_forward_ex", "fce_backward_ex", "fce_fused_fwd_bwd_ex",
             "fce_ce_logits_workspace_size", "fce_ce_logits",
-            "fce_get_label_errors", "fce_get_filter_stats", "fce_status_string",
+            "fce_scale_grads", "fce_get_label_errors", "fce_get_filter_stats",
+            "fce_status_string",
             "fce_last_hip_error",
             "fce_timing_enable", "fce_timing_read")
 
@@ -129,6 +130,8 @@ def load_library(path: str = LIB_PATH):
     lib.fce_ce_logits_workspace_size.argtypes = [i64]
     lib.fce_ce_logits.restype = i32
     lib.fce_ce_logits.argtypes = [vp, i64, vp, i64, i64, i32, op, vp, vp, vp, i64, vp, vp, u64, vp]
+    lib.fce_scale_grads.restype = i32
+    lib.fce_scale_grads.argtypes = [vp, i64, vp, i64, vp, vp]
     lib.fce_get_label_errors.restype = i32
     lib.fce_get_label_errors.argtypes = [vp, ctypes.POINTER(i32), vp]
     lib.fce_get_filter_stats.restype = i32
@@ -186,9 +189,112 @@ def fce_plan(N, H, V, dtype, chunk, schedule=SCHED_AUTO) -> dict:
     return info.as_dict()
 
 
+# ---------------------------------------------------------------- checks
+# Every wrapper checks its tensors before the library sees a pointer: a CPU
+# tensor, one on another device, a non-contiguous view or a mis-sized buffer
+# would hand the kernels an address they must not touch.  Errors are
+# TypeError (wrong type or dtype) or ValueError (device, layout, shape).
+def _tensors(where, **tensors):
+    """Each given tensor is a contiguous tensor on the current GPU."""
+    import torch
+
+    dev = None
+    for name, t in tensors.items():
+        if t is None:
+            continue
+        if not isinstance(t, torch.Tensor):
+            raise TypeError(f"{where}: {name} must be a torch.Tensor, not {type(t).__name__}")
+        if not t.is_cuda:
+            raise ValueError(f"{where}: {name} is on {t.device}; every tensor must be on the GPU")
+        if not t.is_contiguous():
+            raise ValueError(f"{where}: {name} must be contiguous")
+        if dev is None:
+            dev = t.device
+        elif t.device != dev:
+            raise ValueError(f"{where}: {name} is on {t.device}, other tensors on {dev}")
+    if dev is not None and dev.index != torch.cuda.current_device():
+        raise ValueError(f"{where}: tensors are on {dev} but the current device is "
+                         f"cuda:{torch.cuda.current_device()}")
+
+
+def _dtype_is(where, name, t, *dtypes):
+    if t is not None and t.dtype not in dtypes:
+        raise TypeError(f"{where}: {name} has dtype {t.dtype}; expected "
+                        + " or ".join(str(d) for d in dtypes))
+
+
+def _at_least(where, name, t, n):
+    if t is not None and t.numel() < n:
+        raise ValueError(f"{where}: {name} holds {t.numel()} elements, needs {n}")
+
+
+def _shape_is(where, name, t, shape):
+    if t is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{where}: {name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+
+
+def _problem(where, X, W, labels):
+    """(N, H, V) of X [N, H], W [V, H], labels [N]; X and labels may be None
+    for N = 0."""
+    import torch
+
+    if W is None:
+        raise ValueError(f"{where}: W is required")
+    if W.dim() != 2:
+        raise ValueError(f"{where}: W must be [V, H], got shape {tuple(W.shape)}")
+    _dtype_is(where, "W", W, torch.bfloat16, torch.float32)
+    V, H = W.shape
+    if X is None:
+        if labels is not None and labels.numel() != 0:
+            raise ValueError(f"{where}: labels given without X")
+        return 0, H, V
+    if X.dim() != 2 or X.shape[1] != H:
+        raise ValueError(f"{where}: X must be [N, {H}] to match W [{V}, {H}], "
+                         f"got shape {tuple(X.shape)}")
+    if X.dtype != W.dtype:
+        raise TypeError(f"{where}: X ({X.dtype}) and W ({W.dtype}) must share a dtype")
+    N = X.shape[0]
+    if labels is None:
+        raise ValueError(f"{where}: labels are required")
+    _dtype_is(where, "labels", labels, torch.int32)
+    if labels.numel() != N:
+        raise ValueError(f"{where}: labels hold {labels.numel()} elements, X has {N} rows")
+    return N, H, V
+
+
+def _check_call(where, X, W, labels, workspace, reduction, loss=None, lse=None, grad=None,
+                dX=None, dW=None, need_loss=False, need_lse=False, need_grads=False):
+    import torch
+
+    _tensors(where, X=X, W=W, labels=labels, workspace=workspace, loss=loss, lse=lse,
+             grad_loss=grad, dX=dX, dW=dW)
+    if workspace is None:
+        raise ValueError(f"{where}: a workspace tensor is required")
+    N, H, V = _problem(where, X, W, labels)
+    none = REDUCTIONS.get(reduction, reduction) == FCE_NONE
+    f32 = torch.float32
+    for name, t in (("loss", loss), ("lse", lse), ("grad_loss", grad), ("dX", dX), ("dW", dW)):
+        _dtype_is(where, name, t, f32)
+    if need_loss and (N > 0 or not none):
+        if loss is None:
+            raise ValueError(f"{where}: loss is required")
+        _at_least(where, "loss", loss, N if none else 1)
+    if need_lse and N > 0:
+        if lse is None:
+            raise ValueError(f"{where}: lse is required")
+        _at_least(where, "lse", lse, N)
+    _at_least(where, "grad_loss", grad, N if none else 1)
+    if need_grads:
+        if dW is None or (N > 0 and dX is None):
+            raise ValueError(f"{where}: dX and dW are required")
+        _shape_is(where, "dW", dW, (V, H))
+        if N > 0:
+            _shape_is(where, "dX", dX, (N, H))
+    return N, H, V
+
+
 def _common(X, W, labels, ignore_index, label_smoothing, reduction, chunk, schedule):
-    N, H = (X.shape[0], X.shape[1]) if X is not None else (0, W.shape[1])
-    V = W.shape[0]
+    N, H, V = _problem("fce", X, W, labels)
     return [_ptr(X), _ptr(W), _ptr(labels), N, H, V, _dtype_code(W), int(ignore_index),
             float(label_smoothing), REDUCTIONS.get(reduction, reduction), int(chunk),
             SCHEDULES.get(schedule, schedule)]
@@ -196,6 +302,8 @@ def _common(X, W, labels, ignore_index, label_smoothing, reduction, chunk, sched
 
 def fce_forward(X, W, labels, loss, lse, workspace, ignore_index=-100, label_smoothing=0.0,
                 reduction="mean", chunk=1024, schedule="auto", stream=None):
+    _check_call("fce_forward", X, W, labels, workspace, reduction, loss=loss, lse=lse,
+                need_loss=True, need_lse=True)
     args = _common(X, W, labels, ignore_index, label_smoothing, reduction, chunk, schedule)
     st = load_library().fce_forward(*args, _ptr(loss), _ptr(lse), _ptr(workspace),
                                     workspace.numel() * workspace.element_size(), _stream(stream))
@@ -204,6 +312,8 @@ def fce_forward(X, W, labels, loss, lse, workspace, ignore_index=-100, label_smo
 
 def fce_backward(X, W, labels, lse, grad_loss, dX, dW, workspace, ignore_index=-100,
                  label_smoothing=0.0, reduction="mean", chunk=1024, schedule="auto", stream=None):
+    _check_call("fce_backward", X, W, labels, workspace, reduction, lse=lse, grad=grad_loss,
+                dX=dX, dW=dW, need_lse=True, need_grads=True)
     args = _common(X, W, labels, ignore_index, label_smoothing, reduction, chunk, schedule)
     st = load_library().fce_backward(*args, _ptr(lse), _ptr(grad_loss), _ptr(dX), _ptr(dW),
                                      _ptr(workspace), workspace.numel() * workspace.element_size(),
@@ -214,6 +324,8 @@ def fce_backward(X, W, labels, lse, grad_loss, dX, dW, workspace, ignore_index=-
 def fce_fused_fwd_bwd(X, W, labels, loss, dX, dW, workspace, ignore_index=-100,
                       label_smoothing=0.0, reduction="mean", chunk=1024, schedule="auto",
                       stream=None):
+    _check_call("fce_fused_fwd_bwd", X, W, labels, workspace, reduction, loss=loss, dX=dX, dW=dW,
+                need_loss=True, need_grads=True)
     args = _common(X, W, labels, ignore_index, label_smoothing, reduction, chunk, schedule)
     st = load_library().fce_fused_fwd_bwd(*args, _ptr(loss), _ptr(dX), _ptr(dW), _ptr(workspace),
                                           workspace.numel() * workspace.element_size(),
@@ -227,8 +339,8 @@ def fce_workspace_size_ex(N, H, V, dtype, **options) -> int:
 
 
 def _common_ex(X, W, labels):
-    N, H = (X.shape[0], X.shape[1]) if X is not None else (0, W.shape[1])
-    return [_ptr(X), _ptr(W), _ptr(labels), N, H, W.shape[0], _dtype_code(W)]
+    N, H, V = _problem("fce", X, W, labels)
+    return [_ptr(X), _ptr(W), _ptr(labels), N, H, V, _dtype_code(W)]
 
 
 def _ws(workspace):
@@ -236,6 +348,8 @@ def _ws(workspace):
 
 
 def fce_forward_ex(X, W, labels, loss, lse, workspace, stream=None, **options):
+    _check_call("fce_forward_ex", X, W, labels, workspace, options.get("reduction", "mean"),
+                loss=loss, lse=lse, need_loss=True, need_lse=True)
     o = make_options(**options)
     st = load_library().fce_forward_ex(*_common_ex(X, W, labels), ctypes.byref(o), _ptr(loss),
                                        _ptr(lse), *_ws(workspace), _stream(stream))
@@ -243,6 +357,8 @@ def fce_forward_ex(X, W, labels, loss, lse, workspace, stream=None, **options):
 
 
 def fce_backward_ex(X, W, labels, lse, grad_loss, dX, dW, workspace, stream=None, **options):
+    _check_call("fce_backward_ex", X, W, labels, workspace, options.get("reduction", "mean"),
+                lse=lse, grad=grad_loss, dX=dX, dW=dW, need_lse=True, need_grads=True)
     o = make_options(**options)
     st = load_library().fce_backward_ex(*_common_ex(X, W, labels), ctypes.byref(o), _ptr(lse),
                                         _ptr(grad_loss), _ptr(dX), _ptr(dW), *_ws(workspace),
@@ -251,6 +367,8 @@ def fce_backward_ex(X, W, labels, lse, grad_loss, dX, dW, workspace, stream=None
 
 
 def fce_fused_fwd_bwd_ex(X, W, labels, loss, dX, dW, workspace, stream=None, **options):
+    _check_call("fce_fused_fwd_bwd_ex", X, W, labels, workspace, options.get("reduction", "mean"),
+                loss=loss, dX=dX, dW=dW, need_loss=True, need_grads=True)
     o = make_options(**options)
     st = load_library().fce_fused_fwd_bwd_ex(*_common_ex(X, W, labels), ctypes.byref(o),
                                              _ptr(loss), _ptr(dX), _ptr(dW), *_ws(workspace),
@@ -266,9 +384,38 @@ def fce_ce_logits(Z, labels, loss, lse, workspace, dZ=None, grad_loss=None, V=No
                   **options):
     """Loss (and dZ, which may be Z) on given logits Z [N, ldz]; V defaults
     to Z's row length."""
-    o = make_options(**options)
+    import torch
+
+    where = "fce_ce_logits"
+    _tensors(where, Z=Z, labels=labels, loss=loss, lse=lse, workspace=workspace, dZ=dZ,
+             grad_loss=grad_loss)
+    if Z is None or Z.dim() != 2:
+        raise ValueError(f"{where}: Z must be a 2-D [N, ldz] tensor")
+    if workspace is None:
+        raise ValueError(f"{where}: a workspace tensor is required")
+    _dtype_is(where, "Z", Z, torch.bfloat16, torch.float32)
     N, ldz = Z.shape
-    V = ldz if V is None else V
+    V = ldz if V is None else int(V)
+    if not 1 <= V <= ldz:
+        raise ValueError(f"{where}: V = {V} must lie in [1, {ldz}] (the row length of Z)")
+    if labels is None or labels.numel() != N:
+        raise ValueError(f"{where}: labels must hold {N} elements (rows of Z)")
+    _dtype_is(where, "labels", labels, torch.int32)
+    none = REDUCTIONS.get(options.get("reduction", "mean"), -1) == FCE_NONE
+    for name, t in (("loss", loss), ("lse", lse), ("grad_loss", grad_loss)):
+        _dtype_is(where, name, t, torch.float32)
+    if loss is None and (N > 0 or not none):
+        raise ValueError(f"{where}: loss is required")
+    _at_least(where, "loss", loss, N if none else 1)
+    if lse is None and N > 0:
+        raise ValueError(f"{where}: lse is required")
+    _at_least(where, "lse", lse, N)
+    _at_least(where, "grad_loss", grad_loss, N if none else 1)
+    if dZ is not None:
+        _dtype_is(where, "dZ", dZ, Z.dtype)
+        if dZ.dim() != 2 or dZ.shape[0] != N or dZ.shape[1] < V:
+            raise ValueError(f"{where}: dZ must be [{N}, >= {V}], got {tuple(dZ.shape)}")
+    o = make_options(**options)
     lddz = dZ.shape[1] if dZ is not None else 0
     st = load_library().fce_ce_logits(_ptr(Z), ldz, _ptr(labels), N, V, _dtype_code(Z),
                                       ctypes.byref(o), _ptr(loss), _ptr(lse), _ptr(dZ), lddz,
@@ -276,7 +423,26 @@ def fce_ce_logits(Z, labels, loss, lse, workspace, dZ=None, grad_loss=None, V=No
     _check(st, "fce_ce_logits")
 
 
+def fce_scale_grads(dX, dW, grad_loss, stream=None):
+    """dX *= g and dW *= g in place, g = grad_loss[0] (a device scalar); dX
+    may be None."""
+    import torch
+
+    where = "fce_scale_grads"
+    _tensors(where, dX=dX, dW=dW, grad_loss=grad_loss)
+    for name, t in (("dX", dX), ("dW", dW), ("grad_loss", grad_loss)):
+        _dtype_is(where, name, t, torch.float32)
+    if dW is None or grad_loss is None:
+        raise ValueError(f"{where}: dW and grad_loss are required")
+    _at_least(where, "grad_loss", grad_loss, 1)
+    n_dx = dX.numel() if dX is not None else 0
+    st = load_library().fce_scale_grads(_ptr(dX), n_dx, _ptr(dW), dW.numel(), _ptr(grad_loss),
+                                        _stream(stream))
+    _check(st, where)
+
+
 def fce_get_label_errors(workspace, stream=None) -> int:
+    _tensors("fce_get_label_errors", workspace=workspace)
     n = ctypes.c_int32(0)
     _check(load_library().fce_get_label_errors(_ptr(workspace), ctypes.byref(n), _stream(stream)),
            "fce_get_label_errors")
@@ -285,6 +451,7 @@ def fce_get_label_errors(workspace, stream=None) -> int:
 
 def fce_get_filter_stats(workspace, stream=None) -> tuple:
     """(kept, all) dZ tiles of the last filtered backward on this workspace."""
+    _tensors("fce_get_filter_stats", workspace=workspace)
     kept, total = ctypes.c_int64(0), ctypes.c_int64(0)
     _check(load_library().fce_get_filter_stats(_ptr(workspace), ctypes.byref(kept),
                                                ctypes.byref(total), _stream(stream)),

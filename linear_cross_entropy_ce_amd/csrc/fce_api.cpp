@@ -5,6 +5,7 @@
 
 #include <hip/hip_runtime_api.h>
 
+#include <atomic>
 #include <cmath>
 #include <cstring>
 #include <mutex>
@@ -99,18 +100,38 @@ class NullTimer final : public fce::KernelTimer {
   void end(hipStream_t) override {}
 };
 
+// The library's one piece of mutable global state besides the device-arch
+// cache: the optional kernel timer, guarded by g_timer_mu.  While timing is
+// on, each entry point holds the mutex from its first launch to its last
+// (TimerScope), so calls from several threads serialise their enqueueing and
+// their records never interleave; with timing off no lock is taken.
 EventTimer g_timer;
+std::mutex g_timer_mu;
+std::atomic<bool> g_timing_on{false};
 NullTimer g_null_timer;
 std::mutex g_arch_mu;
 int g_arch_ok[64] = {0};  // 0 unknown, 1 gfx950, -1 other
 
-// The timer for one entry-point call (each call starts its own chain of
-// boundary events).
-fce::KernelTimer* timer() {
-  if (!g_timer.enabled) return &g_null_timer;
-  g_timer.new_call();
-  return &g_timer;
-}
+// The timer of one entry-point call.  next() starts a chain of boundary
+// events for one launch sequence.
+class TimerScope {
+ public:
+  TimerScope() {
+    if (g_timing_on.load(std::memory_order_acquire)) {
+      lock_ = std::unique_lock<std::mutex>(g_timer_mu);
+      on_ = g_timer.enabled;
+    }
+  }
+  fce::KernelTimer* next() {
+    if (!on_) return &g_null_timer;
+    g_timer.new_call();
+    return &g_timer;
+  }
+
+ private:
+  std::unique_lock<std::mutex> lock_;
+  bool on_ = false;
+};
 
 fce_status check_device() {
   int dev = 0;
@@ -205,8 +226,10 @@ fce_status forward_impl(const void* X, const void* W, const int32_t* labels, int
   if ((loss == nullptr && !(none && N == 0)) || (N > 0 && lse == nullptr)) return FCE_ERR_NULL;
   if ((s = check_device()) != FCE_OK) return s;
   char* ws = static_cast<char*>(workspace);
-  hipError_t e = fce::launch_label_scan(p, labels, lo, nullptr, ws, stream, timer());
-  if (e == hipSuccess) e = fce::launch_forward(p, X, W, labels, lo, loss, lse, ws, stream, timer());
+  TimerScope ts;
+  hipError_t e = fce::launch_label_scan(p, labels, lo, nullptr, ws, stream, ts.next());
+  if (e == hipSuccess)
+    e = fce::launch_forward(p, X, W, labels, lo, loss, lse, ws, stream, ts.next());
   return from_hip(e);
 }
 
@@ -225,11 +248,12 @@ fce_status backward_impl(const void* X, const void* W, const int32_t* labels, in
   if ((s = check_device()) != FCE_OK) return s;
   const bool none = lo.reduction == fce::Reduction::None;
   char* ws = static_cast<char*>(workspace);
+  TimerScope ts;
   hipError_t e = fce::launch_label_scan(p, labels, lo, none ? nullptr : grad_loss, ws, stream,
-                                        timer());
+                                        ts.next());
   if (e == hipSuccess)
-    e = fce::launch_backward(p, X, W, labels, lo, lse, none ? grad_loss : nullptr, dX, dW, ws,
-                             stream, timer());
+    e = fce::launch_backward(p, X, W, labels, lo, lse, false, none ? grad_loss : nullptr, dX,
+                             dW, ws, stream, ts.next());
   return from_hip(e);
 }
 
@@ -252,15 +276,18 @@ fce_status fused_impl(const void* X, const void* W, const int32_t* labels, int64
   float* lse = reinterpret_cast<float*>(ws + p.off_lse);
   // One label scan serves both passes: with g = 1 its backward scale equals
   // the one fce_backward would compute.
-  hipError_t e = fce::launch_label_scan(p, labels, lo, nullptr, ws, stream, timer());
+  TimerScope ts;
+  hipError_t e = fce::launch_label_scan(p, labels, lo, nullptr, ws, stream, ts.next());
   if (p.variant == fce::Variant::StoreLogits) {
     if (e == hipSuccess)
-      e = fce::launch_fused_store(p, X, W, labels, lo, loss, lse, dX, dW, ws, stream, timer());
+      e = fce::launch_fused_store(p, X, W, labels, lo, loss, lse, dX, dW, ws, stream, ts.next());
     return from_hip(e);
   }
-  if (e == hipSuccess) e = fce::launch_forward(p, X, W, labels, lo, loss, lse, ws, stream, timer());
   if (e == hipSuccess)
-    e = fce::launch_backward(p, X, W, labels, lo, lse, nullptr, dX, dW, ws, stream, timer());
+    e = fce::launch_forward(p, X, W, labels, lo, loss, lse, ws, stream, ts.next());
+  if (e == hipSuccess)
+    e = fce::launch_backward(p, X, W, labels, lo, lse, true, nullptr, dX, dW, ws, stream,
+                             ts.next());
   return from_hip(e);
 }
 
@@ -407,7 +434,20 @@ fce_status fce_ce_logits(const void* Z, int64_t ldz, const int32_t* labels, int6
   c.loss = loss;
   c.lse = lse;
   c.ws = static_cast<char*>(workspace);
-  return from_hip(fce::launch_ce_logits(c, stream, timer()));
+  TimerScope ts;
+  return from_hip(fce::launch_ce_logits(c, stream, ts.next()));
+}
+
+fce_status fce_scale_grads(float* dX, int64_t n_dx, float* dW, int64_t n_dw,
+                           const float* grad_loss, hipStream_t stream) {
+  if (n_dx < 0 || n_dw < 0) return FCE_ERR_SHAPE;
+  if (grad_loss == nullptr || (n_dx > 0 && dX == nullptr) || (n_dw > 0 && dW == nullptr))
+    return FCE_ERR_NULL;
+  if ((n_dx > 0 && !aligned16(dX)) || (n_dw > 0 && !aligned16(dW))) return FCE_ERR_ALIGN;
+  if (n_dx == 0 && n_dw == 0) return FCE_OK;
+  if (fce_status s = check_device(); s != FCE_OK) return s;
+  TimerScope ts;
+  return from_hip(fce::launch_scale_grads(dX, n_dx, dW, n_dw, grad_loss, stream, ts.next()));
 }
 
 fce_status fce_get_label_errors(const void* workspace, int32_t* host_count, hipStream_t stream) {
@@ -455,7 +495,9 @@ const char* fce_last_hip_error(void) {
 }
 
 fce_status fce_timing_enable(int enable) {
+  std::lock_guard<std::mutex> lock(g_timer_mu);
   g_timer.enabled = enable != 0;
+  g_timing_on.store(g_timer.enabled, std::memory_order_release);
   if (!g_timer.enabled) {
     g_timer.records.clear();
     g_timer.open = -1;
@@ -465,6 +507,7 @@ fce_status fce_timing_enable(int enable) {
 
 fce_status fce_timing_read(fce_kernel_timing* out, int cap, int* count) {
   if (count == nullptr || (cap > 0 && out == nullptr)) return FCE_ERR_NULL;
+  std::lock_guard<std::mutex> lock(g_timer_mu);
   std::vector<fce_kernel_timing> agg;
   bool failed = g_timer.failed;
   for (const Record& r : g_timer.records) {

@@ -37,9 +37,12 @@ hipError_t launch_forward(const Plan& p, const void* X, const void* W, const int
                           KernelTimer* timer);
 
 // `grad_tok`: per-token upstream gradient [N] for reduction none, or NULL (1).
+// use_stats: fp32 takes its exponents from the split row statistics the
+// forward left in this workspace (the fused call); otherwise from lse alone.
 hipError_t launch_backward(const Plan& p, const void* X, const void* W, const int32_t* labels,
-                           const LossOpts& o, const float* lse, const float* grad_tok, float* dX,
-                           float* dW, char* ws, hipStream_t st, KernelTimer* timer);
+                           const LossOpts& o, const float* lse, bool use_stats,
+                           const float* grad_tok, float* dX, float* dW, char* ws, hipStream_t st,
+                           KernelTimer* timer);
 
 // Store-logits variant of forward + backward (upstream gradient 1): the plan
 // must be made with Variant::StoreLogits; the label scan runs first.
@@ -70,5 +73,9 @@ struct CeLogitsCall {
   char* ws;
 };
 hipError_t launch_ce_logits(const CeLogitsCall& c, hipStream_t st, KernelTimer* timer);
+
+// dX[0 .. n_dx) and dW[0 .. n_dw) multiplied in place by the device scalar g.
+hipError_t launch_scale_grads(float* dX, int64_t n_dx, float* dW, int64_t n_dw, const float* g,
+                              hipStream_t st, KernelTimer* timer);
 
 }  // namespace fce

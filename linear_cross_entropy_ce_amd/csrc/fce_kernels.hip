@@ -269,7 +269,14 @@ __global__ __launch_bounds__(C::NT) void k_fwd_lse(FwdArgs<typename C::Elem> a) 
           const int off = fm * C::MB + Map::row(lane, i >> 2) - Map::row(lane, 0) + (i & 3);
           const float z = acc.v[fm][fn][i];
           const bool ok = FULL || vbase + Map::row(lane, 0) + off < a.V;
-          s += ok ? hw_exp2(__builtin_fmaf(z, kLog2e, -mb)) : 0.0f;
+          // fp32: exp2((z - m) log2e), exact near the max, so each term's
+          // relative error does not grow with |m|; bf16 keeps the one-FMA form
+          float e;
+          if constexpr (sizeof(T) == 4)
+            e = hw_exp2((z - mnew) * kLog2e);
+          else
+            e = hw_exp2(__builtin_fmaf(z, kLog2e, -mb));
+          s += ok ? e : 0.0f;
           if (SMOOTH) zs += ok ? z : 0.0f;
         }
       rl[fn] = rl[fn] * hw_exp2((rm[fn] - mnew) * kLog2e) + s;
@@ -357,7 +364,7 @@ void launch_fwd_lse(const FwdArgs<typename C::Elem>& fa, int grid, hipStream_t s
 __global__ __launch_bounds__(kLossBlock) void k_lse_merge(
     const floatx4* __restrict__ part, int splits, int64_t n_pad, const int32_t* __restrict__ labels,
     int N, int V, int ignore, float eps, float zloss, float* __restrict__ lse,
-    float* __restrict__ blockloss, float* __restrict__ tok_loss) {
+    float* __restrict__ blockloss, float* __restrict__ tok_loss, float2* __restrict__ stat) {
   __shared__ float s_red[kLossBlock];
   const int tok = blockIdx.x * kLossBlock + threadIdx.x;
   float term = 0.0f;
@@ -369,14 +376,20 @@ __global__ __launch_bounds__(kLossBlock) void k_lse_merge(
         const floatx4 o = part[static_cast<int64_t>(s) * n_pad + tok];
         lse_merge(st, o);
       }
-      const float L = st[0] + hw_log2(st[1]) * kLn2;
+      // LSE = m + log l, kept split as well (m, log2 l): the large part m
+      // cancels exactly against the logits near the max, where the rounded
+      // sum m + log l would carry an error of |LSE| 2^-25
+      const float lg = hw_log2(st[1]);
+      const float L = st[0] + lg * kLn2;
       lse[tok] = L;
-      term = L - (1.0f - eps) * st[2];
+      if (stat) stat[tok] = float2{st[0], lg};
+      term = (st[0] - (1.0f - eps) * st[2]) + lg * kLn2;
       if (eps != 0.0f) term -= (eps / static_cast<float>(V)) * st[3];
       if (zloss != 0.0f) term += zloss * L * L;
       if (tok_loss) tok_loss[tok] = term;
     } else {
       lse[tok] = NAN;
+      if (stat) stat[tok] = float2{0.0f, INFINITY};
       if (tok_loss) tok_loss[tok] = (y == ignore) ? 0.0f : NAN;
     }
   }
@@ -404,6 +417,21 @@ __global__ __launch_bounds__(256) void k_loss_final(const float* __restrict__ bl
   if (threadIdx.x == 0) loss[0] = ctrl->n_invalid > 0 ? NAN : s_red[0] / ctrl->scale_fwd;
 }
 
+// p[0 .. n) *= g[0], 16 bytes per thread and step (p 16-byte aligned; the
+// last n % 4 elements one by one).
+__global__ __launch_bounds__(256) void k_scale(float* __restrict__ p, int64_t n,
+                                               const float* __restrict__ g) {
+  const float s = g[0];
+  const int64_t nv = n / 4;
+  const int64_t stride = static_cast<int64_t>(gridDim.x) * blockDim.x;
+  const int64_t i0 = blockIdx.x * static_cast<int64_t>(blockDim.x) + threadIdx.x;
+  for (int64_t i = i0; i < nv; i += stride) {
+    floatx4* q = reinterpret_cast<floatx4*>(p) + i;
+    *q = *q * s;
+  }
+  if (i0 < n - 4 * nv) p[4 * nv + i0] *= s;
+}
+
 __global__ void k_fill_zero(float* __restrict__ p, int64_t n) {
   for (int64_t i = blockIdx.x * static_cast<int64_t>(blockDim.x) + threadIdx.x; i < n;
        i += static_cast<int64_t>(gridDim.x) * blockDim.x)
@@ -425,6 +453,9 @@ struct DzArgs {
   int64_t ldz;
   const int32_t* flag;  // this token block's "has a valid label" flag
   uint8_t* keep;        // FILTER: [tok_tiles][voc_tiles] tile kept (1) or skipped (0)
+  // fp32: the forward's split row statistics (m, log2 l) + tok0, or NULL to
+  // take the exponent from the LSE alone
+  const float2* stat;
 };
 
 // Gradient filtering ("Cut Cross-Entropy", llms.blog, "Apple Cut
@@ -474,6 +505,23 @@ __global__ __launch_bounds__(C::NT) void k_bwd_dz(DzArgs<typename C::Elem> a) {
       // g_i = 0, so its dZ is exactly 0.
       const float gi = valid ? (a.gtok ? a.gtok[tl] : 1.0f) : 0.0f;
       const float lb = valid ? L * kLog2e : INFINITY;
+      // fp32: exp2((z - m) log2e - log2 l) with the forward's split
+      // statistics (or m = LSE, log2 l = 0 without them): the subtraction is
+      // exact near the max, so p keeps its accuracy at large |LSE|
+      float sm = 0.0f, slg = INFINITY;
+      if constexpr (sizeof(T) == 4) {
+        if (valid) {
+          const float2 sv = a.stat ? a.stat[tl] : float2{L, 0.0f};
+          sm = sv.x;
+          slg = sv.y;
+        }
+      }
+      auto expo = [&](float z) -> float {
+        if constexpr (sizeof(T) == 4)
+          return hw_exp2(__builtin_fmaf(z - sm, kLog2e, -slg));
+        else
+          return hw_exp2(__builtin_fmaf(z, kLog2e, -lb));
+      };
       const float c1 = (1.0f + 2.0f * a.zloss * L) * gi;
       const float c0 = -eps_v * gi;
       const int vrow = m0 + wm * C::WTM + Map::row(lane, 0);  // row of element 0
@@ -495,7 +543,7 @@ __global__ __launch_bounds__(C::NT) void k_bwd_dz(DzArgs<typename C::Elem> a) {
           for (int i = 0; i < C::NV; ++i) {
             const int off = fm * C::MB + Map::row(lane, i >> 2) - Map::row(lane, 0) + (i & 3);
             const bool ok = FULL || vrow + off < a.nvoc;
-            const float e = hw_exp2(__builtin_fmaf(acc.v[fm][fn][i], kLog2e, -lb));
+            const float e = expo(acc.v[fm][fn][i]);
             keep |= ok && e >= kFilterP;
             float d = __builtin_fmaf(e, c1, c0);
             d -= (rel == off) ? t : 0.0f;
@@ -512,8 +560,7 @@ __global__ __launch_bounds__(C::NT) void k_bwd_dz(DzArgs<typename C::Elem> a) {
               float d[4];
 #pragma unroll
               for (int q = 0; q < 4; ++q) {
-                d[q] = __builtin_fmaf(
-                    hw_exp2(__builtin_fmaf(acc.v[fm][fn][4 * g + q], kLog2e, -lb)), c1, c0);
+                d[q] = __builtin_fmaf(expo(acc.v[fm][fn][4 * g + q]), c1, c0);
                 if (LABEL) d[q] -= (rel == off0 + q) ? t : 0.0f;
                 if (!FULL) d[q] = (vrow + off0 + q < a.nvoc) ? d[q] : 0.0f;
               }
@@ -1113,6 +1160,9 @@ struct CeArgs {
   const Ctrl* ctrl;   // scale_bwd = g / D (mean, sum)
   float* lse;
   float* rowloss;  // per-row loss terms
+  // GIVEN with fp32 logits: the forward's split row statistics (m, log2 l)
+  // of each row, or NULL (then m = LSE, log2 l = 0)
+  const float2* stat;
 };
 
 // NC: vectors of the row kept in LDS between the passes (0: none, for the
@@ -1127,7 +1177,7 @@ __global__ __launch_bounds__(kCeThreads) void k_ce_logits(CeArgs a) {
   typedef CeVec<T> CV;
   constexpr int E = CV::E;
   __shared__ floatx4 s_part[kCeThreads / 64];
-  __shared__ float s_bcast[1];
+  __shared__ float s_bcast[2];
   __shared__ u32x4 s_cache[NC > 0 ? NC : 1];  // the row's first vectors (pass 1 -> 2)
   const int row = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int y = a.labels[row];
@@ -1157,9 +1207,14 @@ __global__ __launch_bounds__(kCeThreads) void k_ce_logits(CeArgs a) {
     return;
   }
 
-  float L;
+  // LSE = m + lg ln 2, with the row max m and lg = log2 of the sum of
+  // exp(z - m) kept apart for the exponents of pass 2 (fp32)
+  float L, m_row, lg_row;
   if constexpr (GIVEN) {
     L = a.lse[row];
+    const float2 sv = a.stat ? a.stat[row] : float2{L, 0.0f};
+    m_row = sv.x;
+    lg_row = sv.y;
   } else {
     // pass 1: running (max, sum-exp, sum z) of this thread's vectors
     float m = -INFINITY, l = 0.0f, zs = 0.0f;
@@ -1191,8 +1246,11 @@ __global__ __launch_bounds__(kCeThreads) void k_ce_logits(CeArgs a) {
         const float mn = fmaxf(m, vm);
         const float mnl = mn * kLog2e;
         float acc = 0.0f;
+        // fp32: exp2((z - m) log2e), exact near the max at any |m| (the
+        // one-FMA form carries an error of |m| 2^-25 into every term)
 #pragma unroll
-        for (int e = 0; e < E; ++e) acc += hw_exp2(fmaf(f[e], kLog2e, -mnl));
+        for (int e = 0; e < E; ++e)
+          acc += hw_exp2((sizeof(T) == 4) ? (f[e] - mn) * kLog2e : fmaf(f[e], kLog2e, -mnl));
         l = ((m == -INFINITY) ? 0.0f : l * hw_exp2((m - mn) * kLog2e)) + acc;
         m = mn;
       }
@@ -1209,18 +1267,23 @@ __global__ __launch_bounds__(kCeThreads) void k_ce_logits(CeArgs a) {
     if (tid == 0) {
       floatx4 st = s_part[0];
       for (int w = 1; w < kCeThreads / 64; ++w) lse_merge(st, s_part[w]);
-      const float Lr = st[0] + hw_log2(st[1]) * kLn2;
+      const float lg = hw_log2(st[1]);
+      const float Lr = st[0] + lg * kLn2;
       const float zy = static_cast<float>(zrow[y]);  // the target logit
-      float term = Lr - (1.0f - a.eps) * zy;
+      // (m - z_y) first: exact when the target logit is near the max
+      float term = (st[0] - (1.0f - a.eps) * zy) + lg * kLn2;
       if (smooth) term -= (a.eps / static_cast<float>(a.V)) * st[3];
       if (a.zloss != 0.0f) term += a.zloss * Lr * Lr;
       a.lse[row] = Lr;
       a.rowloss[row] = term;
-      s_bcast[0] = Lr;
+      s_bcast[0] = st[0];
+      s_bcast[1] = lg;
     }
     if (!drow) return;
     __syncthreads();
-    L = s_bcast[0];
+    m_row = s_bcast[0];
+    lg_row = s_bcast[1];
+    L = m_row + lg_row * kLn2;
   }
 
   // pass 2: dZ = (p (1 + 2 alpha L) - eps/V - (1-eps)[i = y]) * scale, p = exp(z - L)
@@ -1243,8 +1306,14 @@ __global__ __launch_bounds__(kCeThreads) void k_ce_logits(CeArgs a) {
       const int j = j0 + u * kCeThreads;
       float f[E];
       CV::unpack(r[u], f);
+      // fp32: exp2((z - m) log2e - log2 l), exact near the max at any |LSE|;
+      // bf16 logits carry far coarser rounding and keep the one-FMA form
 #pragma unroll
-      for (int e = 0; e < E; ++e) f[e] = fmaf(hw_exp2(fmaf(f[e], kLog2e, -Ll)), ga, -gb);
+      for (int e = 0; e < E; ++e) {
+        const float x = (sizeof(T) == 4) ? fmaf(f[e] - m_row, kLog2e, -lg_row)
+                                         : fmaf(f[e], kLog2e, -Ll);
+        f[e] = fmaf(hw_exp2(x), ga, -gb);
+      }
       if (j == jy) {  // the one lane holding the label
 #pragma unroll
         for (int e = 0; e < E; ++e) f[e] -= (e == ey) ? gy : 0.0f;
@@ -1287,6 +1356,7 @@ hipError_t run_forward(const Plan& p, const T* X, const T* W, const int32_t* lab
   Ctrl* ctrl = reinterpret_cast<Ctrl*>(ws + p.off_ctrl);
   float* blockloss = reinterpret_cast<float*>(ws + p.off_blockloss);
   floatx4* part = reinterpret_cast<floatx4*>(ws + p.off_part);
+  float2* stat = p.stat_bytes ? reinterpret_cast<float2*>(ws + p.off_stat) : nullptr;
   const int N = static_cast<int>(p.N), H = static_cast<int>(p.H), V = static_cast<int>(p.V);
   if (N > 0) {
     FwdArgs<T> fa{X, W, labels, N, H, V, ignore,
@@ -1306,7 +1376,7 @@ hipError_t run_forward(const Plan& p, const T* X, const T* W, const int32_t* lab
     timer->begin("lse_merge", 0.0, st);
     k_lse_merge<<<cdiv_i(N, kLossBlock), kLossBlock, 0, st>>>(
         part, fa.splits, p.n_pad, labels, N, V, ignore, eps, o.zloss, lse, blockloss,
-        none ? loss : nullptr);
+        none ? loss : nullptr, stat);
     FCE_CHECK_LAUNCH();
     timer->end(st);
   }
@@ -1478,8 +1548,9 @@ hipError_t transpose_x(const Plan& p, const T* X, char* ws, hipStream_t st, Kern
 
 template <typename T>
 hipError_t run_backward(const Plan& p, const T* X, const T* W, const int32_t* labels,
-                        const LossOpts& o, const float* lse, const float* grad_tok, float* dX,
-                        float* dW, char* ws, hipStream_t st, KernelTimer* timer) {
+                        const LossOpts& o, const float* lse, const float2* stat,
+                        const float* grad_tok, float* dX, float* dW, char* ws, hipStream_t st,
+                        KernelTimer* timer) {
   const int ignore = o.ignore;
   const float eps = o.eps;
   typedef typename ShapeOf<T>::C C;
@@ -1524,7 +1595,7 @@ hipError_t run_backward(const Plan& p, const T* X, const T* W, const int32_t* la
       DzArgs<T> da{X + tok0 * H, W + voc0 * H, labels + tok0, lse + tok0, ntok, nvoc,
                    static_cast<int>(voc0), static_cast<int>(H), static_cast<int>(V), ignore, eps,
                    o.zloss, grad_tok ? grad_tok + tok0 : nullptr, voc_tiles, tok_tiles, 4, dz,
-                   p.ldz, flags + ia, keep};
+                   p.ldz, flags + ia, keep, stat ? stat + tok0 : nullptr};
       timer->begin("bwd_dz", blk_flops, st);
       if constexpr (sizeof(T) == 2) {
         if (filt) {
@@ -1601,6 +1672,7 @@ hipError_t run_fused_store(const Plan& p, const T* X, const T* W, const int32_t*
   floatx4* part = reinterpret_cast<floatx4*>(ws + p.off_part);
   T* zs = reinterpret_cast<T*>(ws + p.off_scratch);
   float* dxpart = reinterpret_cast<float*>(ws + p.off_dxpart);
+  float2* stat = p.stat_bytes ? reinterpret_cast<float2*>(ws + p.off_stat) : nullptr;
   const int64_t N = p.N, H = p.H, V = p.V;
   if (N == 0) {
     timer->begin("fill_zero", 0.0, st);
@@ -1631,12 +1703,14 @@ hipError_t run_fused_store(const Plan& p, const T* X, const T* W, const int32_t*
     timer->begin("lse_merge", 0.0, st);
     k_lse_merge<<<cdiv_i(ntok, kLossBlock), kLossBlock, 0, st>>>(
         part, fa.splits, p.n_pad, labels + tok0, ntok, static_cast<int>(V), o.ignore, o.eps,
-        o.zloss, lse + tok0, blockloss + tok0 / kLossBlock, none ? loss + tok0 : nullptr);
+        o.zloss, lse + tok0, blockloss + tok0 / kLossBlock, none ? loss + tok0 : nullptr,
+        stat ? stat + tok0 : nullptr);
     FCE_CHECK_LAUNCH();
     timer->end(st);
     // logits -> dZ in place (upstream gradient 1 per token for reduction none)
     CeArgs ca{zs, p.ldz, zs, p.ldz, labels + tok0, ntok, static_cast<int>(V), o.ignore,
-              static_cast<int>(o.reduction), o.eps, o.zloss, nullptr, ctrl, lse + tok0, nullptr};
+              static_cast<int>(o.reduction), o.eps, o.zloss, nullptr, ctrl, lse + tok0, nullptr,
+              stat ? stat + tok0 : nullptr};
     timer->begin("sl_dz", 0.0, st);
     k_ce_logits<T, true, 0><<<ntok, kCeThreads, 0, st>>>(ca);
     FCE_CHECK_LAUNCH();
@@ -1692,13 +1766,34 @@ hipError_t launch_forward(const Plan& p, const void* X, const void* W, const int
 }
 
 hipError_t launch_backward(const Plan& p, const void* X, const void* W, const int32_t* labels,
-                           const LossOpts& o, const float* lse, const float* grad_tok, float* dX,
-                           float* dW, char* ws, hipStream_t st, KernelTimer* timer) {
+                           const LossOpts& o, const float* lse, bool use_stats,
+                           const float* grad_tok, float* dX, float* dW, char* ws, hipStream_t st,
+                           KernelTimer* timer) {
+  const float2* stat = (use_stats && p.stat_bytes)
+                           ? reinterpret_cast<const float2*>(ws + p.off_stat)
+                           : nullptr;
   if (p.dtype == Dtype::BF16)
     return run_backward<bf16>(p, static_cast<const bf16*>(X), static_cast<const bf16*>(W), labels,
-                              o, lse, grad_tok, dX, dW, ws, st, timer);
+                              o, lse, nullptr, grad_tok, dX, dW, ws, st, timer);
   return run_backward<float>(p, static_cast<const float*>(X), static_cast<const float*>(W), labels,
-                             o, lse, grad_tok, dX, dW, ws, st, timer);
+                             o, lse, stat, grad_tok, dX, dW, ws, st, timer);
+}
+
+hipError_t launch_scale_grads(float* dX, int64_t n_dx, float* dW, int64_t n_dw, const float* g,
+                              hipStream_t st, KernelTimer* timer) {
+  timer->begin("scale_grads", 0.0, st);
+  if (n_dx > 0) {
+    k_scale<<<static_cast<unsigned>(std::min<int64_t>(4096, std::max<int64_t>(1, cdiv_i(n_dx, 1024)))),
+              256, 0, st>>>(dX, n_dx, g);
+    FCE_CHECK_LAUNCH();
+  }
+  if (n_dw > 0) {
+    k_scale<<<static_cast<unsigned>(std::min<int64_t>(4096, std::max<int64_t>(1, cdiv_i(n_dw, 1024)))),
+              256, 0, st>>>(dW, n_dw, g);
+    FCE_CHECK_LAUNCH();
+  }
+  timer->end(st);
+  return hipSuccess;
 }
 
 hipError_t launch_ce_logits(const CeLogitsCall& c, hipStream_t st, KernelTimer* timer) {
@@ -1715,7 +1810,7 @@ hipError_t launch_ce_logits(const CeLogitsCall& c, hipStream_t st, KernelTimer* 
   if (N > 0) {
     CeArgs a{c.Z, c.ldz, c.dZ, c.lddz, c.labels, N, V, c.o.ignore,
              static_cast<int>(c.o.reduction), c.o.eps, c.o.zloss, none ? c.grad : nullptr,
-             ctrl, c.lse, none ? c.loss : rowloss};
+             ctrl, c.lse, none ? c.loss : rowloss, nullptr};
     timer->begin("ce_logits", 0.0, st);
     if (c.bf16 && c.dZ)
       k_ce_logits<bf16, false, kCeCache><<<N, kCeThreads, 0, st>>>(a);

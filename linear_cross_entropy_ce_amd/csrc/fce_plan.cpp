@@ -221,6 +221,11 @@ bool make_plan(int64_t N, int64_t H, int64_t V, Dtype dtype, int64_t chunk, Sche
   off = align_up(off + sizeof(float) * static_cast<size_t>(p.n_loss_blocks));
   p.off_lse = off;
   off = align_up(off + sizeof(float) * static_cast<size_t>(std::max<int64_t>(N, 1)));
+  if (dtype == Dtype::F32) {
+    p.off_stat = off;
+    p.stat_bytes = 8u * static_cast<size_t>(std::max<int64_t>(N, 1));
+    off = align_up(off + p.stat_bytes);
+  }
   p.off_scratch = off;
   p.scratch_bytes = (N == 0) ? 0
                              : static_cast<size_t>(p.scratch_rows) * static_cast<size_t>(p.ldz) *

@@ -42,6 +42,9 @@ struct Plan {
   // workspace layout (byte offsets, 256-byte aligned)
   size_t off_ctrl = 0, off_flags = 0, off_part = 0, off_blockloss = 0, off_lse = 0,
          off_scratch = 0, off_dxpart = 0, total = 0;
+  // fp32: the forward's split row statistics (row max m, log2 of the sum of
+  // exp(z - m)) per token, float2 [N]; 0 bytes for bf16
+  size_t off_stat = 0, stat_bytes = 0;
   // Filtered: per logit block, kept flags [tt][vt] and the kept-block lists
   int64_t filt_tt = 0, filt_vt = 0;
   size_t off_keep = 0, off_rowlist = 0, off_rowcnt = 0, off_collist = 0, off_colcnt = 0,

@@ -8,3 +8,17 @@ if ROOT not in sys.path:
 
 def pytest_configure(config):
     config.addinivalue_line("markers", "gpu: needs an MI355X (gfx950) GPU and the built HIP library")
+
+
+def pytest_terminal_summary(terminalreporter):
+    # every error the GPU parity tests measured, with its bound (a passing
+    # run's log then shows the margins, not just a pass)
+    try:
+        import parity_log
+    except ImportError:
+        return
+    lines = parity_log.summary_lines()
+    if lines:
+        terminalreporter.section("parity errors against the fp64 oracle")
+        for line in lines:
+            terminalreporter.write_line(line)

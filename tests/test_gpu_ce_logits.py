@@ -8,6 +8,7 @@ torch = pytest.importorskip("torch")
 
 import linear_cross_entropy_ce_amd as fce  # noqa: E402
 import oracle.fce_oracle as orc  # noqa: E402
+import parity_log  # noqa: E402
 import workloads as wk  # noqa: E402
 
 pytestmark = pytest.mark.gpu
@@ -83,9 +84,9 @@ def check(inp, got, grad=1.0, tol=None, **opts):
     else:
         err = abs(got["loss"][0] - loss) / max(abs(loss), 1.0)
     el = rel_l2(got["lse"][valid], lse[valid])
-    print(f"[{wl.name} {wl.N}x{wl.V} {wl.dtype} {red}] loss {err:.2e} lse {el:.2e}", end="",
-          flush=True)
-    assert err <= tl and el <= tl
+    label = f"ce_logits {wl.name} {wl.N}x{wl.V} {wl.dtype} {red}"
+    print(f"[{label}] loss {err:.2e} lse {el:.2e}", end="", flush=True)
+    errs = dict(loss=err, lse=el)
     if "dZ" in got:
         # a row's dZ has norm of order s_i, the row's gradient scale (g / D,
         # or g_i for reduction none); the relative error's denominator is
@@ -95,10 +96,14 @@ def check(inp, got, grad=1.0, tol=None, **opts):
         floor = 1e-2 * np.linalg.norm(np.where(valid, g, 0.0))
         ed = np.linalg.norm(got["dZ"].astype(np.float64) - dZ) / max(np.linalg.norm(dZ), floor)
         print(f" dZ {ed:.2e}", flush=True)
-        assert ed <= tg
-        assert np.all(got["dZ"][~valid] == 0.0)
+        errs["dZ"] = ed
     else:
         print(flush=True)
+    parity_log.record(label, tl, tg, **errs)
+    assert err <= tl and el <= tl
+    if "dZ" in got:
+        assert errs["dZ"] <= tg
+        assert np.all(got["dZ"][~valid] == 0.0)
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "fp32"])
@@ -157,10 +162,11 @@ def test_large_logits_stay_finite():
     inp = wk.draw_logits(wl)
     got = run(inp)
     assert np.isfinite(got["loss"]).all() and np.isfinite(got["dZ"]).all()
-    # fp32 forms z - LSE with an absolute rounding error of about |LSE| u
-    # (u = 2^-24), so each probability carries that relative error
-    big = 4.0 * np.abs(got["lse"]).max() * 2.0 ** -24
-    check(inp, got, tol=(1e-5, max(1e-5, big)))
+    # |LSE| is in the hundreds: the kernel keeps the row max m and log2 of
+    # the sum apart and forms each exponent as (z - m) log2e - log2 l, exact
+    # near the max, so fp32's 1e-5 holds here as for small logits
+    print(f"|LSE| up to {np.abs(got['lse']).max():.0f}")
+    check(inp, got)
 
 
 def test_full_size_llama2_shape():
