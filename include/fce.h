@@ -186,6 +186,31 @@ fce_status fce_fused_fwd_bwd(const void* X, const void* W, const int32_t* labels
                              fce_schedule schedule, float* loss, float* dX, float* dW,
                              void* workspace, size_t workspace_bytes, hipStream_t stream);
 
+/* ---- The entry point that allocates nothing.
+ *
+ * For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid allocation):
+ * fce_fused_fwd_bwd_ex with the library's own static scratch as the
+ * workspace.  The scratch is a device array of FCE_STATIC_SCRATCH_BYTES that
+ * every GPU the library runs on holds until the process ends (one copy per
+ * GPU); the call itself allocates nothing.  The caller still passes inputs
+ * and outputs, as for fce_fused_fwd_bwd_ex, whose arguments, options and
+ * results this call shares bitwise.  A problem whose workspace
+ * (fce_workspace_size_ex with the same options) exceeds
+ * FCE_STATIC_SCRATCH_BYTES returns FCE_ERR_WORKSPACE with nothing enqueued;
+ * a smaller chunk, or FCE_SCHED_TOKEN, shrinks the workspace.  Every call
+ * on one GPU uses that GPU's one scratch: calls that overlap on one GPU
+ * (different streams, or threads without ordering) race and must not be
+ * made; calls ordered on one stream are safe.  The scratch keeps the last
+ * call's contents; nothing in it needs to start at zero, since each call
+ * writes every byte of it that it reads. */
+#define FCE_STATIC_SCRATCH_BYTES ((size_t)64 << 20)
+
+fce_status fce_fused_fwd_bwd_noalloc(const void* X, const void* W, const int32_t* labels,
+                                     int64_t N, int64_t H, int64_t V, fce_dtype dtype,
+                                     const fce_options* opt, float* loss, float* dX, float* dW,
+                                     hipStream_t stream);
+
 /* Applies the upstream scalar gradient to gradients computed with g = 1:
  * dX[i] *= g for i < n_dx and dW[j] *= g for j < n_dw, in place, where g is
  * the device scalar grad_loss[0] (chain rule of the loss scale; llms.blog,

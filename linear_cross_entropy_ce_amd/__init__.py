@@ -34,6 +34,8 @@ from ._binding import (  # noqa: F401
     fce_forward_ex,
     fce_fused_fwd_bwd,
     fce_fused_fwd_bwd_ex,
+    fce_fused_fwd_bwd_noalloc,
+    STATIC_SCRATCH_BYTES,
     fce_workspace_size_ex,
     make_options,
     fce_get_label_errors,

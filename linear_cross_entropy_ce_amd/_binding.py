@@ -39,7 +39,8 @@ VARIANTS = {"recompute": FCE_VARIANT_RECOMPUTE, "store_logits": FCE_VARIANT_STOR
 EXPORTED = ("fce_workspace_size", "fce_plan", "fce_forward", "fce_backward", "fce_fused_fwd_bwd",
             "fce_workspace_size_ex", "fce_forward_ex", "fce_backward_ex", "fce_fused_fwd_bwd_ex",
             "fce_ce_logits_workspace_size", "fce_ce_logits",
-            "fce_scale_grads", "fce_get_label_errors", "fce_get_filter_stats",
+            "fce_fused_fwd_bwd_noalloc", "fce_scale_grads", "fce_get_label_errors",
+            "fce_get_filter_stats",
             "fce_status_string",
             "fce_last_hip_error",
             "fce_timing_enable", "fce_timing_read")
@@ -130,6 +131,8 @@ def load_library(path: str = LIB_PATH):
     lib.fce_ce_logits_workspace_size.argtypes = [i64]
     lib.fce_ce_logits.restype = i32
     lib.fce_ce_logits.argtypes = [vp, i64, vp, i64, i64, i32, op, vp, vp, vp, i64, vp, vp, u64, vp]
+    lib.fce_fused_fwd_bwd_noalloc.restype = i32
+    lib.fce_fused_fwd_bwd_noalloc.argtypes = common_ex + [vp, vp, vp, vp]
     lib.fce_scale_grads.restype = i32
     lib.fce_scale_grads.argtypes = [vp, i64, vp, i64, vp, vp]
     lib.fce_get_label_errors.restype = i32
@@ -374,6 +377,35 @@ def fce_fused_fwd_bwd_ex(X, W, labels, loss, dX, dW, workspace, stream=None, **o
                                              _ptr(loss), _ptr(dX), _ptr(dW), *_ws(workspace),
                                              _stream(stream))
     _check(st, "fce_fused_fwd_bwd_ex")
+
+
+# bytes of the library's static scratch (FCE_STATIC_SCRATCH_BYTES in fce.h)
+STATIC_SCRATCH_BYTES = 64 << 20
+
+
+def fce_fused_fwd_bwd_noalloc(X, W, labels, loss, dX, dW, stream=None, **options):
+    """fce_fused_fwd_bwd_ex on the library's static scratch: no workspace
+    argument, nothing allocated."""
+    _tensors("fce_fused_fwd_bwd_noalloc", X=X, W=W, labels=labels, loss=loss, dX=dX, dW=dW)
+    import torch
+
+    N, H, V = _problem("fce_fused_fwd_bwd_noalloc", X, W, labels)
+    for name, t in (("loss", loss), ("dX", dX), ("dW", dW)):
+        _dtype_is("fce_fused_fwd_bwd_noalloc", name, t, torch.float32)
+    none = REDUCTIONS.get(options.get("reduction", "mean"), -1) == FCE_NONE
+    if loss is None and (N > 0 or not none):
+        raise ValueError("fce_fused_fwd_bwd_noalloc: loss is required")
+    _at_least("fce_fused_fwd_bwd_noalloc", "loss", loss, N if none else 1)
+    if dW is None or (N > 0 and dX is None):
+        raise ValueError("fce_fused_fwd_bwd_noalloc: dX and dW are required")
+    _shape_is("fce_fused_fwd_bwd_noalloc", "dW", dW, (V, H))
+    if N > 0:
+        _shape_is("fce_fused_fwd_bwd_noalloc", "dX", dX, (N, H))
+    o = make_options(**options)
+    st = load_library().fce_fused_fwd_bwd_noalloc(*_common_ex(X, W, labels), ctypes.byref(o),
+                                                  _ptr(loss), _ptr(dX), _ptr(dW),
+                                                  _stream(stream))
+    _check(st, "fce_fused_fwd_bwd_noalloc")
 
 
 def fce_ce_logits_workspace_size(N) -> int:

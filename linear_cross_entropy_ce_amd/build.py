@@ -17,7 +17,7 @@ LIBDIR = os.path.join(PKG, "lib")
 LIB = os.path.join(LIBDIR, "libfce.so")
 OBJDIR = os.path.join(ROOT, "_build")
 
-SOURCES = ["fce_kernels.hip", "fce_api.cpp", "fce_plan.cpp"]
+SOURCES = ["fce_kernels.hip", "fce_api.cpp", "fce_plan.cpp", "fce_noalloc.hip"]
 ARCH = "gfx950"
 # Packed fp32 instructions are disabled for all device code.
 HIPCC_FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",

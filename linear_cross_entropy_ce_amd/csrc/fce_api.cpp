@@ -438,6 +438,30 @@ fce_status fce_ce_logits(const void* Z, int64_t ldz, const int32_t* labels, int6
   return from_hip(fce::launch_ce_logits(c, stream, ts.next()));
 }
 
+fce_status fce_fused_fwd_bwd_noalloc(const void* X, const void* W, const int32_t* labels,
+                                     int64_t N, int64_t H, int64_t V, fce_dtype dtype,
+                                     const fce_options* opt, float* loss, float* dX, float* dW,
+                                     hipStream_t stream) {
+  // the plan's workspace must fit the static scratch (checked before any
+  // device call, like every other argument error)
+  if (dtype != FCE_F32 && dtype != FCE_BF16) return FCE_ERR_ARG;
+  const size_t need = fce_workspace_size_ex(N, H, V, dtype, opt);
+  if (need == 0) {
+    // invalid arguments: let the shared validation name them
+    Plan p;
+    fce::LossOpts lo;
+    const fce_status s = validate(X, W, labels, N, H, V, dtype, opt, true, kAllVariants,
+                                  FCE_STATIC_SCRATCH_BYTES, W, &p, &lo);
+    return s != FCE_OK ? s : FCE_ERR_ARG;
+  }
+  if (need > FCE_STATIC_SCRATCH_BYTES) return FCE_ERR_WORKSPACE;
+  if (fce_status s = check_device(); s != FCE_OK) return s;
+  void* ws = nullptr;
+  size_t bytes = 0;
+  if (hipError_t e = fce::static_scratch(&ws, &bytes); e != hipSuccess) return from_hip(e);
+  return fused_impl(X, W, labels, N, H, V, dtype, opt, true, loss, dX, dW, ws, bytes, stream);
+}
+
 fce_status fce_scale_grads(float* dX, int64_t n_dx, float* dW, int64_t n_dw,
                            const float* grad_loss, hipStream_t stream) {
   if (n_dx < 0 || n_dw < 0) return FCE_ERR_SHAPE;

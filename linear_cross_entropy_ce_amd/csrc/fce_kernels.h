@@ -74,6 +74,10 @@ struct CeLogitsCall {
 };
 hipError_t launch_ce_logits(const CeLogitsCall& c, hipStream_t st, KernelTimer* timer);
 
+// The current device's copy of the library's static scratch
+// (FCE_STATIC_SCRATCH_BYTES), looked up on the first call per device.
+hipError_t static_scratch(void** ptr, size_t* bytes);
+
 // dX[0 .. n_dx) and dW[0 .. n_dw) multiplied in place by the device scalar g.
 hipError_t launch_scale_grads(float* dX, int64_t n_dx, float* dW, int64_t n_dw, const float* g,
                               hipStream_t st, KernelTimer* timer);

@@ -308,3 +308,25 @@ def test_autograd_wrapper_rejects_bad_variants_before_any_call():
         fce.linear_cross_entropy(X, W, y, variant="store_logits", reduction="none")
     with pytest.raises(ValueError):
         fce.linear_cross_entropy(X, W, y, variant="bogus")
+
+
+def test_noalloc_rejects_oversized_problems_before_touching_the_device():
+    lib = B.load_library()
+    o = B.make_options(chunk=8192)
+    # 8192 x 4096 x 128256 at chunk 8192 needs far more than the static scratch
+    assert lib.fce_workspace_size_ex(8192, 4096, 128256, 1, ctypes.byref(o)) > B.STATIC_SCRATCH_BYTES
+    assert lib.fce_fused_fwd_bwd_noalloc(FAKE, FAKE, FAKE, 8192, 4096, 128256, 1, ctypes.byref(o),
+                                         FAKE, FAKE, FAKE, None) == B.FCE_ERR_WORKSPACE
+    # argument errors keep their own codes
+    assert lib.fce_fused_fwd_bwd_noalloc(FAKE, FAKE, FAKE, -1, 64, 100, 1, ctypes.byref(o),
+                                         FAKE, FAKE, FAKE, None) == B.FCE_ERR_SHAPE
+    assert lib.fce_fused_fwd_bwd_noalloc(FAKE, FAKE, FAKE, 64, 64, 100, 1, None,
+                                         FAKE, FAKE, FAKE, None) == B.FCE_ERR_NULL
+    assert lib.fce_fused_fwd_bwd_noalloc(FAKE, FAKE, FAKE, 64, 64, 100, 5, ctypes.byref(o),
+                                         FAKE, FAKE, FAKE, None) == B.FCE_ERR_ARG
+
+
+def test_static_scratch_size_matches_header():
+    text = open(os.path.join(ROOT, "include", "fce.h")).read()
+    m = re.search(r"#define FCE_STATIC_SCRATCH_BYTES \(\(size_t\)(\d+) << (\d+)\)", text)
+    assert m and int(m.group(1)) << int(m.group(2)) == B.STATIC_SCRATCH_BYTES
