@@ -922,22 +922,24 @@ __device__ __forceinline__ void store_grad_tile_staged_t(const Acc<C>& acc, floa
   }
 }
 
-// TRANS: the tile is (out)^T, out element (n, m) at out + n ldo + m (the dW
-// product computed as X^T dZ).
-template <class C, bool A_KMAJOR, bool FILTER, bool TRANS = false>
-__global__ __launch_bounds__(C::NT) void k_bwd_grad(GradArgs<typename C::Elem> a) {
+// One output tile of a gradient product: tile `bid` of the product's grid
+// (tm_tiles x tn_tiles, in the XCD-aware order) and split z of nz over the
+// contraction.  TRANS: the tile is (out)^T, out element (n, m) at
+// out + n ldo + m (the dW product computed as X^T dZ).
+template <class C, bool A_KMAJOR, bool FILTER, bool TRANS>
+__device__ __forceinline__ void grad_tile(const GradArgs<typename C::Elem>& a, int bid, int z,
+                                          int nz, const DmaStages& lds) {
   typedef typename C::Elem T;
-  FCE_DMA_STAGES(lds);
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave / C::WAVES_N, wn = wave % C::WAVES_N;
   int tm, tn;
   if (FILTER && a.kcount[a.korder[0]] != a.kcount[a.korder[a.tm_tiles - 1]]) {
     // rows of unequal length: the longest first, in dispatch order
-    tm = a.korder[blockIdx.x / a.tn_tiles];
-    tn = blockIdx.x % a.tn_tiles;
+    tm = a.korder[bid / a.tn_tiles];
+    tn = bid % a.tn_tiles;
   } else {
-    grouped_tile(xcd_remap(blockIdx.x, a.tm_tiles * a.tn_tiles), a.tm_tiles, a.tn_tiles,
-                 a.group_m, tm, tn);
+    grouped_tile(xcd_remap(bid, a.tm_tiles * a.tn_tiles), a.tm_tiles, a.tn_tiles, a.group_m, tm,
+                 tn);
   }
   const int m0 = tm * C::BM, n0 = tn * C::BN;
   const bool skip = (*a.flag == 0);  // all labels of the token block ignored: dZ = 0
@@ -945,12 +947,12 @@ __global__ __launch_bounds__(C::NT) void k_bwd_grad(GradArgs<typename C::Elem> a
   Opnd<T> A = a.A, B = a.B;
   int K = a.K;
   float* out = a.out;
-  if (gridDim.y > 1) {
-    const int k0 = static_cast<int>(blockIdx.y) * a.ksplit;
+  if (nz > 1) {
+    const int k0 = z * a.ksplit;
     A = opnd_from_k<A_KMAJOR>(A, k0);
     B = opnd_from_k<false>(B, k0);
     K = min(a.ksplit, a.K - k0);
-    out += static_cast<int64_t>(blockIdx.y) * a.split_stride;
+    out += static_cast<int64_t>(z) * a.split_stride;
   }
   Acc<C> acc;
   if constexpr (FILTER) {
@@ -1024,6 +1026,33 @@ __global__ __launch_bounds__(C::NT) void k_bwd_grad(GradArgs<typename C::Elem> a
             tile[TRANS ? static_cast<int64_t>(c) * a.ldo + r : static_cast<int64_t>(r) * a.ldo + c] =
                 old[j][fn][i] + s * acc.v[f0 + j][fn][i];
         }
+  }
+}
+
+// One gradient product: a grid of tm_tiles x tn_tiles workgroups, by nz
+// splits of the contraction along y.
+template <class C, bool A_KMAJOR, bool FILTER, bool TRANS = false>
+__global__ __launch_bounds__(C::NT) void k_bwd_grad(GradArgs<typename C::Elem> a) {
+  FCE_DMA_STAGES(lds);
+  grad_tile<C, A_KMAJOR, FILTER, TRANS>(a, blockIdx.x, blockIdx.y, gridDim.y, lds);
+}
+
+// Both gradient products of one logit block in one launch (bf16): they read
+// the same dZ block and write disjoint outputs, so their tiles share one
+// grid.  Workgroups [0, n_dw) are dW tiles; the rest are dX tiles, split z
+// of dx_splits over the vocabulary taking n_dx consecutive ids.  One grid
+// lets the ragged last wave of either product fill with the other's tiles,
+// and leaves one launch boundary per block instead of two.
+template <class C, bool DW_KMAJOR, bool DW_TRANS>
+__global__ __launch_bounds__(C::NT) void k_bwd_grad_pair(GradArgs<bf16> gw, GradArgs<bf16> gx,
+                                                         int n_dw, int n_dx, int dx_splits) {
+  FCE_DMA_STAGES(lds);
+  const int b = blockIdx.x;
+  if (b < n_dw) {
+    grad_tile<C, DW_KMAJOR, false, DW_TRANS>(gw, b, 0, 1, lds);
+  } else {
+    const int r = b - n_dw;
+    grad_tile<C, true, false, false>(gx, r % n_dx, r / n_dx, dx_splits, lds);
   }
 }
 
@@ -1411,7 +1440,7 @@ hipError_t grad_products(const Plan& p, const T* X, const T* W, const T* dz, int
                          const Ctrl* ctrl, const int32_t* flag, float* dX, float* dW,
                          float* dxpart, const FilterLists* fl, const T* Xt, int64_t ldxt,
                          hipStream_t st, KernelTimer* timer, const char* name_dw,
-                         const char* name_dx) {
+                         const char* name_dx, const char* name_pair) {
   typedef typename ShapeOf<T>::C C;
   const int64_t H = p.H;
   const int h_tiles = cdiv_i(H, C::BN);
@@ -1460,20 +1489,6 @@ hipError_t grad_products(const Plan& p, const T* X, const T* W, const T* dz, int
     // vocabulary rows of dZ^T X (6.48 against 6.56 ms at 8192 x 4096 x 12288)
     gt.group_m = 4;
   }
-  timer->begin(name_dw, blk_flops, st);
-  if constexpr (sizeof(T) == 2) {
-    if (fl)
-      k_bwd_grad<C, false, true><<<voc_tiles * h_tiles, C::NT, 0, st>>>(gw);
-    else if (Xt != nullptr)
-      k_bwd_grad<C, true, false, true><<<voc_tiles * h_tiles, C::NT, 0, st>>>(gt);
-    else
-      k_bwd_grad<C, false, false><<<voc_tiles * h_tiles, C::NT, 0, st>>>(gw);
-  } else {
-    k_bwd_grad<C, false, false><<<voc_tiles * h_tiles, C::NT, 0, st>>>(gw);
-  }
-  FCE_CHECK_LAUNCH();
-  timer->end(st);
-
   // dX[tok0 : tok0+ntok] (=|+=) s * dZ W[voc0 : voc0+nvoc]
   GradArgs<T> gx;
   gx.A = Opnd<T>{dz, ldz, ntok, nvoc_cov};                         // (t, v) at dz[t*ldz + v]
@@ -1504,17 +1519,39 @@ hipError_t grad_products(const Plan& p, const T* X, const T* W, const T* dz, int
     gx.accumulate = 0;
     gx.split_stride = static_cast<int64_t>(ntok) * H;
   }
-  timer->begin(name_dx, blk_flops, st);
+  const int n_dw = voc_tiles * h_tiles, n_dx = tok_tiles * h_tiles;
+  bool paired = false;
   if constexpr (sizeof(T) == 2) {
-    if (fl)
-      k_bwd_grad<C, true, true><<<tok_tiles * h_tiles, C::NT, 0, st>>>(gx);
-    else
-      k_bwd_grad<C, true, false><<<dim3(tok_tiles * h_tiles, splits), C::NT, 0, st>>>(gx);
-  } else {
-    k_bwd_grad<C, true, false><<<dim3(tok_tiles * h_tiles, splits), C::NT, 0, st>>>(gx);
+    if (fl == nullptr) {
+      // one launch for both products (bf16, unfiltered)
+      paired = true;
+      timer->begin(name_pair, 2.0 * blk_flops, st);
+      if (Xt != nullptr)
+        k_bwd_grad_pair<C, true, true><<<n_dw + n_dx * splits, C::NT, 0, st>>>(gt, gx, n_dw, n_dx,
+                                                                               splits);
+      else
+        k_bwd_grad_pair<C, false, false><<<n_dw + n_dx * splits, C::NT, 0, st>>>(gw, gx, n_dw,
+                                                                                 n_dx, splits);
+      FCE_CHECK_LAUNCH();
+      timer->end(st);
+    }
   }
-  FCE_CHECK_LAUNCH();
-  timer->end(st);
+  if (!paired) {
+    timer->begin(name_dw, blk_flops, st);
+    if constexpr (sizeof(T) == 2)
+      k_bwd_grad<C, false, true><<<n_dw, C::NT, 0, st>>>(gw);  // filtered
+    else
+      k_bwd_grad<C, false, false><<<n_dw, C::NT, 0, st>>>(gw);
+    FCE_CHECK_LAUNCH();
+    timer->end(st);
+    timer->begin(name_dx, blk_flops, st);
+    if constexpr (sizeof(T) == 2)
+      k_bwd_grad<C, true, true><<<n_dx, C::NT, 0, st>>>(gx);  // filtered
+    else
+      k_bwd_grad<C, true, false><<<dim3(n_dx, splits), C::NT, 0, st>>>(gx);
+    FCE_CHECK_LAUNCH();
+    timer->end(st);
+  }
   if (splits > 1) {
     timer->begin("dx_reduce", 0.0, st);
     k_dx_reduce<<<1024, 256, 0, st>>>(dxpart, splits, gx.split_stride, dX + tok0 * H, H, ntok,
@@ -1646,7 +1683,7 @@ hipError_t run_backward(const Plan& p, const T* X, const T* W, const int32_t* la
       const hipError_t e = grad_products<T>(p, X, W, dz, p.ldz, tok0, ntok, voc0, nvoc, ia > 0,
                                             ib > 0, ctrl, flags + ia, dX, dW, dxpart,
                                             filt ? &fl : nullptr, xt, p.ldxt, st, timer, "bwd_dw",
-                                            "bwd_dx");
+                                            "bwd_dx", "bwd_grad");
       if (e != hipSuccess) return e;
     }
   }
@@ -1717,7 +1754,8 @@ hipError_t run_fused_store(const Plan& p, const T* X, const T* W, const int32_t*
     timer->end(st);
     const hipError_t e = grad_products<T>(p, X, W, zs, p.ldz, tok0, ntok, 0, static_cast<int>(V),
                                           ia > 0, false, ctrl, flags + ia, dX, dW, dxpart,
-                                          nullptr, xt, p.ldxt, st, timer, "sl_dw", "sl_dx");
+                                          nullptr, xt, p.ldxt, st, timer, "sl_dw", "sl_dx",
+                                          "sl_grad");
     if (e != hipSuccess) return e;
   }
   if (none) return hipSuccess;

@@ -28,23 +28,79 @@ size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 int64_t round_up(int64_t a, int64_t b) { return cdiv(a, b) * b; }
 
-// Modelled time of one backward schedule, in seconds: MFMA work of the
-// three products with each grid rounded up to whole waves over the CUs, plus
-// the fp32 read-modify-write bytes of dW and dX.  Only the ranking of
-// candidates matters.  Blocks are full except the last in each dimension,
-// so four block shapes cover the whole schedule.
+}  // namespace
+
+int64_t dx_split_count(int64_t tok_tiles, int64_t voc_tiles, int64_t h_tiles) {
+  constexpr int64_t kMinSplitTiles = 4;
+  const int64_t n_dw = voc_tiles * h_tiles, n_dx = tok_tiles * h_tiles;
+  if (n_dw + n_dx >= kNumCUs) return 1;
+  return std::max<int64_t>(1, std::min(cdiv(kNumCUs - n_dw, n_dx), voc_tiles / kMinSplitTiles));
+}
+
+namespace {
+
+// Makespan of n1 equal jobs of length l1 followed by n2 of length l2, each
+// started in order on the first of P workers to come free: how the hardware
+// fills the CUs with the workgroups of one grid.  The first run takes
+// floor(n1 / P) full rounds plus a partial one; the second run's jobs are
+// identical, so it ends at the first time M by which the workers, from the
+// times they come free, can have finished n2 of them.
+double two_run_makespan(int64_t n1, double l1, int64_t n2, double l2, int64_t P) {
+  const int64_t r1 = n1 / P, rem1 = n1 % P;
+  const double ta = static_cast<double>(r1) * l1;                     // P - rem1 workers free
+  const double tb = static_cast<double>(r1 + (rem1 > 0 ? 1 : 0)) * l1;  // rem1 workers free
+  const double end1 = tb;
+  if (n2 <= 0) return end1;
+  const int64_t na = P - rem1, nb = rem1;
+  auto done_by = [&](double M) {
+    const double fa = std::floor((M - ta) / l2 + 1e-9), fb = std::floor((M - tb) / l2 + 1e-9);
+    return static_cast<double>(na) * std::max(0.0, fa) + static_cast<double>(nb) * std::max(0.0, fb);
+  };
+  // the answer is ta + k l2 or tb + k l2 for some k; walk k upward
+  double best = std::numeric_limits<double>::infinity();
+  for (int64_t k = 1; k <= n2 / std::max<int64_t>(na, 1) + 2; ++k) {
+    const double m1 = ta + static_cast<double>(k) * l2;
+    if (done_by(m1) >= static_cast<double>(n2)) best = std::min(best, m1);
+    const double m2 = tb + static_cast<double>(k) * l2;
+    if (nb > 0 && done_by(m2) >= static_cast<double>(n2)) best = std::min(best, m2);
+    if (best < m1) break;
+  }
+  return std::max(end1, best);
+}
+
+// Modelled time of one backward schedule, in seconds, per logit block:
+//  - the dZ stream: `splits` workgroups per token tile, each over up to
+//    ceil(tv / splits) vocabulary tiles of contraction H;
+//  - dW and dX in one grid, dW tiles first (contraction: the block's
+//    tokens), then dX tiles (contraction: its vocabulary columns, split as
+//    dx_split_count says), placed as the hardware places workgroups;
+//  - a fixed cost per launch, the split dX partials' reduce;
+// plus the fp32 read-modify-write bytes of dW and dX across blocks.  Only the
+// ranking of candidates matters.  Blocks are full except the last in each
+// dimension, so four block shapes cover the whole schedule.
 double model_time(const Plan& p, int64_t CN, int64_t CV, int64_t a, int64_t b) {
   const double peak = (p.dtype == Dtype::BF16) ? 2.5e15 : 1.5e14;
   const double bw = 5.0e12;
+  const double launch = 6e-6;  // per kernel launch
   const double t = static_cast<double>(p.tile);
   const double per_cu = peak / kNumCUs;
-  auto waves = [](int64_t tiles) { return static_cast<double>(cdiv(tiles, kNumCUs)); };
   const int64_t h_tiles = cdiv(p.H, p.tile);
+  auto tile_time = [&](double K) { return 2.0 * t * t * K / per_cu; };
   auto block = [&](int64_t cn, int64_t cv) {
     const int64_t tn = cdiv(cn, p.tile), tv = cdiv(cv, p.tile);
-    return waves(tn * tv) * 2.0 * t * t * static_cast<double>(p.H) / per_cu +       // recompute
-           waves(tv * h_tiles) * 2.0 * t * t * static_cast<double>(tn * p.tile) / per_cu +  // dW
-           waves(tn * h_tiles) * 2.0 * t * t * static_cast<double>(tv * p.tile) / per_cu;   // dX
+    const int64_t splits = std::max<int64_t>(1, std::min<int64_t>(tv, kNumCUs / tn));
+    const double t_dz = two_run_makespan(tn * splits, static_cast<double>(cdiv(tv, splits)) *
+                                                          tile_time(static_cast<double>(p.H)),
+                                         0, 0.0, kNumCUs);
+    const int64_t s = dx_split_count(tn, tv, h_tiles);
+    const double k_dw = static_cast<double>(tn * p.tile);
+    const double k_dx = static_cast<double>(tv * p.tile) / static_cast<double>(s);
+    const double t_grad = two_run_makespan(tv * h_tiles, tile_time(k_dw), tn * h_tiles * s,
+                                           tile_time(k_dx), kNumCUs);
+    const double reduce = (s > 1) ? launch + 4.0 * static_cast<double>(cn * p.H) *
+                                                 static_cast<double>(s + 2) / bw
+                                  : 0.0;
+    return t_dz + t_grad + 2.0 * launch + reduce;
   };
   const int64_t cn_last = p.N - (a - 1) * CN, cv_last = p.V - (b - 1) * CV;
   const double time = static_cast<double>((a - 1) * (b - 1)) * block(CN, CV) +
@@ -193,16 +249,12 @@ bool make_plan(int64_t N, int64_t H, int64_t V, Dtype dtype, int64_t chunk, Sche
   // by one 128-byte line.
   p.ldz = p.CV;
   if ((p.ldz * p.elem_bytes) % 1024 == 0) p.ldz += 128 / p.elem_bytes;
-  // ---- dX split: enough splits to fill the CUs with one wave, each at
-  // least kMinSplitTiles vocabulary tiles long
-  if (N > 0) {
-    constexpr int64_t kMinSplitTiles = 4;
-    const int64_t grid = cdiv(std::min(p.CN, N), BN) * cdiv(H, BN);
-    const int64_t ktiles = cdiv(std::min(p.CV, V), BM);
-    if (grid < kNumCUs && variant != Variant::Filtered)
-      p.dx_splits = std::max<int64_t>(
-          1, std::min(cdiv(kNumCUs, grid), ktiles / kMinSplitTiles));
-  }
+  // ---- dX split: when the dW and dX grids of a block together fill less
+  // than one wave of the CUs, enough splits of dX over the vocabulary to
+  // fill it, each at least four vocabulary tiles long
+  if (N > 0 && variant != Variant::Filtered)
+    p.dx_splits = dx_split_count(cdiv(std::min(p.CN, N), BN), cdiv(std::min(p.CV, V), BM),
+                                 cdiv(H, BN));
   p.grad_rmw_bytes = (N == 0) ? 4 * V * H
                               : 4 * V * H * (2 * p.a - 1) + 4 * N * H * (2 * p.b - 1);
   if (store && N > 0) p.grad_rmw_bytes = 4 * V * H * (2 * p.a - 1) + 4 * N * H;

@@ -72,6 +72,11 @@ constexpr int kLossBlock = 256;  // tokens per block of the loss reduction
 constexpr size_t kOffFilterStats = 64;
 static_assert(sizeof(Ctrl) <= kOffFilterStats, "filter counters after the control block");
 
+// Splits of the dX product over the vocabulary for a logit block of
+// tok_tiles x voc_tiles tiles: the dW and dX tiles of a block share one
+// grid, and dX is split only when that grid is under one wave of the CUs.
+int64_t dx_split_count(int64_t tok_tiles, int64_t voc_tiles, int64_t h_tiles);
+
 // Returns false if the arguments are invalid (shapes, chunk, overflow).
 bool make_plan(int64_t N, int64_t H, int64_t V, Dtype dtype, int64_t chunk, Schedule sched,
                Plan* out, Variant variant = Variant::Recompute);

@@ -62,6 +62,9 @@ def _flags(name: str) -> list[bool]:
 
 def kernel_key(name: str) -> str | None:
     """Map a (mangled or demangled) kernel name to the library's timer name."""
+    if "k_bwd_grad_pair" in name:
+        # both gradient products of a logit block in one launch
+        return "bwd_grad"
     if "k_bwd_grad" in name:
         # flags A_KMAJOR, FILTER, TRANS: dX has a K-major A (dZ); dW has an
         # M-major one (dZ^T), or is the transposed product X^T dZ (TRANS)

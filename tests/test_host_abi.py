@@ -117,15 +117,17 @@ def test_plan_invariants(N, H, V, dtype, chunk, sched):
         if sched == "vocab":
             assert a == 1
     assert p["grad_rmw_bytes"] == 4 * V * H * (2 * a - 1) + 4 * N * H * (2 * b - 1)
-    # the dX product splits over V only when its grid is under one wave of
-    # 256 CUs, then with enough splits to fill it, each at least 4 tiles long
-    grid = -(-min(CN, N) // tile) * -(-H // tile)
+    # the dW and dX tiles of a block share one grid; dX splits over V only
+    # when that grid is under one wave of 256 CUs, then with enough splits
+    # to fill it, each at least 4 tiles long
+    n_dx = -(-min(CN, N) // tile) * -(-H // tile)
     ktiles = -(-min(CV, V) // tile)
+    n_dw = ktiles * -(-H // tile)
     S = p["dx_splits"]
-    if grid >= 256 or ktiles < 8:
+    if n_dw + n_dx >= 256 or ktiles < 8:
         assert S == 1
     else:
-        assert S == min(-(-256 // grid), ktiles // 4)
+        assert S == max(1, min(-(-(256 - n_dw) // n_dx), ktiles // 4))
     dxpart = S * min(CN, N) * H * 4 if S > 1 else 0
     assert p["workspace_bytes"] >= p["scratch_bytes"] + p["partial_bytes"] + dxpart
 

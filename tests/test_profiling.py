@@ -18,6 +18,9 @@ MANGLED = {
     f"void fce::(anonymous namespace)::k_bwd_grad<{_DEM}, true, false>(GradArgs<__bf16>)": "bwd_dx",
     f"void fce::(anonymous namespace)::k_bwd_grad<{_DEM}, false, true>(GradArgs<__bf16>)": "bwd_dw",
     f"_ZN3fce12_GLOBAL__N_18k_bwd_dz{_CFG}Lb1ELb0EEEvNS0_6DzArgsINT_4ElemEEE": "bwd_dz",
+    # k_bwd_grad_pair<C, DW_KMAJOR, DW_TRANS>: dW and dX of a block in one grid
+    f"_ZN3fce12_GLOBAL__N_115k_bwd_grad_pair{_CFG}Lb1ELb1EEEvNS0_8GradArgsIDF16bEES7_iii": "bwd_grad",
+    f"void fce::(anonymous namespace)::k_bwd_grad_pair<{_DEM}, false, false>(GradArgs<__bf16>, GradArgs<__bf16>, int, int, int)": "bwd_grad",
     # k_fwd_lse<C, SMOOTH, STORE>: the storing one belongs to store-logits
     f"_ZN3fce12_GLOBAL__N_19k_fwd_lse{_CFG}Lb1ELb0EEEvNS0_7FwdArgsINT_4ElemEEE": "fwd_lse",
     f"_ZN3fce12_GLOBAL__N_19k_fwd_lse{_CFG}Lb0ELb1EEEvNS0_7FwdArgsINT_4ElemEEE": "sl_fwd",
