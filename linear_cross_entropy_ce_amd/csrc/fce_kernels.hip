@@ -1141,6 +1141,12 @@ constexpr int kCeUnroll = 4;  // 16-byte loads in flight per thread
 // 160 KiB), so pass 2 reads only the rest from memory again: 62% of a
 // 128256-column bf16 row.
 constexpr int kCeCache = 10112;
+// Rows of at most kCeResidentVecs vectors (bf16: 131072 columns) stay on chip
+// whole between the passes: thread t's vectors t + 1024 i sit in LDS for
+// i < kCeLdsIters (144 KiB) and in registers for the next kCeRegIters (28
+// VGPRs), so pass 2 reads no memory.
+constexpr int kCeLdsIters = 9, kCeRegIters = 7;
+constexpr int kCeResidentVecs = (kCeLdsIters + kCeRegIters) * kCeThreads;
 
 template <typename T>
 struct CeVec;
@@ -1195,19 +1201,24 @@ struct CeArgs {
 };
 
 // NC: vectors of the row kept in LDS between the passes (0: none, for the
-// loss alone, whose workgroups then overlap at row boundaries).
+// loss alone, whose workgroups then overlap at row boundaries).  RC > 0: the
+// whole row stays on chip (NC = kCeLdsIters x kCeThreads vectors in LDS, RC
+// per thread in registers; the row has at most NC + RC x kCeThreads vectors)
+// and both passes walk it with compile-time indices.
 // GIVEN: lse holds each valid row's LSE already (the store-logits variant,
 // whose forward computed it from the fp32 accumulators); only pass 2 runs,
 // neither lse nor the loss terms are written, and dZ leaves out the scale
 // g / D, which the gradient products apply in fp32 (the per-token g_i of
 // reduction none is kept).
-template <typename T, bool GIVEN, int NC>
+template <typename T, bool GIVEN, int NC, int RC = 0>
 __global__ __launch_bounds__(kCeThreads) void k_ce_logits(CeArgs a) {
+  static_assert(RC == 0 || (!GIVEN && NC % kCeThreads == 0), "resident rows: LDS whole iterations");
   typedef CeVec<T> CV;
   constexpr int E = CV::E;
   __shared__ floatx4 s_part[kCeThreads / 64];
   __shared__ float s_bcast[2];
   __shared__ u32x4 s_cache[NC > 0 ? NC : 1];  // the row's first vectors (pass 1 -> 2)
+  u32x4 rcache[RC > 0 ? RC : 1];               // RC > 0: the rest of the row
   const int row = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int y = a.labels[row];
   const bool valid = label_ok(y, a.ignore, a.V);
@@ -1248,40 +1259,64 @@ __global__ __launch_bounds__(kCeThreads) void k_ce_logits(CeArgs a) {
     // pass 1: running (max, sum-exp, sum z) of this thread's vectors
     float m = -INFINITY, l = 0.0f, zs = 0.0f;
     const bool smooth = a.eps != 0.0f;
-    for (int j0 = tid; j0 < nv; j0 += kCeUnroll * kCeThreads) {
-      u32x4 r[kCeUnroll];
+    auto accumulate = [&](const u32x4& rv, int j) {
+      float f[E];
+      CV::unpack(rv, f);
+      const int lim = a.V - j * E;
+      if (lim < E) {
+        if (smooth) {
 #pragma unroll
-      for (int u = 0; u < kCeUnroll; ++u) r[u] = buf_load16(rz, (j0 + u * kCeThreads) * 16);
-#pragma unroll
-      for (int u = 0; u < kCeUnroll; ++u) {
-        if (j0 + u * kCeThreads < NC) s_cache[j0 + u * kCeThreads] = r[u];
-        float f[E];
-        CV::unpack(r[u], f);
-        const int lim = a.V - (j0 + u * kCeThreads) * E;
-        if (lim < E) {
-          if (smooth) {
-#pragma unroll
-            for (int e = 0; e < E; ++e) zs += (e < lim) ? f[e] : 0.0f;
-          }
-          pad(f, lim, -INFINITY);
-        } else if (smooth) {
-#pragma unroll
-          for (int e = 0; e < E; ++e) zs += f[e];
+          for (int e = 0; e < E; ++e) zs += (e < lim) ? f[e] : 0.0f;
         }
-        float vm = f[0];
+        pad(f, lim, -INFINITY);
+      } else if (smooth) {
 #pragma unroll
-        for (int e = 1; e < E; ++e) vm = fmaxf(vm, f[e]);
-        if (vm == -INFINITY) continue;
-        const float mn = fmaxf(m, vm);
-        const float mnl = mn * kLog2e;
-        float acc = 0.0f;
-        // fp32: exp2((z - m) log2e), exact near the max at any |m| (the
-        // one-FMA form carries an error of |m| 2^-25 into every term)
+        for (int e = 0; e < E; ++e) zs += f[e];
+      }
+      float vm = f[0];
 #pragma unroll
-        for (int e = 0; e < E; ++e)
-          acc += hw_exp2((sizeof(T) == 4) ? (f[e] - mn) * kLog2e : fmaf(f[e], kLog2e, -mnl));
-        l = ((m == -INFINITY) ? 0.0f : l * hw_exp2((m - mn) * kLog2e)) + acc;
-        m = mn;
+      for (int e = 1; e < E; ++e) vm = fmaxf(vm, f[e]);
+      if (vm == -INFINITY) return;
+      const float mn = fmaxf(m, vm);
+      const float mnl = mn * kLog2e;
+      float acc = 0.0f;
+      // fp32: exp2((z - m) log2e), exact near the max at any |m| (the
+      // one-FMA form carries an error of |m| 2^-25 into every term)
+#pragma unroll
+      for (int e = 0; e < E; ++e)
+        acc += hw_exp2((sizeof(T) == 4) ? (f[e] - mn) * kLog2e : fmaf(f[e], kLog2e, -mnl));
+      l = ((m == -INFINITY) ? 0.0f : l * hw_exp2((m - mn) * kLog2e)) + acc;
+      m = mn;
+    };
+    if constexpr (RC > 0) {
+      // the whole row: vectors past the row load as zero and are padded out
+#pragma unroll
+      for (int g = 0; g < NC / kCeThreads + RC; g += kCeUnroll) {
+        u32x4 r[kCeUnroll];
+#pragma unroll
+        for (int u = 0; u < kCeUnroll; ++u)
+          if (g + u < NC / kCeThreads + RC) r[u] = buf_load16(rz, (tid + (g + u) * kCeThreads) * 16);
+#pragma unroll
+        for (int u = 0; u < kCeUnroll; ++u) {
+          const int i = g + u;
+          if (i >= NC / kCeThreads + RC) break;
+          if (i < NC / kCeThreads)
+            s_cache[tid + i * kCeThreads] = r[u];
+          else
+            rcache[i - NC / kCeThreads] = r[u];
+          accumulate(r[u], tid + i * kCeThreads);
+        }
+      }
+    } else {
+      for (int j0 = tid; j0 < nv; j0 += kCeUnroll * kCeThreads) {
+        u32x4 r[kCeUnroll];
+#pragma unroll
+        for (int u = 0; u < kCeUnroll; ++u) r[u] = buf_load16(rz, (j0 + u * kCeThreads) * 16);
+#pragma unroll
+        for (int u = 0; u < kCeUnroll; ++u) {
+          if (j0 + u * kCeThreads < NC) s_cache[j0 + u * kCeThreads] = r[u];
+          accumulate(r[u], j0 + u * kCeThreads);
+        }
       }
     }
     // wave, then fixed-order workgroup merge of (m, l, sum z)
@@ -1323,33 +1358,41 @@ __global__ __launch_bounds__(kCeThreads) void k_ce_logits(CeArgs a) {
   const float gy = (1.0f - a.eps) * scale;
   const float Ll = L * kLog2e;
   const int jy = y / E, ey = y % E;
-  for (int j0 = tid; j0 < nv; j0 += kCeUnroll * kCeThreads) {
-    u32x4 r[kCeUnroll];
+  auto emit = [&](const u32x4& rv, int j) {
+    float f[E];
+    CV::unpack(rv, f);
+    // fp32: exp2((z - m) log2e - log2 l), exact near the max at any |LSE|;
+    // bf16 logits carry far coarser rounding and keep the one-FMA form
 #pragma unroll
-    for (int u = 0; u < kCeUnroll; ++u) {
-      const int j = j0 + u * kCeThreads;
-      r[u] = (j < NC) ? s_cache[j] : buf_load16(rz, j * 16);
+    for (int e = 0; e < E; ++e) {
+      const float x = (sizeof(T) == 4) ? fmaf(f[e] - m_row, kLog2e, -lg_row)
+                                       : fmaf(f[e], kLog2e, -Ll);
+      f[e] = fmaf(hw_exp2(x), ga, -gb);
     }
+    if (j == jy) {  // the one lane holding the label
 #pragma unroll
-    for (int u = 0; u < kCeUnroll; ++u) {
-      const int j = j0 + u * kCeThreads;
-      float f[E];
-      CV::unpack(r[u], f);
-      // fp32: exp2((z - m) log2e - log2 l), exact near the max at any |LSE|;
-      // bf16 logits carry far coarser rounding and keep the one-FMA form
+      for (int e = 0; e < E; ++e) f[e] -= (e == ey) ? gy : 0.0f;
+    }
+    const int lim = a.V - j * E;
+    if (lim < E) pad(f, lim, 0.0f);
+    __builtin_amdgcn_raw_buffer_store_b128(CV::pack(f), rd, j * 16, 0, 0);
+  };
+  if constexpr (RC > 0) {
+    // from LDS and registers only; stores past the row are dropped
 #pragma unroll
-      for (int e = 0; e < E; ++e) {
-        const float x = (sizeof(T) == 4) ? fmaf(f[e] - m_row, kLog2e, -lg_row)
-                                         : fmaf(f[e], kLog2e, -Ll);
-        f[e] = fmaf(hw_exp2(x), ga, -gb);
+    for (int i = 0; i < NC / kCeThreads + RC; ++i)
+      emit(i < NC / kCeThreads ? s_cache[tid + i * kCeThreads] : rcache[i - NC / kCeThreads],
+           tid + i * kCeThreads);
+  } else {
+    for (int j0 = tid; j0 < nv; j0 += kCeUnroll * kCeThreads) {
+      u32x4 r[kCeUnroll];
+#pragma unroll
+      for (int u = 0; u < kCeUnroll; ++u) {
+        const int j = j0 + u * kCeThreads;
+        r[u] = (j < NC) ? s_cache[j] : buf_load16(rz, j * 16);
       }
-      if (j == jy) {  // the one lane holding the label
 #pragma unroll
-        for (int e = 0; e < E; ++e) f[e] -= (e == ey) ? gy : 0.0f;
-      }
-      const int lim = a.V - j * E;
-      if (lim < E) pad(f, lim, 0.0f);
-      __builtin_amdgcn_raw_buffer_store_b128(CV::pack(f), rd, j * 16, 0, 0);
+      for (int u = 0; u < kCeUnroll; ++u) emit(r[u], j0 + u * kCeThreads);
     }
   }
 }
@@ -1850,7 +1893,9 @@ hipError_t launch_ce_logits(const CeLogitsCall& c, hipStream_t st, KernelTimer* 
              static_cast<int>(c.o.reduction), c.o.eps, c.o.zloss, none ? c.grad : nullptr,
              ctrl, c.lse, none ? c.loss : rowloss, nullptr};
     timer->begin("ce_logits", 0.0, st);
-    if (c.bf16 && c.dZ)
+    if (c.bf16 && c.dZ && (V + 7) / 8 <= kCeResidentVecs)
+      k_ce_logits<bf16, false, kCeLdsIters * kCeThreads, kCeRegIters><<<N, kCeThreads, 0, st>>>(a);
+    else if (c.bf16 && c.dZ)
       k_ce_logits<bf16, false, kCeCache><<<N, kCeThreads, 0, st>>>(a);
     else if (c.bf16)
       k_ce_logits<bf16, false, 0><<<N, kCeThreads, 0, st>>>(a);
