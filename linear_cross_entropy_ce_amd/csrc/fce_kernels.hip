@@ -1358,7 +1358,11 @@ __global__ __launch_bounds__(kCeThreads) void k_ce_logits(CeArgs a) {
   const float gy = (1.0f - a.eps) * scale;
   const float Ll = L * kLog2e;
   const int jy = y / E, ey = y % E;
-  auto emit = [&](const u32x4& rv, int j) {
+  // One vector j.  PLAIN (workgroup-uniform): the iteration holds neither
+  // the label's vector nor one past the row's whole vectors, so it needs no
+  // one-hot term and no tail mask.
+  const int nvf = a.V / E;
+  auto emit = [&](const u32x4& rv, int j, int first) {
     float f[E];
     CV::unpack(rv, f);
     // fp32: exp2((z - m) log2e - log2 l), exact near the max at any |LSE|;
@@ -1369,12 +1373,15 @@ __global__ __launch_bounds__(kCeThreads) void k_ce_logits(CeArgs a) {
                                        : fmaf(f[e], kLog2e, -Ll);
       f[e] = fmaf(hw_exp2(x), ga, -gb);
     }
-    if (j == jy) {  // the one lane holding the label
+    const bool plain = first + kCeThreads <= nvf && (jy < first || jy >= first + kCeThreads);
+    if (!plain) {
+      if (j == jy) {  // the one lane holding the label
 #pragma unroll
-      for (int e = 0; e < E; ++e) f[e] -= (e == ey) ? gy : 0.0f;
+        for (int e = 0; e < E; ++e) f[e] -= (e == ey) ? gy : 0.0f;
+      }
+      const int lim = a.V - j * E;
+      if (lim < E) pad(f, lim, 0.0f);
     }
-    const int lim = a.V - j * E;
-    if (lim < E) pad(f, lim, 0.0f);
     __builtin_amdgcn_raw_buffer_store_b128(CV::pack(f), rd, j * 16, 0, 0);
   };
   if constexpr (RC > 0) {
@@ -1382,7 +1389,7 @@ __global__ __launch_bounds__(kCeThreads) void k_ce_logits(CeArgs a) {
 #pragma unroll
     for (int i = 0; i < NC / kCeThreads + RC; ++i)
       emit(i < NC / kCeThreads ? s_cache[tid + i * kCeThreads] : rcache[i - NC / kCeThreads],
-           tid + i * kCeThreads);
+           tid + i * kCeThreads, i * kCeThreads);
   } else {
     for (int j0 = tid; j0 < nv; j0 += kCeUnroll * kCeThreads) {
       u32x4 r[kCeUnroll];
@@ -1392,7 +1399,8 @@ __global__ __launch_bounds__(kCeThreads) void k_ce_logits(CeArgs a) {
         r[u] = (j < NC) ? s_cache[j] : buf_load16(rz, j * 16);
       }
 #pragma unroll
-      for (int u = 0; u < kCeUnroll; ++u) emit(r[u], j0 + u * kCeThreads);
+      for (int u = 0; u < kCeUnroll; ++u)
+        emit(r[u], j0 + u * kCeThreads, j0 - tid + u * kCeThreads);
     }
   }
 }
