@@ -1039,19 +1039,23 @@ __global__ __launch_bounds__(C::NT) void k_bwd_grad(GradArgs<typename C::Elem> a
 
 // Both gradient products of one logit block in one launch (bf16): they read
 // the same dZ block and write disjoint outputs, so their tiles share one
-// grid.  Workgroups [0, n_dw) are dW tiles; the rest are dX tiles, split z
-// of dx_splits over the vocabulary taking n_dx consecutive ids.  One grid
+// grid.  The dW tiles take n_dw consecutive workgroup ids and the dX tiles
+// n_dx per split z of dx_splits over the vocabulary; the longer kind of tile
+// comes first (dx_first), so the short ones fill in behind it.  One grid
 // lets the ragged last wave of either product fill with the other's tiles,
 // and leaves one launch boundary per block instead of two.
 template <class C, bool DW_KMAJOR, bool DW_TRANS>
 __global__ __launch_bounds__(C::NT) void k_bwd_grad_pair(GradArgs<bf16> gw, GradArgs<bf16> gx,
-                                                         int n_dw, int n_dx, int dx_splits) {
+                                                         int n_dw, int n_dx, int dx_splits,
+                                                         int dx_first) {
   FCE_DMA_STAGES(lds);
   const int b = blockIdx.x;
-  if (b < n_dw) {
-    grad_tile<C, DW_KMAJOR, false, DW_TRANS>(gw, b, 0, 1, lds);
+  const int n_x = n_dx * dx_splits;
+  const bool is_dw = dx_first ? b >= n_x : b < n_dw;
+  if (is_dw) {
+    grad_tile<C, DW_KMAJOR, false, DW_TRANS>(gw, dx_first ? b - n_x : b, 0, 1, lds);
   } else {
-    const int r = b - n_dw;
+    const int r = dx_first ? b : b - n_dw;
     grad_tile<C, true, false, false>(gx, r % n_dx, r / n_dx, dx_splits, lds);
   }
 }
@@ -1574,15 +1578,17 @@ hipError_t grad_products(const Plan& p, const T* X, const T* W, const T* dz, int
   bool paired = false;
   if constexpr (sizeof(T) == 2) {
     if (fl == nullptr) {
-      // one launch for both products (bf16, unfiltered)
+      // one launch for both products (bf16, unfiltered); the tiles with the
+      // longer contraction first
       paired = true;
+      const int dx_first = (splits > 1 ? ksplit : nvoc_cov) > (Xt != nullptr ? gt.K : gw.K);
       timer->begin(name_pair, 2.0 * blk_flops, st);
       if (Xt != nullptr)
         k_bwd_grad_pair<C, true, true><<<n_dw + n_dx * splits, C::NT, 0, st>>>(gt, gx, n_dw, n_dx,
-                                                                               splits);
+                                                                               splits, dx_first);
       else
-        k_bwd_grad_pair<C, false, false><<<n_dw + n_dx * splits, C::NT, 0, st>>>(gw, gx, n_dw,
-                                                                                 n_dx, splits);
+        k_bwd_grad_pair<C, false, false><<<n_dw + n_dx * splits, C::NT, 0, st>>>(
+            gw, gx, n_dw, n_dx, splits, dx_first);
       FCE_CHECK_LAUNCH();
       timer->end(st);
     }

@@ -28,17 +28,6 @@ size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 int64_t round_up(int64_t a, int64_t b) { return cdiv(a, b) * b; }
 
-}  // namespace
-
-int64_t dx_split_count(int64_t tok_tiles, int64_t voc_tiles, int64_t h_tiles) {
-  constexpr int64_t kMinSplitTiles = 4;
-  const int64_t n_dw = voc_tiles * h_tiles, n_dx = tok_tiles * h_tiles;
-  if (n_dw + n_dx >= kNumCUs) return 1;
-  return std::max<int64_t>(1, std::min(cdiv(kNumCUs - n_dw, n_dx), voc_tiles / kMinSplitTiles));
-}
-
-namespace {
-
 // Makespan of n1 equal jobs of length l1 followed by n2 of length l2, each
 // started in order on the first of P workers to come free: how the hardware
 // fills the CUs with the workgroups of one grid.  The first run takes
@@ -68,39 +57,73 @@ double two_run_makespan(int64_t n1, double l1, int64_t n2, double l2, int64_t P)
   return std::max(end1, best);
 }
 
+constexpr double kLaunchSeconds = 6e-6;  // per kernel launch
+constexpr double kRmwBandwidth = 5.0e12;  // fp32 read-modify-write, bytes per second
+
+// Time of one bf16 or fp32 output tile of the engine with contraction K.
+double tile_seconds(Dtype dtype, double tile, double K) {
+  const double peak = (dtype == Dtype::BF16) ? 2.5e15 : 1.5e14;
+  return 2.0 * tile * tile * K / (peak / kNumCUs);
+}
+
+}  // namespace
+
+// The dW and dX grids of a logit block of tok_tiles x voc_tiles tiles share
+// one launch.  dX may be split s ways over the vocabulary (fp32 partials
+// [s][block tokens][H], then a fixed-order reduce): s is the count with the
+// shortest modelled time, the longer of the two tile kinds going first in the
+// grid (longest first), and the partials no larger than the dZ block.
+GradSchedule grad_schedule(Dtype dtype, int64_t H, int64_t tile, int64_t tok_tiles,
+                           int64_t voc_tiles) {
+  const int64_t h_tiles = cdiv(H, tile);
+  const double t = static_cast<double>(tile);
+  const double l_dw = tile_seconds(dtype, t, static_cast<double>(tok_tiles * tile));
+  const int64_t elem = (dtype == Dtype::BF16) ? 2 : 4;
+  const int64_t smax = std::max<int64_t>(1, std::min<int64_t>(voc_tiles / 4, 16));
+  GradSchedule best{1, false, std::numeric_limits<double>::infinity()};
+  for (int64_t s = 1; s <= smax; ++s) {
+    if (s > 1 && s * 4 * H > voc_tiles * tile * elem) break;  // partials <= the dZ block
+    const int64_t ksplit = cdiv(cdiv(voc_tiles, s), 1) * tile;  // whole tiles per split
+    const int64_t splits = cdiv(voc_tiles * tile, ksplit);
+    if (splits != s) continue;
+    const double l_dx = tile_seconds(dtype, t, static_cast<double>(ksplit));
+    const int64_t n_dw = voc_tiles * h_tiles, n_dx = tok_tiles * h_tiles * s;
+    const bool dx_first = l_dx > l_dw;
+    double time = dx_first ? two_run_makespan(n_dx, l_dx, n_dw, l_dw, kNumCUs)
+                           : two_run_makespan(n_dw, l_dw, n_dx, l_dx, kNumCUs);
+    if (s > 1)
+      time += kLaunchSeconds + 4.0 * static_cast<double>(tok_tiles * tile * H) *
+                                   static_cast<double>(s + 2) / kRmwBandwidth;
+    if (time < best.seconds * (1.0 - 1e-9)) best = GradSchedule{s, dx_first, time};
+  }
+  return best;
+}
+
+namespace {
+
 // Modelled time of one backward schedule, in seconds, per logit block:
 //  - the dZ stream: `splits` workgroups per token tile, each over up to
 //    ceil(tv / splits) vocabulary tiles of contraction H;
-//  - dW and dX in one grid, dW tiles first (contraction: the block's
-//    tokens), then dX tiles (contraction: its vocabulary columns, split as
-//    dx_split_count says), placed as the hardware places workgroups;
-//  - a fixed cost per launch, the split dX partials' reduce;
+//  - dW and dX in one grid (contractions: the block's tokens, and its
+//    vocabulary columns split as grad_schedule says), the longer tiles
+//    first, placed as the hardware places workgroups, plus the split dX
+//    partials' reduce;
+//  - a fixed cost per launch;
 // plus the fp32 read-modify-write bytes of dW and dX across blocks.  Only the
 // ranking of candidates matters.  Blocks are full except the last in each
 // dimension, so four block shapes cover the whole schedule.
 double model_time(const Plan& p, int64_t CN, int64_t CV, int64_t a, int64_t b) {
-  const double peak = (p.dtype == Dtype::BF16) ? 2.5e15 : 1.5e14;
-  const double bw = 5.0e12;
-  const double launch = 6e-6;  // per kernel launch
+  const double bw = kRmwBandwidth;
   const double t = static_cast<double>(p.tile);
-  const double per_cu = peak / kNumCUs;
-  const int64_t h_tiles = cdiv(p.H, p.tile);
-  auto tile_time = [&](double K) { return 2.0 * t * t * K / per_cu; };
   auto block = [&](int64_t cn, int64_t cv) {
     const int64_t tn = cdiv(cn, p.tile), tv = cdiv(cv, p.tile);
     const int64_t splits = std::max<int64_t>(1, std::min<int64_t>(tv, kNumCUs / tn));
-    const double t_dz = two_run_makespan(tn * splits, static_cast<double>(cdiv(tv, splits)) *
-                                                          tile_time(static_cast<double>(p.H)),
-                                         0, 0.0, kNumCUs);
-    const int64_t s = dx_split_count(tn, tv, h_tiles);
-    const double k_dw = static_cast<double>(tn * p.tile);
-    const double k_dx = static_cast<double>(tv * p.tile) / static_cast<double>(s);
-    const double t_grad = two_run_makespan(tv * h_tiles, tile_time(k_dw), tn * h_tiles * s,
-                                           tile_time(k_dx), kNumCUs);
-    const double reduce = (s > 1) ? launch + 4.0 * static_cast<double>(cn * p.H) *
-                                                 static_cast<double>(s + 2) / bw
-                                  : 0.0;
-    return t_dz + t_grad + 2.0 * launch + reduce;
+    const double t_dz = two_run_makespan(
+        tn * splits,
+        static_cast<double>(cdiv(tv, splits)) * tile_seconds(p.dtype, t, static_cast<double>(p.H)),
+        0, 0.0, kNumCUs);
+    const GradSchedule g = grad_schedule(p.dtype, p.H, p.tile, tn, tv);
+    return t_dz + g.seconds + 2.0 * kLaunchSeconds;
   };
   const int64_t cn_last = p.N - (a - 1) * CN, cv_last = p.V - (b - 1) * CV;
   const double time = static_cast<double>((a - 1) * (b - 1)) * block(CN, CV) +
@@ -249,12 +272,11 @@ bool make_plan(int64_t N, int64_t H, int64_t V, Dtype dtype, int64_t chunk, Sche
   // by one 128-byte line.
   p.ldz = p.CV;
   if ((p.ldz * p.elem_bytes) % 1024 == 0) p.ldz += 128 / p.elem_bytes;
-  // ---- dX split: when the dW and dX grids of a block together fill less
-  // than one wave of the CUs, enough splits of dX over the vocabulary to
-  // fill it, each at least four vocabulary tiles long
+  // ---- dX split over the vocabulary for the block's shared dW / dX grid
   if (N > 0 && variant != Variant::Filtered)
-    p.dx_splits = dx_split_count(cdiv(std::min(p.CN, N), BN), cdiv(std::min(p.CV, V), BM),
-                                 cdiv(H, BN));
+    p.dx_splits = grad_schedule(dtype, H, p.tile, cdiv(std::min(p.CN, N), BN),
+                                cdiv(std::min(p.CV, V), BM))
+                      .splits;
   p.grad_rmw_bytes = (N == 0) ? 4 * V * H
                               : 4 * V * H * (2 * p.a - 1) + 4 * N * H * (2 * p.b - 1);
   if (store && N > 0) p.grad_rmw_bytes = 4 * V * H * (2 * p.a - 1) + 4 * N * H;

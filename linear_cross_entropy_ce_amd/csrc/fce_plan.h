@@ -72,10 +72,16 @@ constexpr int kLossBlock = 256;  // tokens per block of the loss reduction
 constexpr size_t kOffFilterStats = 64;
 static_assert(sizeof(Ctrl) <= kOffFilterStats, "filter counters after the control block");
 
-// Splits of the dX product over the vocabulary for a logit block of
-// tok_tiles x voc_tiles tiles: the dW and dX tiles of a block share one
-// grid, and dX is split only when that grid is under one wave of the CUs.
-int64_t dx_split_count(int64_t tok_tiles, int64_t voc_tiles, int64_t h_tiles);
+// How the dW and dX tiles of a logit block of tok_tiles x voc_tiles tiles
+// share one grid: the splits of dX over the vocabulary, whether the dX tiles
+// (the longer kind) go first, and the modelled time of the grid.
+struct GradSchedule {
+  int64_t splits;
+  bool dx_first;
+  double seconds;
+};
+GradSchedule grad_schedule(Dtype dtype, int64_t H, int64_t tile, int64_t tok_tiles,
+                           int64_t voc_tiles);
 
 // Returns false if the arguments are invalid (shapes, chunk, overflow).
 bool make_plan(int64_t N, int64_t H, int64_t V, Dtype dtype, int64_t chunk, Schedule sched,

@@ -194,6 +194,19 @@ def cmd_counters(args):
             names.append(r["Counter_Name"])
     per = {n: per_dispatch(args.csv, n) for n in names}
     kernels = sorted({k for d in per.values() for k in d})
+    # durations of the same dispatches from a kernel trace of the same run
+    dur = {}
+    if getattr(args, "trace", None):
+        by_id = {}
+        for r in _rows(args.trace):
+            by_id[r["Dispatch_Id"]] = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) * 1e-9
+        ids = defaultdict(set)
+        for r in _rows(args.csv):
+            k = kernel_key(r["Kernel_Name"])
+            if k is not None and r["Dispatch_Id"] in by_id:
+                ids[k].add(r["Dispatch_Id"])
+        for k, s_ in ids.items():
+            dur[k] = sum(by_id[i] for i in s_) / len(s_)
     out = [f"# {args.title}", "", "Commands (on the MI355X box, from the repository root, with "
            "`cd /tmp && export TMPDIR=/tmp` first):", ""]
     out += [f"    {c}" for c in (args.command or [])]
@@ -209,14 +222,21 @@ def cmd_counters(args):
         if "SQ_VALU_MFMA_BUSY_CYCLES" in avg and "SQ_BUSY_CYCLES" in avg:
             # SQ_BUSY_CYCLES is summed over the 32 shader engines, the MFMA
             # busy cycles over the 1024 SIMDs (32 per engine): their ratio over
-            # 32 is the fraction of busy cycles each SIMD's matrix pipe worked
-            derived.append(f"| {k} | {avg['SQ_VALU_MFMA_BUSY_CYCLES'] / max(32.0 * avg['SQ_BUSY_CYCLES'], 1):.3f} | "
-                           + (f"{avg['SQ_LDS_BANK_CONFLICT'] / max(avg.get('SQ_INSTS_LDS', 1), 1):.4f}"
-                              if "SQ_LDS_BANK_CONFLICT" in avg else "")
-                           + " |")
+            # 32 is the fraction of busy cycles each SIMD's matrix pipe worked.
+            # Over a dispatch's duration, SQ_BUSY_CYCLES / 32 gives the clock.
+            busy = avg["SQ_VALU_MFMA_BUSY_CYCLES"] / max(32.0 * avg["SQ_BUSY_CYCLES"], 1)
+            conf = (f"{avg['SQ_LDS_BANK_CONFLICT'] / max(avg.get('SQ_INSTS_LDS', 1), 1):.4f}"
+                    if "SQ_LDS_BANK_CONFLICT" in avg else "")
+            if k in dur:
+                clk = avg["SQ_BUSY_CYCLES"] / 32.0 / dur[k] / 1e9
+                derived.append(f"| {k} | {dur[k] * 1e6:,.1f} | {clk:.3f} | {busy:.3f} | "
+                               f"{busy * clk / 2.4:.3f} | {conf} |")
+            else:
+                derived.append(f"| {k} | | | {busy:.3f} | | {conf} |")
     if derived:
-        out += ["", "| kernel | MFMA busy fraction per SIMD | LDS bank-conflict cycles per LDS instruction |",
-                "|:--|--:|--:|"] + derived
+        out += ["", "| kernel | duration us | clock GHz | MFMA busy fraction per SIMD | "
+                "busy x clock / 2.4 GHz (fraction of dense peak) | LDS bank-conflict cycles per "
+                "LDS instruction |", "|:--|--:|--:|--:|--:|--:|"] + derived
     if args.notes:
         out += [""] + args.notes
     with open(args.out, "w") as fh:
@@ -275,6 +295,7 @@ def main(argv=None):
     n.add_argument("--out", required=True)
     n.add_argument("--command", action="append")
     n.add_argument("--notes", action="append")
+    n.add_argument("--trace", help="kernel_trace.csv of the same run (durations, clock)")
     s = sub.add_parser("stats")
     s.add_argument("--csv", required=True)
     s.add_argument("--title", required=True)

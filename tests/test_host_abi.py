@@ -117,17 +117,14 @@ def test_plan_invariants(N, H, V, dtype, chunk, sched):
         if sched == "vocab":
             assert a == 1
     assert p["grad_rmw_bytes"] == 4 * V * H * (2 * a - 1) + 4 * N * H * (2 * b - 1)
-    # the dW and dX tiles of a block share one grid; dX splits over V only
-    # when that grid is under one wave of 256 CUs, then with enough splits
-    # to fill it, each at least 4 tiles long
-    n_dx = -(-min(CN, N) // tile) * -(-H // tile)
+    # the dW and dX tiles of a block share one grid; dX splits over V into
+    # at most 16 parts of at least 4 vocabulary tiles, and its fp32 partials
+    # never exceed the dZ block
     ktiles = -(-min(CV, V) // tile)
-    n_dw = ktiles * -(-H // tile)
     S = p["dx_splits"]
-    if n_dw + n_dx >= 256 or ktiles < 8:
-        assert S == 1
-    else:
-        assert S == max(1, min(-(-(256 - n_dw) // n_dx), ktiles // 4))
+    assert 1 <= S <= max(1, min(ktiles // 4, 16))
+    if S > 1:
+        assert S * 4 * H <= ktiles * tile * eb
     dxpart = S * min(CN, N) * H * 4 if S > 1 else 0
     assert p["workspace_bytes"] >= p["scratch_bytes"] + p["partial_bytes"] + dxpart
 
