@@ -59,6 +59,11 @@
  *   FCE_SCHED_AUTO   the block shape with the same budget that moves the
  *                    fewest fp32 gradient bytes (see fce_plan).
  * The loss and gradients are the same up to fp32 summation order.
+ *
+ * Plans are cached by (N, H, V, dtype, chunk, schedule, variant): the first
+ * call with a key runs the block-shape search on the host (milliseconds,
+ * tens of them at the largest shapes), later calls reuse its result.  The
+ * cache is process-wide, guarded by a mutex, and holds up to 256 plans.
  */
 #ifndef FCE_H
 #define FCE_H
@@ -321,7 +326,9 @@ const char* fce_last_hip_error(void);
  * consecutive kernels share the event between them (one event per kernel
  * boundary), and each call starts with an event of its own, so work the
  * caller enqueues between calls is never counted.  The events cost the
- * stream a few microseconds each.  fce_timing_read synchronises on the
+ * stream a few microseconds each.  fce_timing_enable(1) creates a pool of
+ * events first (more are created only when a run of calls between reads
+ * needs them), and returns FCE_ERR_HIP if it cannot.  fce_timing_read synchronises on the
  * recorded events, fills up to `cap` entries and resets the counters.  The
  * timer is process-wide and guarded by a mutex: while it is enabled, each
  * entry point holds that mutex while it enqueues its launches, so calls

@@ -44,6 +44,10 @@ struct Record {
   int start, stop;  // event indices
 };
 
+// Events created when timing is switched on: about 25 kernel boundaries per
+// fused call at the largest plans, for 40 calls between reads.
+constexpr size_t kTimerPreallocEvents = 1024;
+
 class EventTimer final : public fce::KernelTimer {
  public:
   bool enabled = false;
@@ -100,8 +104,8 @@ class NullTimer final : public fce::KernelTimer {
   void end(hipStream_t) override {}
 };
 
-// The library's one piece of mutable global state besides the device-arch
-// cache: the optional kernel timer, guarded by g_timer_mu.  While timing is
+// Mutable global state besides the device-arch cache and the planner's plan
+// cache (fce_plan.cpp): the optional kernel timer, guarded by g_timer_mu.  While timing is
 // on, each entry point holds the mutex from its first launch to its last
 // (TimerScope), so calls from several threads serialise their enqueueing and
 // their records never interleave; with timing off no lock is taken.
@@ -520,6 +524,15 @@ const char* fce_last_hip_error(void) {
 
 fce_status fce_timing_enable(int enable) {
   std::lock_guard<std::mutex> lock(g_timer_mu);
+  if (enable) {
+    // create the events now: creating them inside the timed calls can stall
+    // the enqueueing thread long enough to leave the GPU idle
+    while (g_timer.pool.size() < kTimerPreallocEvents) {
+      hipEvent_t e;
+      if (hipEventCreate(&e) != hipSuccess) return FCE_ERR_HIP;
+      g_timer.pool.push_back(e);
+    }
+  }
   g_timer.enabled = enable != 0;
   g_timing_on.store(g_timer.enabled, std::memory_order_release);
   if (!g_timer.enabled) {

@@ -615,7 +615,12 @@ __global__ __launch_bounds__(C::NT) void k_bwd_dz(DzArgs<typename C::Elem> a) {
 // group's epilogue runs beside the other group's MFMAs.  Same dZ bits as
 // k_bwd_dz: the per-token factors are computed once, before the stream,
 // with the same expressions.
-template <class C>
+// FILTER: also cast the gradient-filtering votes (kFilterP): a wave whose
+// part of a vocabulary tile holds a softmax value of at least 2^-12, or the
+// label of one of its tokens, writes 1 to the tile's keep flag (zeroed
+// before the launch; concurrent writers write the same byte).  Every tile is
+// still stored, so a kept tile's dZ is whole.
+template <class C, bool FILTER = false>
 __global__ __launch_bounds__(C::NT) void k_bwd_dz_stream(DzArgs<bf16> a, int splits) {
   int tt, sp;
   grouped_tile(xcd_remap(blockIdx.x, a.tok_tiles * splits), a.tok_tiles, splits, a.group_m, tt,
@@ -672,11 +677,15 @@ __global__ __launch_bounds__(C::NT) void k_bwd_dz_stream(DzArgs<bf16> a, int spl
   auto epilogue = [&](auto full_c, const Acc<C>& acc, int m0) {
     constexpr bool FULL = decltype(full_c)::value;
     const int vrow = m0 + rbase;  // row of element 0
+    bool vote = false;            // FILTER: this lane's vote for the tile
 #pragma unroll
     for (int fn = 0; fn < C::FN; ++fn) {
       const int c = wn * C::WTN + fn * C::NB + Map::col(lane);
       const float lb = s_lb[c], c1 = s_c1[c], c0 = s_c0[c], tk = s_tk[c];
       const int rel = s_yv[c] - vrow;
+      // the label of this token in the tile's BM rows (never for an
+      // ignored row, whose label row is far out of range)
+      if (FILTER) vote |= static_cast<unsigned>(s_yv[c] - m0) < static_cast<unsigned>(C::BM);
       auto column = [&](auto label_c) {
         constexpr bool LABEL = decltype(label_c)::value;
 #pragma unroll
@@ -685,8 +694,9 @@ __global__ __launch_bounds__(C::NT) void k_bwd_dz_stream(DzArgs<bf16> a, int spl
           floatx4 d;
 #pragma unroll
           for (int q = 0; q < 4; ++q) {
-            float v = __builtin_fmaf(
-                hw_exp2(__builtin_fmaf(acc.v[fm][fn][q], kLog2e, -lb)), c1, c0);
+            const float e = hw_exp2(__builtin_fmaf(acc.v[fm][fn][q], kLog2e, -lb));
+            if (FILTER) vote |= (FULL || vrow + off0 + q < a.nvoc) && e >= kFilterP;
+            float v = __builtin_fmaf(e, c1, c0);
             if (LABEL) v -= (rel == off0 + q) ? tk : 0.0f;
             if (!FULL) v = (vrow + off0 + q < a.nvoc) ? v : 0.0f;
             d[q] = v;
@@ -722,6 +732,9 @@ __global__ __launch_bounds__(C::NT) void k_bwd_dz_stream(DzArgs<bf16> a, int spl
                 v[j]);
       // one token column at a time (keeps the live values of one column)
       __builtin_amdgcn_sched_barrier(0);
+    }
+    if constexpr (FILTER) {
+      if (__ballot(vote) != 0 && lane == 0) a.keep[tt * a.voc_tiles + m0 / C::BM] = 1;
     }
   };
   // the epilogue's stores per wave, every one unconditional (masked columns
@@ -1657,9 +1670,13 @@ hipError_t run_backward(const Plan& p, const T* X, const T* W, const int32_t* la
   uint8_t* keep = reinterpret_cast<uint8_t*>(ws + p.off_keep);
   unsigned long long* fstats = reinterpret_cast<unsigned long long*>(ws + p.off_ctrl +
                                                                      kOffFilterStats);
-  if (filt) {  // kept / all tile counters of this call
+  if (filt) {  // kept / all tile counters of this call, and every block's kept flags
     timer->begin("fill_zero", 0.0, st);
     k_fill_zero<<<1, 256, 0, st>>>(reinterpret_cast<float*>(fstats), 4);
+    FCE_CHECK_LAUNCH();
+    const int64_t nk = static_cast<int64_t>((p.keep_bytes + 3) / 4);  // within the 256-byte padding
+    k_fill_zero<<<static_cast<int>(std::min<int64_t>(1024, std::max<int64_t>(1, (nk + 255) / 256))),
+                  256, 0, st>>>(reinterpret_cast<float*>(keep), nk);
     FCE_CHECK_LAUNCH();
     timer->end(st);
   }
@@ -1686,19 +1703,27 @@ hipError_t run_backward(const Plan& p, const T* X, const T* W, const int32_t* la
       const int voc_tiles = cdiv_i(nvoc, C::BM);
       const double blk_flops = 2.0 * static_cast<double>(ntok) * nvoc * H;
 
+      uint8_t* const keep_blk = filt ? keep + (ia * p.b + ib) * p.filt_tt * p.filt_vt : nullptr;
       DzArgs<T> da{X + tok0 * H, W + voc0 * H, labels + tok0, lse + tok0, ntok, nvoc,
                    static_cast<int>(voc0), static_cast<int>(H), static_cast<int>(V), ignore, eps,
                    o.zloss, grad_tok ? grad_tok + tok0 : nullptr, voc_tiles, tok_tiles, 4, dz,
-                   p.ldz, flags + ia, keep, stat ? stat + tok0 : nullptr};
+                   p.ldz, flags + ia, keep_blk, stat ? stat + tok0 : nullptr};
+      // bf16 with H % 128 == 0: about one workgroup per CU, each streaming a
+      // run of vocabulary tiles
+      const bool dz_stream = sizeof(T) == 2 && H % 128 == 0 && H >= 256;
       timer->begin("bwd_dz", blk_flops, st);
       if constexpr (sizeof(T) == 2) {
-        if (filt) {
+        if (filt && dz_stream) {
+          // the dZ stream with the filter votes (flags zeroed at the start)
+          const int splits = std::max(1, std::min(voc_tiles, kNumCUs / tok_tiles));
+          da.group_m = std::max(1, 32 / splits);
+          k_bwd_dz_stream<C, true><<<tok_tiles * splits, C::NT, 0, st>>>(da, splits);
+        } else if (filt) {
           if (H % 32 == 0)
             k_bwd_dz<C, true, true><<<voc_tiles * tok_tiles, C::NT, 0, st>>>(da);
           else
             k_bwd_dz<C, false, true><<<voc_tiles * tok_tiles, C::NT, 0, st>>>(da);
-        } else if (H % 128 == 0 && H >= 256) {
-          // about one workgroup per CU, each streaming a run of vocabulary tiles
+        } else if (dz_stream) {
           const int splits = std::max(1, std::min(voc_tiles, kNumCUs / tok_tiles));
           da.group_m = std::max(1, 32 / splits);
           k_bwd_dz_stream<C><<<tok_tiles * splits, C::NT, 0, st>>>(da, splits);
@@ -1725,7 +1750,7 @@ hipError_t run_backward(const Plan& p, const T* X, const T* W, const int32_t* la
       if (filt) {
         timer->begin("filter_lists", 0.0, st);
         k_filter_lists<<<tok_tiles + voc_tiles, 64, 0, st>>>(
-            keep, tok_tiles, voc_tiles, reinterpret_cast<int*>(ws + p.off_rowlist),
+            keep_blk, tok_tiles, voc_tiles, reinterpret_cast<int*>(ws + p.off_rowlist),
             reinterpret_cast<int*>(ws + p.off_rowcnt), reinterpret_cast<int*>(ws + p.off_collist),
             reinterpret_cast<int*>(ws + p.off_colcnt), fstats);
         FCE_CHECK_LAUNCH();

@@ -16,6 +16,9 @@
 #include <algorithm>
 #include <cmath>
 #include <limits>
+#include <map>
+#include <mutex>
+#include <tuple>
 
 #include "fce_tiles.h"
 
@@ -136,8 +139,10 @@ double model_time(const Plan& p, int64_t CN, int64_t CV, int64_t a, int64_t b) {
 
 }  // namespace
 
-bool make_plan(int64_t N, int64_t H, int64_t V, Dtype dtype, int64_t chunk, Schedule sched,
-               Plan* out, Variant variant) {
+namespace {
+
+bool build_plan(int64_t N, int64_t H, int64_t V, Dtype dtype, int64_t chunk, Schedule sched,
+                Plan* out, Variant variant) {
   if (!out || N < 0 || H < 1 || V < 1 || chunk < 1) return false;
   if (variant != Variant::Recompute && variant != Variant::StoreLogits &&
       variant != Variant::Filtered)
@@ -333,8 +338,10 @@ bool make_plan(int64_t N, int64_t H, int64_t V, Dtype dtype, int64_t chunk, Sche
     p.filt_tt = cdiv(std::min(p.CN, std::max<int64_t>(N, 1)), BN);
     p.filt_vt = cdiv(std::min(p.CV, V), BM);
     const size_t tiles = static_cast<size_t>(p.filt_tt * p.filt_vt);
+    // kept flags: a region per logit block, all zeroed once per call
     p.off_keep = off;
-    off = align_up(off + tiles);
+    p.keep_bytes = tiles * static_cast<size_t>(std::max<int64_t>(p.a, 1) * std::max<int64_t>(p.b, 1));
+    off = align_up(off + p.keep_bytes);
     p.off_rowlist = off;
     off = align_up(off + 4 * tiles);
     p.off_collist = off;
@@ -349,6 +356,49 @@ bool make_plan(int64_t N, int64_t H, int64_t V, Dtype dtype, int64_t chunk, Sche
     off = align_up(off + 4 * static_cast<size_t>(p.filt_vt));
   }
   p.total = off;
+  *out = p;
+  return true;
+}
+
+// Plans by their arguments: the block-shape search costs milliseconds (tens
+// at the largest shapes), and a call that waits for it leaves the GPU idle
+// when nothing of the caller's is queued ahead of it.  A plan is a pure
+// function of the key, so the cache changes no result.  Guarded by a mutex;
+// emptied when full.
+struct PlanKey {
+  int64_t N, H, V, chunk;
+  int dtype, sched, variant;
+  bool operator<(const PlanKey& o) const {
+    return std::tie(N, H, V, chunk, dtype, sched, variant) <
+           std::tie(o.N, o.H, o.V, o.chunk, o.dtype, o.sched, o.variant);
+  }
+};
+constexpr size_t kPlanCacheSize = 256;
+std::mutex g_plan_mu;
+std::map<PlanKey, Plan> g_plans;
+
+}  // namespace
+
+bool make_plan(int64_t N, int64_t H, int64_t V, Dtype dtype, int64_t chunk, Schedule sched,
+               Plan* out, Variant variant) {
+  if (!out) return false;
+  const PlanKey key{N, H, V, chunk, static_cast<int>(dtype), static_cast<int>(sched),
+                    static_cast<int>(variant)};
+  {
+    std::lock_guard<std::mutex> lock(g_plan_mu);
+    const auto it = g_plans.find(key);
+    if (it != g_plans.end()) {
+      *out = it->second;
+      return true;
+    }
+  }
+  Plan p;
+  if (!build_plan(N, H, V, dtype, chunk, sched, &p, variant)) return false;
+  {
+    std::lock_guard<std::mutex> lock(g_plan_mu);
+    if (g_plans.size() >= kPlanCacheSize) g_plans.clear();
+    g_plans.emplace(key, p);
+  }
   *out = p;
   return true;
 }

@@ -45,10 +45,12 @@ struct Plan {
   // fp32: the forward's split row statistics (row max m, log2 of the sum of
   // exp(z - m)) per token, float2 [N]; 0 bytes for bf16
   size_t off_stat = 0, stat_bytes = 0;
-  // Filtered: per logit block, kept flags [tt][vt] and the kept-block lists
+  // Filtered: kept flags [tt][vt] (filt_tt x filt_vt bytes per logit block,
+  // block ia * b + ib at keep + (ia * b + ib) filt_tt filt_vt) and the
+  // kept-block lists of the current block
   int64_t filt_tt = 0, filt_vt = 0;
-  size_t off_keep = 0, off_rowlist = 0, off_rowcnt = 0, off_collist = 0, off_colcnt = 0,
-         off_roworder = 0, off_colorder = 0;
+  size_t off_keep = 0, keep_bytes = 0, off_rowlist = 0, off_rowcnt = 0, off_collist = 0,
+         off_colcnt = 0, off_roworder = 0, off_colorder = 0;
   size_t scratch_bytes = 0, partial_bytes = 0, dxpart_bytes = 0;
   // X transposed ([H][ldxt] in the input dtype, zero past N), for the dW
   // product as (dW)^T = X^T dZ: bf16 recompute and store-logits only, 0 bytes

@@ -129,6 +129,37 @@ def test_plan_invariants(N, H, V, dtype, chunk, sched):
     assert p["workspace_bytes"] >= p["scratch_bytes"] + p["partial_bytes"] + dxpart
 
 
+def test_plan_cache_returns_the_searched_plan():
+    """Plans are cached by their arguments: repeated and concurrent requests
+    (8 threads over 12 keys) return exactly the plan of the first, serial
+    request, and keys that differ in one field keep their own plans."""
+    import threading
+
+    keys = [(N, H, V, dt, chunk, s)
+            for (N, H, V) in [(4096, 2048, 32000), (2304, 1536, 50257), (520, 264, 3001)]
+            for dt in (B.FCE_BF16, B.FCE_F32)
+            for (chunk, s) in [(1024, 0), (256, 1)]]
+    first = {k: fce.fce_plan(k[0], k[1], k[2], k[3], k[4], k[5]) for k in keys}
+    assert first[keys[0]] != first[keys[4]]  # chunk and schedule differ
+    got, errs = {}, []
+
+    def worker(i):
+        try:
+            for k in keys[i % 3:] + keys[:i % 3]:
+                got.setdefault(k, []).append(fce.fce_plan(*k))
+        except Exception as e:  # pragma: no cover
+            errs.append(e)
+
+    ts = [threading.Thread(target=worker, args=(i,)) for i in range(8)]
+    for t in ts:
+        t.start()
+    for t in ts:
+        t.join()
+    assert not errs
+    for k in keys:
+        assert len(got[k]) == 8 and all(g == first[k] for g in got[k]), k
+
+
 def test_plan_rejects_bad_arguments():
     lib = B.load_library()
     info = B.PlanInfo()
