@@ -93,7 +93,16 @@ def cpu_baseline(wl, inp, n_tokens: int):
     n = min(n_tokens, wl.N)
     X, y = inp.X[:n], inp.labels[:n]
     t0 = time.perf_counter()
-    orc.linear_cross_entropy(X, inp.W, y, wk.IGNORE_INDEX, wl.label_smoothing, "mean")
+    last = [t0]
+
+    def progress(done, total):  # a line every 20 s of a long call
+        now = time.perf_counter()
+        if now - last[0] >= 20.0:
+            last[0] = now
+            log(f"  oracle: {done} of {total} valid rows, {now - t0:.0f} s")
+
+    orc.linear_cross_entropy(X, inp.W, y, wk.IGNORE_INDEX, wl.label_smoothing, "mean",
+                             progress=progress)
     dt = time.perf_counter() - t0
     what = (f"one full oracle call on all {n} tokens of {wl.name}" if n == wl.N else
             f"first {n} of {wl.N} tokens of {wl.name}")

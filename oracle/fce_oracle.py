@@ -155,14 +155,16 @@ def dlogits(Z: np.ndarray, lse: np.ndarray, y: np.ndarray, eps: float, scale,
 
 def linear_cross_entropy(X, W, labels, ignore_index: int = -100, label_smoothing: float = 0.0,
                          reduction: str = "mean", grad_loss=1.0, row_block: int = 256,
-                         z_loss: float = 0.0) -> OracleResult:
+                         z_loss: float = 0.0, progress=None) -> OracleResult:
     """Loss, LSE and gradients of the linear cross-entropy, fp64.
 
     Per block of valid rows: Z = X_b W^T, LSE, losses, dZ, then
     dX_b = dZ W and dW += dZ^T X_b ([LLMS] step 4; [L27] "Trick 2": the two
     products of the matmul backward).  Ignored rows have zero loss and zero
     gradient and an undefined (NaN) LSE.  For reduction "none" the loss is
-    the array of per-row losses and grad_loss may be one value per row."""
+    the array of per-row losses and grad_loss may be one value per row.
+    progress: optional callable, given (valid rows done, valid rows) after
+    each block (reporting only)."""
     X = _as_f64(X)
     W = _as_f64(W)
     y = np.asarray(labels).astype(np.int64)
@@ -194,6 +196,8 @@ def linear_cross_entropy(X, W, labels, ignore_index: int = -100, label_smoothing
         dX[idx] = dZ @ W
         dW += dZ.T @ Xb
         lse[idx] = lse_b
+        if progress is not None:
+            progress(s + idx.size, rows.size)
     loss = per_row if reduction == "none" else total / D
     return OracleResult(loss, lse, dX, dW, n_valid)
 
