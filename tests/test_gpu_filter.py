@@ -102,11 +102,14 @@ def _clear_of_threshold(X, W, y, **kw):
     return np.array_equal(lo, hi)
 
 
+# H 264: the per-tile dZ kernel casts the votes; H 256 (a multiple of 128):
+# the dZ stream does
+@pytest.mark.parametrize("H", [264, 256])
 @pytest.mark.parametrize("chunk", [1024, 200])
-def test_filtered_against_oracle(chunk):
+def test_filtered_against_oracle(chunk, H):
     # chunk 200: token blocks of 256 and vocabulary blocks, so the tile grid
-    # spans several logit blocks
-    X, W, y = structured(0)
+    # spans several logit blocks (each with its own kept flags)
+    X, W, y = structured(0, H=H)
     kw = dict(label_smoothing=0.05, z_loss=1e-3)
     assert _clear_of_threshold(X, W, y, **kw)
     ref = orc.filtered_linear_cross_entropy(X, W, y, threshold=THR, **kw)
@@ -120,7 +123,7 @@ def test_filtered_against_oracle(chunk):
     assert not got["dW"][gone].any()
     le = abs(got["loss"][0] - ref.result.loss) / abs(ref.result.loss)
     ex, ew = rel_l2(got["dX"], ref.result.dX), rel_l2(got["dW"], ref.result.dW)
-    print(f"[filtered chunk {chunk}] kept {got['kept']}/{got['total']} (oracle "
+    print(f"[filtered chunk {chunk} H {H}] kept {got['kept']}/{got['total']} (oracle "
           f"{int(ref.keep.sum())}/{ref.keep.size}); loss {le:.2e}; dX {ex:.2e}; dW {ew:.2e}",
           flush=True)
     assert got["kept"] == int(ref.keep.sum()) and got["total"] == ref.keep.size
@@ -128,10 +131,11 @@ def test_filtered_against_oracle(chunk):
     assert np.all(got["dX"][y == -100] == 0.0)
 
 
-def test_filtered_isolated_hot_entries():
+@pytest.mark.parametrize("H", [264, 256])
+def test_filtered_isolated_hot_entries(H):
     # every kept tile outside the label tiles is kept by a single entry, so
     # each lane's vote counts
-    X, W, y = sparse_hot(0)
+    X, W, y = sparse_hot(0, H=H)
     assert _clear_of_threshold(X, W, y)
     ref = orc.filtered_linear_cross_entropy(X, W, y, threshold=THR)
     v = y != -100
@@ -139,7 +143,7 @@ def test_filtered_isolated_hot_entries():
     big = np.exp(Z - ref.result.lse[v][:, None]) >= THR
     assert 20 <= big.sum() <= 40  # the planted entries, nothing else
     got = run(*to_dev(X, W, y), chunk=1024, variant="filtered")
-    print(f"[filtered sparse] kept {got['kept']}/{got['total']} (oracle {int(ref.keep.sum())})",
+    print(f"[filtered sparse H {H}] kept {got['kept']}/{got['total']} (oracle {int(ref.keep.sum())})",
           flush=True)
     assert got["kept"] == int(ref.keep.sum())
     assert rel_l2(got["dX"], ref.result.dX) <= 2e-2 and rel_l2(got["dW"], ref.result.dW) <= 2e-2
