@@ -935,25 +935,30 @@ __device__ __forceinline__ void store_grad_tile_staged_t(const Acc<C>& acc, floa
   }
 }
 
-// One output tile of a gradient product: tile `bid` of the product's grid
-// (tm_tiles x tn_tiles, in the XCD-aware order) and split z of nz over the
-// contraction.  TRANS: the tile is (out)^T, out element (n, m) at
-// out + n ldo + m (the dW product computed as X^T dZ).
-template <class C, bool A_KMAJOR, bool FILTER, bool TRANS>
-__device__ __forceinline__ void grad_tile(const GradArgs<typename C::Elem>& a, int bid, int z,
-                                          int nz, const DmaStages& lds) {
-  typedef typename C::Elem T;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wm = wave / C::WAVES_N, wn = wave % C::WAVES_N;
-  int tm, tn;
+// Tile (tm, tn) of a gradient product's grid (tm_tiles x tn_tiles) for
+// workgroup `bid`: the XCD-aware order, or with FILTER and rows of unequal
+// kept length, the longest rows first in dispatch order.
+template <class C, bool FILTER>
+__device__ __forceinline__ void grad_tile_index(const GradArgs<typename C::Elem>& a, int bid,
+                                                int& tm, int& tn) {
   if (FILTER && a.kcount[a.korder[0]] != a.kcount[a.korder[a.tm_tiles - 1]]) {
-    // rows of unequal length: the longest first, in dispatch order
     tm = a.korder[bid / a.tn_tiles];
     tn = bid % a.tn_tiles;
   } else {
     grouped_tile(xcd_remap(bid, a.tm_tiles * a.tn_tiles), a.tm_tiles, a.tn_tiles, a.group_m, tm,
                  tn);
   }
+}
+
+// Output tile (tm, tn) of a gradient product, split z of nz over the
+// contraction.  TRANS: the tile is (out)^T, out element (n, m) at
+// out + n ldo + m (the dW product computed as X^T dZ).
+template <class C, bool A_KMAJOR, bool FILTER, bool TRANS>
+__device__ __forceinline__ void grad_tile_at(const GradArgs<typename C::Elem>& a, int tm, int tn,
+                                             int z, int nz, const DmaStages& lds) {
+  typedef typename C::Elem T;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave / C::WAVES_N, wn = wave % C::WAVES_N;
   const int m0 = tm * C::BM, n0 = tn * C::BN;
   const bool skip = (*a.flag == 0);  // all labels of the token block ignored: dZ = 0
   if (skip && a.accumulate) return;
@@ -1042,6 +1047,15 @@ __device__ __forceinline__ void grad_tile(const GradArgs<typename C::Elem>& a, i
   }
 }
 
+// Tile `bid` of a gradient product's grid (see grad_tile_index).
+template <class C, bool A_KMAJOR, bool FILTER, bool TRANS>
+__device__ __forceinline__ void grad_tile(const GradArgs<typename C::Elem>& a, int bid, int z,
+                                          int nz, const DmaStages& lds) {
+  int tm, tn;
+  grad_tile_index<C, FILTER>(a, bid, tm, tn);
+  grad_tile_at<C, A_KMAJOR, FILTER, TRANS>(a, tm, tn, z, nz, lds);
+}
+
 // One gradient product: a grid of tm_tiles x tn_tiles workgroups, by nz
 // splits of the contraction along y.
 template <class C, bool A_KMAJOR, bool FILTER, bool TRANS = false>
@@ -1070,6 +1084,41 @@ __global__ __launch_bounds__(C::NT) void k_bwd_grad_pair(GradArgs<bf16> gw, Grad
   } else {
     const int r = dx_first ? b : b - n_dw;
     grad_tile<C, true, false, false>(gx, r % n_dx, r / n_dx, dx_splits, lds);
+  }
+}
+
+// The filtered products of one logit block in one launch, dX tiles first
+// when theirs is the longer contraction.  A dW tile whose vocabulary tile
+// keeps every token block is computed as the exact path computes it, the
+// (h, v) tile of (dW)^T = X^T dZ on the ping-pong loop (use_t: X^T is at
+// hand, gt describes that product); every other dW tile as dZ^T X over its
+// kept token blocks.  When every vocabulary tile keeps every token block
+// (korder lists them by descending count), the dW tiles also take the exact
+// path's tile order.
+template <class C>
+__global__ __launch_bounds__(C::NT) void k_bwd_grad_pair_filt(GradArgs<bf16> gw, GradArgs<bf16> gt,
+                                                              GradArgs<bf16> gx, int n_dw,
+                                                              int n_dx, int dx_first, int use_t) {
+  FCE_DMA_STAGES(lds);
+  const int b = blockIdx.x;
+  const bool is_dw = dx_first ? b >= n_dx : b < n_dw;
+  if (is_dw) {
+    const int loc = dx_first ? b - n_dx : b;
+    const int full = (gw.K + kMapBlock - 1) / kMapBlock;
+    if (use_t && *gw.flag != 0 && gw.kcount[gw.korder[gw.tm_tiles - 1]] == full) {
+      // every dW tile keeps every token block: the exact path's product, in
+      // its tile order (groups of H-tile rows)
+      grad_tile<C, true, false, true>(gt, loc, 0, 1, lds);
+      return;
+    }
+    int tm, tn;  // vocabulary tile, H tile
+    grad_tile_index<C, true>(gw, loc, tm, tn);
+    if (use_t && *gw.flag != 0 && gw.kcount[tm] == full)
+      grad_tile_at<C, true, false, true>(gt, tn, tm, 0, 1, lds);
+    else
+      grad_tile_at<C, false, true, false>(gw, tm, tn, 0, 1, lds);
+  } else {
+    grad_tile<C, true, true, false>(gx, dx_first ? b : b - n_dw, 0, 1, lds);
   }
 }
 
@@ -1544,7 +1593,7 @@ hipError_t grad_products(const Plan& p, const T* X, const T* W, const T* dz, int
   // tiles: X^T is zero past N and dZ^T rows past the block's tokens load as
   // zero, so the extra columns add nothing.
   GradArgs<T> gt = gw;
-  if (Xt != nullptr && fl == nullptr) {
+  if (Xt != nullptr) {
     gt.A = Opnd<T>{Xt + tok0, ldxt, static_cast<int>(H), tok_tiles * C::BN};  // (h, t) at Xt[h*ldxt + t]
     gt.B = Opnd<T>{dz, ldz, nvoc, ntok};                                      // (v, t) at dz[t*ldz + v]
     gt.K = tok_tiles * C::BN;
@@ -1588,12 +1637,18 @@ hipError_t grad_products(const Plan& p, const T* X, const T* W, const T* dz, int
     gx.split_stride = static_cast<int64_t>(ntok) * H;
   }
   const int n_dw = voc_tiles * h_tiles, n_dx = tok_tiles * h_tiles;
-  bool paired = false;
   if constexpr (sizeof(T) == 2) {
-    if (fl == nullptr) {
+    if (fl != nullptr) {
+      // the filtered products in one launch
+      const int dx_first = nvoc_cov > gw.K;
+      timer->begin(name_pair, 2.0 * blk_flops, st);
+      k_bwd_grad_pair_filt<C><<<n_dw + n_dx, C::NT, 0, st>>>(gw, gt, gx, n_dw, n_dx, dx_first,
+                                                             Xt != nullptr);
+      FCE_CHECK_LAUNCH();
+      timer->end(st);
+    } else {
       // one launch for both products (bf16, unfiltered); the tiles with the
       // longer contraction first
-      paired = true;
       const int dx_first = (splits > 1 ? ksplit : nvoc_cov) > (Xt != nullptr ? gt.K : gw.K);
       timer->begin(name_pair, 2.0 * blk_flops, st);
       if (Xt != nullptr)
@@ -1606,19 +1661,13 @@ hipError_t grad_products(const Plan& p, const T* X, const T* W, const T* dz, int
       timer->end(st);
     }
   }
-  if (!paired) {
+  if constexpr (sizeof(T) == 4) {  // fp32: one launch per product
     timer->begin(name_dw, blk_flops, st);
-    if constexpr (sizeof(T) == 2)
-      k_bwd_grad<C, false, true><<<n_dw, C::NT, 0, st>>>(gw);  // filtered
-    else
-      k_bwd_grad<C, false, false><<<n_dw, C::NT, 0, st>>>(gw);
+    k_bwd_grad<C, false, false><<<n_dw, C::NT, 0, st>>>(gw);
     FCE_CHECK_LAUNCH();
     timer->end(st);
     timer->begin(name_dx, blk_flops, st);
-    if constexpr (sizeof(T) == 2)
-      k_bwd_grad<C, true, true><<<n_dx, C::NT, 0, st>>>(gx);  // filtered
-    else
-      k_bwd_grad<C, true, false><<<dim3(n_dx, splits), C::NT, 0, st>>>(gx);
+    k_bwd_grad<C, true, false><<<dim3(n_dx, splits), C::NT, 0, st>>>(gx);
     FCE_CHECK_LAUNCH();
     timer->end(st);
   }
@@ -1689,7 +1738,7 @@ hipError_t run_backward(const Plan& p, const T* X, const T* W, const int32_t* la
   }
   // X^T for the dW products (when the plan has room for it)
   const T* xt = nullptr;
-  if (!filt) {
+  {
     const hipError_t e = transpose_x(p, X, ws, st, timer, &xt);
     if (e != hipSuccess) return e;
   }

@@ -316,16 +316,16 @@ bool build_plan(int64_t N, int64_t H, int64_t V, Dtype dtype, int64_t chunk, Sch
                                            static_cast<size_t>(H) * sizeof(float)
                                      : 0;
   off = align_up(off + p.dxpart_bytes);
-  // X^T for the dW products of the bf16 recompute and store-logits paths,
-  // taken as (dW)^T = X^T dZ when token blocks hold at least 8192 tokens (the
-  // product's K): with one block of 8192 to 32768 tokens it ran faster than
-  // dZ^T X, with two accumulating blocks of 4096 or eight of 1024 slower.
+  // X^T for the dW products of the bf16 paths, taken as (dW)^T = X^T dZ when
+  // token blocks hold at least 8192 tokens (the product's K): with one block
+  // of 8192 to 32768 tokens it ran faster than dZ^T X, with two accumulating
+  // blocks of 4096 or eight of 1024 slower.  The filtered path takes it for
+  // the dW tiles that keep every token block.
   // Rows of the token extent are
   // rounded up to a tile, so that the product's K loop runs whole tiles over
   // zeros past N; 256 rows of it stay under 2 GiB (32-bit tile offsets), else
   // dW keeps the untransposed product
-  if (dtype == Dtype::BF16 && (variant == Variant::Recompute || variant == Variant::StoreLogits) &&
-      N > 0 && p.CN >= 8192) {
+  if (dtype == Dtype::BF16 && N > 0 && p.CN >= 8192) {
     const int64_t ldxt = round_up(N, G);
     if (ldxt < row_cap) {
       p.ldxt = ldxt;

@@ -21,6 +21,8 @@ MANGLED = {
     # k_bwd_grad_pair<C, DW_KMAJOR, DW_TRANS>: dW and dX of a block in one grid
     f"_ZN3fce12_GLOBAL__N_115k_bwd_grad_pair{_CFG}Lb1ELb1EEEvNS0_8GradArgsIDF16bEES7_iii": "bwd_grad",
     f"void fce::(anonymous namespace)::k_bwd_grad_pair<{_DEM}, false, false>(GradArgs<__bf16>, GradArgs<__bf16>, int, int, int)": "bwd_grad",
+    # the filtered products of a block in one grid
+    f"_ZN3fce12_GLOBAL__N_120k_bwd_grad_pair_filt{_CFG}EEvNS0_8GradArgsIDF16bEES7_S7_iiii": "bwd_grad",
     # k_fwd_lse<C, SMOOTH, STORE>: the storing one belongs to store-logits
     f"_ZN3fce12_GLOBAL__N_19k_fwd_lse{_CFG}Lb1ELb0EEEvNS0_7FwdArgsINT_4ElemEEE": "fwd_lse",
     f"_ZN3fce12_GLOBAL__N_19k_fwd_lse{_CFG}Lb0ELb1EEEvNS0_7FwdArgsINT_4ElemEEE": "sl_fwd",
