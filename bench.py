@@ -197,6 +197,42 @@ def run_side(torch, fce, wk, args, side, X, W, y, loss, lse, dX, dW, ws, step, s
             log(f"  naive torch: {side['naive_torch']}")
         except torch.cuda.OutOfMemoryError as e:  # pragma: no cover
             side["naive_torch"] = {"error": str(e)[:200]}
+        try:
+            side["vendor_gemms"] = vendor_gemms(torch, X, W, min(k2, 5))
+            log(f"  vendor GEMMs: {side['vendor_gemms']}")
+        except torch.cuda.OutOfMemoryError as e:  # pragma: no cover
+            side["vendor_gemms"] = {"error": str(e)[:200]}
+
+
+def vendor_gemms(torch, X, W, steps):
+    """Context only: the step's three GEMM shapes through torch (hipBLASLt,
+    bf16 in and out, no epilogue): logits X W^T (the forward, and the
+    backward's recompute), dX = dZ W and dW = dZ^T X, with a stand-in dZ of
+    small random values.  Their sum, with the logits GEMM twice, is what the
+    vendor library takes for the step's 8NVH without any loss arithmetic."""
+    N, H = X.shape
+    V = W.shape[0]
+    g = torch.Generator(device=X.device).manual_seed(5)
+    dZ = (torch.randn(N, V, device=X.device, generator=g) * 1e-4).to(torch.bfloat16)
+    dZt = dZ.t().contiguous()
+    Wt = W.t().contiguous()
+    out = {"what": "torch mm (hipBLASLt), bf16 in and out, same shapes; context only"}
+    shapes = {"logits_XWt": lambda: torch.mm(X, Wt),
+              "dX_dZW": lambda: torch.mm(dZ, W),
+              "dW_dZtX": lambda: torch.mm(dZt, X)}
+    stream = torch.cuda.current_stream()
+    total = 0.0
+    for name, fn in shapes.items():
+        fn()
+        t, _ = time_steps(torch, fn, steps, stream)
+        ms = t / steps
+        out[name] = {"ms": round(ms, 4), "tflops": round(2.0 * N * V * H / (ms / 1e3) / 1e12, 1)}
+        total += ms * (2 if name == "logits_XWt" else 1)
+    out["four_gemm_ms"] = round(total, 4)
+    out["four_gemm_tflops_8NVH"] = round(8.0 * N * V * H / (total / 1e3) / 1e12, 1)
+    del dZ, dZt, Wt
+    torch.cuda.empty_cache()
+    return out
 
 
 def store_logits_side(torch, fce, wk, args, X, W, y, loss, dX, dW, eps, stream):
