@@ -8,7 +8,9 @@ torch = pytest.importorskip("torch")
 
 import linear_cross_entropy_ce_amd as fce  # noqa: E402
 import oracle.fce_oracle as orc  # noqa: E402
+import parity_log  # noqa: E402
 import workloads as wk  # noqa: E402
+from linear_cross_entropy_ce_amd import _binding as B  # noqa: E402
 
 pytestmark = pytest.mark.gpu
 
@@ -129,6 +131,57 @@ def test_filtered_against_oracle(chunk, H):
     assert got["kept"] == int(ref.keep.sum()) and got["total"] == ref.keep.size
     assert le <= 2e-3 and ex <= 2e-2 and ew <= 2e-2
     assert np.all(got["dX"][y == -100] == 0.0)
+
+
+def mixed_rows(seed, s=64.0):
+    """8192 tokens whose column 0 is zero except in token tile 1, where every
+    row is s e_0 and W's column 0 is zero: those 256 tokens see all-zero
+    logits (p = 1/5120, below 2^-12) and are dropped from every vocabulary
+    tile but the two label tiles.  The hot tiles 5 and 8 keep the other 31
+    token tiles.  A partially kept dW row then has column 0 exactly zero,
+    where X^T dZ over all tokens would add the dropped s / 5120 terms."""
+    X, W, y = structured(seed, N=8192, H=256, V=5120, hot=(5, 8))
+    X[:, 0] = 0.0
+    W[:, 0] = 0.0
+    X[256:512] = 0.0
+    X[256:512, 0] = s
+    return X, W, y
+
+
+def test_filtered_token_block_of_8192_mixed_rows():
+    # One logit block of all 8192 tokens (vocabulary schedule): the plan then
+    # holds X^T, and one launch mixes the dW forms: X^T dZ for the vocabulary
+    # tiles that keep every token tile (the label tiles), the mapped dZ^T X
+    # over the kept token tiles for the hot tiles, nothing for the rest.
+    X, W, y = mixed_rows(2)
+    opts = dict(chunk=1024, schedule="vocab", variant="filtered")
+    p = fce.fce_plan(8192, 256, W.shape[0], fce.FCE_BF16, 1024, B.SCHED_VOCAB)
+    assert p["block_tokens"] == 8192 and p["n_token_blocks"] == 1
+    ref = orc.filtered_linear_cross_entropy(X, W, y, threshold=THR)
+    nt, nv = ref.keep.shape
+    rows = ref.keep.sum(axis=0)  # kept token tiles per vocabulary tile
+    full, part = rows == nt, (rows > 0) & (rows < nt)
+    assert full[:2].all() and part[[5, 8]].all() and (rows == 0).sum() == nv - 4
+    # every block's largest valid softmax value is clear of the threshold
+    v = y != -100
+    P = np.exp(X.astype(np.float64) @ W.T.astype(np.float64) - ref.result.lse[:, None])
+    P[~v] = 0.0
+    top = P.reshape(nt, TILE, nv, TILE).max(axis=(1, 3))
+    assert not ((top > THR / 1.05) & (top < THR * 1.05)).any()
+    got = run(*to_dev(X, W, y), **opts)
+    ex, ew = rel_l2(got["dX"], ref.result.dX), rel_l2(got["dW"], ref.result.dW)
+    print(f"[filtered 8192-token block] kept {got['kept']}/{got['total']} (oracle "
+          f"{int(ref.keep.sum())}); dX {ex:.2e}; dW {ew:.2e}", flush=True)
+    parity_log.record("filtered 8192x256x5120 one token block (mixed dW forms)", 2e-3, 2e-2,
+                      dX=ex, dW=ew)
+    assert got["kept"] == int(ref.keep.sum())
+    tiles = np.repeat(np.arange(nv), TILE)
+    assert not got["dW"][rows[tiles] == 0].any()
+    # the partially kept rows leave out the dropped token tile's s e_0 terms
+    # (column 0 exactly zero); the fully kept ones hold them
+    assert not got["dW"][part[tiles], 0].any()
+    assert np.abs(got["dW"][full[tiles], 0]).min() > 0
+    assert ex <= 2e-2 and ew <= 2e-2
 
 
 @pytest.mark.parametrize("H", [264, 256])
