@@ -1213,6 +1213,10 @@ constexpr int kCeCache = 10112;
 // VGPRs), so pass 2 reads no memory.
 constexpr int kCeLdsIters = 9, kCeRegIters = 7;
 constexpr int kCeResidentVecs = (kCeLdsIters + kCeRegIters) * kCeThreads;
+// How far a vector's maximum may pass a thread's reference point m before
+// m moves (natural-log units): terms exp(z - m) stay below e^16 = 2^23.1, so
+// a thread's sum of up to 2^21 of them cannot overflow.
+constexpr float kCeLag = 16.0f;
 
 template <typename T>
 struct CeVec;
@@ -1289,6 +1293,7 @@ __global__ __launch_bounds__(kCeThreads) void k_ce_logits(CeArgs a) {
   const int y = a.labels[row];
   const bool valid = label_ok(y, a.ignore, a.V);
   const int nv = (a.V + E - 1) / E;  // 16-byte vectors per row
+  const int nvf = a.V / E;           // whole vectors of the row
   const T* zrow = static_cast<const T*>(a.Z) + row * a.ldz;
   T* drow = a.dZ ? static_cast<T*>(a.dZ) + row * a.lddz : nullptr;
   // Loads past the row's vectors return zeros and stores there are dropped:
@@ -1313,8 +1318,9 @@ __global__ __launch_bounds__(kCeThreads) void k_ce_logits(CeArgs a) {
     return;
   }
 
-  // LSE = m + lg ln 2, with the row max m and lg = log2 of the sum of
-  // exp(z - m) kept apart for the exponents of pass 2 (fp32)
+  // LSE = m + lg ln 2, with the row's reference m (its maximum, or at most
+  // kCeLag below it) and lg = log2 of the sum of exp(z - m) kept apart for
+  // the exponents of pass 2 (fp32)
   float L, m_row, lg_row;
   if constexpr (GIVEN) {
     L = a.lse[row];
@@ -1322,37 +1328,52 @@ __global__ __launch_bounds__(kCeThreads) void k_ce_logits(CeArgs a) {
     m_row = sv.x;
     lg_row = sv.y;
   } else {
-    // pass 1: running (max, sum-exp, sum z) of this thread's vectors
-    float m = -INFINITY, l = 0.0f, zs = 0.0f;
+    // pass 1: running (m, sum-exp, sum z) of this thread's vectors.  m is a
+    // reference point for the exponentials, not the running maximum: it moves
+    // up to a vector's maximum only when that passes it by more than kCeLag,
+    // so a term exp(z - m) stays below e^kCeLag and most vectors need no
+    // rescaling of the sum.  The sum then stands for sum exp(z - m) at that m,
+    // which is what the merges and LSE = m + log sum take.
+    // Before the first vector with a finite maximum the terms use a
+    // reference of +inf, so that they vanish instead of forming inf - inf.
+    float m = -INFINITY, mt = INFINITY, mtl = INFINITY, mup = -INFINITY, l = 0.0f, zs = 0.0f;
     const bool smooth = a.eps != 0.0f;
-    auto accumulate = [&](const u32x4& rv, int j) {
+    // WHOLE (workgroup-uniform): every thread's vector of this iteration lies
+    // inside the row's whole vectors, so no element needs a tail mask
+    auto accumulate = [&](const u32x4& rv, int j, bool whole) {
       float f[E];
       CV::unpack(rv, f);
-      const int lim = a.V - j * E;
-      if (lim < E) {
+      if (whole) {
+        if (smooth) {
+#pragma unroll
+          for (int e = 0; e < E; ++e) zs += f[e];
+        }
+      } else {
+        const int lim = a.V - j * E;
         if (smooth) {
 #pragma unroll
           for (int e = 0; e < E; ++e) zs += (e < lim) ? f[e] : 0.0f;
         }
         pad(f, lim, -INFINITY);
-      } else if (smooth) {
-#pragma unroll
-        for (int e = 0; e < E; ++e) zs += f[e];
       }
       float vm = f[0];
 #pragma unroll
       for (int e = 1; e < E; ++e) vm = fmaxf(vm, f[e]);
-      if (vm == -INFINITY) return;
-      const float mn = fmaxf(m, vm);
-      const float mnl = mn * kLog2e;
-      float acc = 0.0f;
-      // fp32: exp2((z - m) log2e), exact near the max at any |m| (the
+      if (vm > mup) {  // first finite maximum, or one far above the reference
+        l = (m == -INFINITY) ? 0.0f : l * hw_exp2((m - vm) * kLog2e);
+        m = mt = vm;
+        mtl = vm * kLog2e;
+        mup = vm + kCeLag;
+      }
+      // fp32: exp2((z - m) log2e), within kCeLag of exact at any |m| (the
       // one-FMA form carries an error of |m| 2^-25 into every term)
+      auto term = [&](float z) {
+        return hw_exp2((sizeof(T) == 4) ? (z - mt) * kLog2e : fmaf(z, kLog2e, -mtl));
+      };
+      float acc = term(f[0]);
 #pragma unroll
-      for (int e = 0; e < E; ++e)
-        acc += hw_exp2((sizeof(T) == 4) ? (f[e] - mn) * kLog2e : fmaf(f[e], kLog2e, -mnl));
-      l = ((m == -INFINITY) ? 0.0f : l * hw_exp2((m - mn) * kLog2e)) + acc;
-      m = mn;
+      for (int e = 1; e < E; ++e) acc += term(f[e]);
+      l += acc;
     };
     if constexpr (RC > 0) {
       // the whole row: vectors past the row load as zero and are padded out
@@ -1370,7 +1391,7 @@ __global__ __launch_bounds__(kCeThreads) void k_ce_logits(CeArgs a) {
             s_cache[tid + i * kCeThreads] = r[u];
           else
             rcache[i - NC / kCeThreads] = r[u];
-          accumulate(r[u], tid + i * kCeThreads);
+          accumulate(r[u], tid + i * kCeThreads, (i + 1) * kCeThreads <= nvf);
         }
       }
     } else {
@@ -1381,7 +1402,7 @@ __global__ __launch_bounds__(kCeThreads) void k_ce_logits(CeArgs a) {
 #pragma unroll
         for (int u = 0; u < kCeUnroll; ++u) {
           if (j0 + u * kCeThreads < NC) s_cache[j0 + u * kCeThreads] = r[u];
-          accumulate(r[u], j0 + u * kCeThreads);
+          accumulate(r[u], j0 + u * kCeThreads, j0 - tid + (u + 1) * kCeThreads <= nvf);
         }
       }
     }
@@ -1427,7 +1448,6 @@ __global__ __launch_bounds__(kCeThreads) void k_ce_logits(CeArgs a) {
   // One vector j.  PLAIN (workgroup-uniform): the iteration holds neither
   // the label's vector nor one past the row's whole vectors, so it needs no
   // one-hot term and no tail mask.
-  const int nvf = a.V / E;
   auto emit = [&](const u32x4& rv, int j, int first) {
     float f[E];
     CV::unpack(rv, f);

@@ -169,6 +169,27 @@ def test_large_logits_stay_finite():
     check(inp, got)
 
 
+@pytest.mark.parametrize("dtype,V", [("bf16", 70001), ("fp32", 40000)])
+@pytest.mark.parametrize("mode", ["separate", "loss"])
+def test_rows_whose_maximum_climbs(dtype, V, mode):
+    # Each thread's reference point moves when a later vector's maximum
+    # passes it by more than 16 nats: rows that climb 200 nats from left to
+    # right move it at every iteration, falling rows never after the first,
+    # and a late spike of 60 nats over the row moves it once, far.
+    wl = wk.custom(48, 64, V, dtype, 0.02, "uniform", 1.1, 0.1, 0.0, seed=91)
+    inp = wk.draw_logits(wl)
+    ramp = np.linspace(0.0, 200.0, V, dtype=np.float32)
+    Z = inp.Z
+    Z[0::3] += ramp
+    Z[1::3] += ramp[::-1]
+    Z[2::3, V - 37] += 60.0
+    if dtype == "bf16":
+        inp.Z_bits = wk.round_to_bf16_bits(Z)
+        inp.Z = wk.bf16_bits_to_f32(inp.Z_bits)
+    got = run(inp, mode=mode, label_smoothing=0.05)
+    check(inp, got, label_smoothing=0.05)
+
+
 def test_full_size_llama2_shape():
     # 4096 x 32000 logits (the 4096x2048x32000 workload's logit shape), every element
     inp = wk.draw_logits(wk.WORKLOADS[2])
