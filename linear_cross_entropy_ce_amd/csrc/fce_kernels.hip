@@ -1445,6 +1445,9 @@ __global__ __launch_bounds__(kCeThreads) void k_ce_logits(CeArgs a) {
   const float gy = (1.0f - a.eps) * scale;
   const float Ll = L * kLog2e;
   const int jy = y / E, ey = y % E;
+  // dZ over Z: streaming stores (the lines were just read and are not read
+  // again); into another buffer the default policy measured faster
+  const bool inplace = a.dZ == a.Z;
   // One vector j.  PLAIN (workgroup-uniform): the iteration holds neither
   // the label's vector nor one past the row's whole vectors, so it needs no
   // one-hot term and no tail mask.
@@ -1468,7 +1471,11 @@ __global__ __launch_bounds__(kCeThreads) void k_ce_logits(CeArgs a) {
       const int lim = a.V - j * E;
       if (lim < E) pad(f, lim, 0.0f);
     }
-    __builtin_amdgcn_raw_buffer_store_b128(CV::pack(f), rd, j * 16, 0, 0);
+    const u32x4 out = CV::pack(f);
+    if (inplace)
+      __builtin_amdgcn_raw_buffer_store_b128(out, rd, j * 16, 0, kBufNonTemporal);
+    else
+      __builtin_amdgcn_raw_buffer_store_b128(out, rd, j * 16, 0, 0);
   };
   if constexpr (RC > 0) {
     // from LDS and registers only; stores past the row are dropped
