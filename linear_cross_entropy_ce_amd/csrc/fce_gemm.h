@@ -645,7 +645,13 @@ __device__ __forceinline__ void barrier_after_vmcnt() {
 // soon as row r has issued, so the reads of the next tile overlap the
 // current tile's MFMAs without a second rolling set.  Scheduling barriers
 // between rows keep every read after the last use of the register it
-// overwrites.
+// overwrites.  Odd rows walk their double fragments in reverse, so that
+// every MFMA of a K tile shares one operand register with the one before
+// it, also across rows: on random data the matrix pipes run power-limited,
+// and fewer operand changes per MFMA let the clock rise (the step at
+// 8192 x 4096 x 128256 took 25.73 instead of 25.99 ms, every product
+// faster).  Each accumulator still receives its MFMAs in K order, so the
+// results are bitwise the same.
 template <class C, bool A_KMAJOR, bool B_KMAJOR, bool KFULL>
 struct DmaEngine {
   static constexpr int S = 4, BK = 32;
@@ -698,7 +704,8 @@ struct DmaEngine {
   }
   __device__ __forceinline__ void mma_row(Acc<C>& acc, int set, int r) {
 #pragma unroll
-    for (int d = 0; d < NDB; ++d) {
+    for (int i = 0; i < NDB; ++i) {
+      const int d = (r & 1) ? NDB - 1 - i : i;  // odd rows in reverse
       const int fm = ROLL_A ? r : d, fn = ROLL_A ? d : r;
       const bf16x8& a = ROLL_A ? fr[r] : fd[set][d];
       const bf16x8& b = ROLL_A ? fd[set][d] : fr[r];

@@ -1198,9 +1198,10 @@ __global__ __launch_bounds__(256) void k_dx_reduce(const float* __restrict__ par
 // logit-space memory table: probs and dlogits reuse the logits buffer): for
 // logits Z the caller holds, one workgroup per row computes
 // LSE = m + log sum exp(z - m), the loss term and, if asked, dZ, written
-// over Z or into another buffer.  HBM-bound: the row is streamed twice, the
-// first time for (max, sum-exp, sum z), the second time for dZ.  The part of
-// the row that fits in LDS is kept there between the passes.
+// over Z or into another buffer.  HBM-bound: pass 1 reads the row for
+// (reference max, sum-exp, sum z), pass 2 writes dZ.  A row of up to 131072
+// bf16 columns stays on chip between the passes; of a longer one, the part
+// that fits in LDS.
 constexpr int kCeThreads = 1024;
 constexpr int kCeUnroll = 4;  // 16-byte loads in flight per thread
 // Pass 1 also keeps a row's first kCeCache vectors in LDS (158 KiB of the
